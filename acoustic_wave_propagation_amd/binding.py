@@ -1,0 +1,194 @@
+"""ctypes binding of libstencil3d.so (include/stencil3d.h).
+
+Argument marshalling only: every function here checks that torch tensors
+match the descriptor, takes their device pointers and the current HIP
+stream, and calls the C entry point of the same name.  All computation runs
+in the library's HIP kernels; there is no fallback.  A missing library is an
+error (run ``python -m acoustic_wave_propagation_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libstencil3d.so")
+
+ST_MAX_R = 4
+ST_F32, ST_F64 = 0, 1
+HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
+
+# every entry point declared in include/stencil3d.h
+EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
+           "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
+           "wave_step", "wave_add_source", "wave_run")
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``stencil3d_desc``."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", ctypes.c_int32),
+                ("nx", ctypes.c_int64), ("ny", ctypes.c_int64),
+                ("nz", ctypes.c_int64), ("radius", ctypes.c_int32),
+                ("boundary", ctypes.c_int32),
+                ("cx", ctypes.c_double * (ST_MAX_R + 1)),
+                ("cy", ctypes.c_double * (ST_MAX_R + 1)),
+                ("cz", ctypes.c_double * (ST_MAX_R + 1))]
+
+    @property
+    def shape(self):
+        return (self.nz, self.ny, self.nx)
+
+
+class Stencil3DError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (%d)" % (where, strerror(code), code))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libstencil3d.so is not built (%s); run "
+                "python -m acoustic_wave_propagation_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, dp = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                            ctypes.c_double)
+        D = ctypes.POINTER(Desc)
+        sig = {
+            "stencil3d_abi_version": (i32, []),
+            "stencil3d_strerror": (ctypes.c_char_p, [i32]),
+            "stencil3d_desc_init": (i32, [D, i32, i64, i64, i64, i32, i32]),
+            "stencil3d_desc_validate": (i32, [D]),
+            "stencil3d_apply": (i32, [D, vp, vp, vp]),
+            "stencil3d_jacobi": (i32, [D, vp, vp, i32, vp]),
+            "wave_step": (i32, [D, vp, vp, vp, vp, vp, dp, dp, vp]),
+            "wave_add_source": (i32, [D, vp, i64, i64, i64, dp, vp]),
+            "wave_run": (i32, [D, vp, vp, vp, vp, dp, dp, i32, i64, i64, i64,
+                               ctypes.POINTER(ctypes.c_double), vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().stencil3d_abi_version()
+
+
+def strerror(code: int) -> str:
+    return lib().stencil3d_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise Stencil3DError(code, where)
+
+
+def desc_init(dtype, shape, radius: int, boundary: int = HALO_UNTOUCHED) -> Desc:
+    """Descriptor of a (nz, ny, nx) grid with the library's Laplacian
+    weights.  dtype: "f32" | "f64" | a torch / numpy float dtype."""
+    d = Desc()
+    nz, ny, nx = shape
+    _check(lib().stencil3d_desc_init(ctypes.byref(d), _dtype_code(dtype),
+                                     nx, ny, nz, radius, boundary),
+           "stencil3d_desc_init")
+    return d
+
+
+def desc_validate(d: Desc) -> int:
+    """Raw status of ``stencil3d_desc_validate`` (0 = valid)."""
+    return lib().stencil3d_desc_validate(ctypes.byref(d))
+
+
+def _dtype_code(dtype) -> int:
+    s = str(dtype)
+    if s in ("f32", "float32", "torch.float32"):
+        return ST_F32
+    if s in ("f64", "float64", "torch.float64"):
+        return ST_F64
+    raise ValueError("unsupported dtype %r" % (dtype,))
+
+
+def _ptr(t, d: Desc, name: str) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if _dtype_code(t.dtype) != d.dtype:
+        raise ValueError("%s has dtype %s, descriptor says %s"
+                         % (name, t.dtype, "f64" if d.dtype else "f32"))
+    if t.numel() != d.nx * d.ny * d.nz:
+        raise ValueError("%s has %d elements, descriptor grid has %d"
+                         % (name, t.numel(), d.nx * d.ny * d.nz))
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def stencil3d_apply(d: Desc, inp, out, stream=None):
+    """out = star(inp) on the interior (+ boundary copy if d asks for it)."""
+    _check(lib().stencil3d_apply(ctypes.byref(d), _ptr(inp, d, "in"),
+                                 _ptr(out, d, "out"), _stream(inp, stream)),
+           "stencil3d_apply")
+    return out
+
+
+def stencil3d_jacobi(d: Desc, buf0, buf1, sweeps: int, stream=None):
+    """Ping-pong sweeps with a fixed boundary; returns the buffer holding
+    the result."""
+    _check(lib().stencil3d_jacobi(ctypes.byref(d), _ptr(buf0, d, "buf0"),
+                                  _ptr(buf1, d, "buf1"), int(sweeps),
+                                  _stream(buf0, stream)), "stencil3d_jacobi")
+    return buf0 if sweeps % 2 == 0 else buf1
+
+
+def wave_step(d: Desc, u_prev, u, u_next, vel2, eta, dt: float, h: float,
+              stream=None):
+    _check(lib().wave_step(ctypes.byref(d), _ptr(u_prev, d, "u_prev"),
+                           _ptr(u, d, "u"), _ptr(u_next, d, "u_next"),
+                           _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"),
+                           float(dt), float(h), _stream(u, stream)),
+           "wave_step")
+    return u_next
+
+
+def wave_add_source(d: Desc, u, ix: int, iy: int, iz: int, value: float,
+                    stream=None):
+    _check(lib().wave_add_source(ctypes.byref(d), _ptr(u, d, "u"), ix, iy, iz,
+                                 float(value), _stream(u, stream)),
+           "wave_add_source")
+    return u
+
+
+def wave_run(d: Desc, u_prev, u, vel2, eta, dt: float, h: float, nsteps: int,
+             src=(0, 0, 0), src_trace=None, stream=None):
+    """Two-buffer leapfrog; returns (older, newest) tensors."""
+    n = int(nsteps)
+    tr = None
+    if src_trace is not None:
+        vals = [float(v) for v in src_trace]
+        if len(vals) < n:
+            raise ValueError("src_trace needs %d values" % n)
+        tr = (ctypes.c_double * max(n, 1))(*vals[:max(n, 1)])
+    ix, iy, iz = src
+    _check(lib().wave_run(ctypes.byref(d), _ptr(u_prev, d, "u_prev"),
+                          _ptr(u, d, "u"), _ptr(vel2, d, "vel2"),
+                          _ptr(eta, d, "eta"), float(dt), float(h), n, ix, iy,
+                          iz, tr, _stream(u, stream)), "wave_run")
+    return (u_prev, u) if n % 2 == 0 else (u, u_prev)

@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the 25-point (R = 4) star stencil on a 512^3 fp32 interior
+(520^3 allocated with a 4-point halo) on one MI355X, plus the acoustic wave
+step on a 1024^3 interior as a secondary figure.
+
+    python bench.py [--steps K] [--warmup W] [--no-wave] [--no-cpu]
+
+Prints ONE JSON line.  A step is one stencil3d_apply over the whole grid
+(input already resident in HBM).  `value` = interior points * K / wall time
+of the K timed steps (GPoints/s).  `roofline.achieved` = algorithmic bytes
+of one launch / its mean duration from HIP events recorded on the launch
+stream.  `cpu_baseline` times the CPU oracle on the host cores over a
+bounded number of whole-grid applications.
+
+--calib adds a plain device copy of known size (for the counter runs that
+turn FETCH_SIZE / WRITE_SIZE into bytes); --only-headline skips everything
+but the timed stencil launches (for profiler runs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
+          "R=4 25-pt stencil at 512³ fp32")
+KERNEL_SOURCES = ["acoustic_wave_propagation_amd/csrc/star2p5d.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "star2p5d_r4_512cube_traffic.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """Bytes per launch measured by the committed counter runs, if they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
+                  re.escape(kernel), text)
+    if not m or not t or m.group(1) != kernel_hash():
+        return None
+    return float(t.group(1))
+
+
+def timed_launches(torch, fn, steps, warmup):
+    """W untimed calls, then K timed ones: wall time of the K (synchronised
+    on both sides) and per-launch HIP-event durations on the launch
+    stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # s
+    return wall, durs
+
+
+def star_bytes(interior, R, elem):
+    """One read of the interior plus its 2R-deep face slabs, one write of
+    the interior (edges and corners of the halo are never read)."""
+    nz, ny, nx = interior
+    n = nx * ny * nz
+    faces = 2 * R * (ny * nz + nx * nz + nx * ny)
+    return elem * (n + faces) + elem * n
+
+
+def bench_headline(torch, B, wl, args):
+    w = wl.R4_512
+    dev = torch.device("cuda:0")
+    log("generating %s %s" % (w.name, w.shape))
+    host = wl.input_planes(w)
+    inp = torch.from_numpy(host).to(dev)
+    out = torch.zeros_like(inp)
+    d = B.desc_init("f32", w.shape, w.radius)
+    fn = lambda: B.stencil3d_apply(d, inp, out)
+    wall, durs = timed_launches(torch, fn, args.steps, args.warmup)
+    pts = w.interior_points
+    nbytes = star_bytes(w.interior, w.radius, 4)
+    mean = float(durs.mean())
+    achieved = nbytes / mean / 1e9
+    res = dict(
+        value=pts * args.steps / wall / 1e9,
+        ms_per_step=wall / args.steps * 1e3,
+        kernel_ms=dict(mean=mean * 1e3, median=float(np.median(durs)) * 1e3,
+                       min=float(durs.min()) * 1e3),
+        roofline=dict(bound="hbm", achieved=round(achieved, 1),
+                      peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(achieved / PEAK_HBM_GBS, 4),
+                      traffic=recorded_traffic("star2p5d_r4_f32"),
+                      algorithmic_bytes=nbytes,
+                      kernel="star2p5d_kernel<float,4,false>"),
+        gbs_wall=round(nbytes * args.steps / wall / 1e9, 1),
+    )
+    return res, host
+
+
+def bench_wave(torch, B, wl, args):
+    """20-step leapfrog on 1032^3 (1024^3 interior), native time loop."""
+    w = wl.WAVE_1024
+    e = w.extra
+    dev = torch.device("cuda:0")
+    log("generating %s %s" % (w.name, w.shape))
+    shp = w.shape
+
+    def up(gen):
+        t = torch.empty(shp, dtype=torch.float32, device=dev)
+        for z0 in range(0, shp[0], 64):
+            z1 = min(shp[0], z0 + 64)
+            t[z0:z1].copy_(torch.from_numpy(gen(z0, z1)))
+        return t
+
+    vel2 = up(lambda a, b: wl.vel2_planes(w, a, b))
+    eta = up(lambda a, b: wl.eta_planes(w, a, b))
+    u_prev = torch.zeros_like(vel2)
+    u = torch.zeros_like(vel2)
+    d = B.desc_init("f32", shp, w.radius)
+    src = wl.source_point(w)
+    trace = wl.source_trace(w)
+    fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
+                            w.sweeps, src, trace)
+    runs = max(1, min(args.steps, 5))
+    wall, durs = timed_launches(torch, fn, runs, 1)
+    pts = w.interior_points * w.sweeps
+    per_step = float(durs.mean()) / w.sweeps
+    nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
+    achieved = nbytes / per_step / 1e9
+    del vel2, eta, u_prev, u
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, value=pts * runs / wall / 1e9,
+                unit="GPoints/s", ms_per_step=per_step * 1e3,
+                steps_per_run=w.sweeps, runs=runs,
+                roofline=dict(bound="hbm", achieved=round(achieved, 1),
+                              peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(achieved / PEAK_HBM_GBS, 4),
+                              algorithmic_bytes_per_step=nbytes,
+                              note="per-step mean incl. the 1-thread "
+                                   "source kernel"))
+
+
+def cpu_baseline(wl, host, budget_s):
+    """The oracle as it stands, on the host cores: whole 520^3 applications
+    repeated until the time budget is spent (at least one)."""
+    import oracle
+    w = wl.R4_512
+    c = oracle.laplacian_weights(w.radius)
+    out = np.zeros(host.shape, dtype=np.float64)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.star_apply(host, w.radius, c, out=out)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    med = float(np.median(times))
+    return dict(value=round(w.interior_points / med / 1e9, 4),
+                unit="GPoints/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d whole-grid applications of the 520^3 R=4 fp32 "
+                       "workload (fp64 oracle, long-double accumulation); "
+                       "median %.2f s each" % (len(times), med))
+
+
+def calib_copy(torch, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling the counters."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("calibration copy: %d bytes read, %d bytes written per launch"
+        % (nbytes, nbytes))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-wave", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calib", action="store_true")
+    ap.add_argument("--only-headline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from acoustic_wave_propagation_amd import binding as B
+    from acoustic_wave_propagation_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fail loudly if the library is missing
+
+    head, host = bench_headline(torch, B, wl, args)
+    log("headline: %.1f GPoints/s, kernel %.4f ms, %.1f GB/s"
+        % (head["value"], head["kernel_ms"]["mean"],
+           head["roofline"]["achieved"]))
+    if args.calib:
+        calib_copy(torch)
+    if args.only_headline:
+        return
+    wave = None if args.no_wave else bench_wave(torch, B, wl, args)
+    if wave:
+        log("wave: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
+            % (wave["value"], wave["ms_per_step"],
+               wave["roofline"]["achieved"]))
+    cpu = None if args.no_cpu else cpu_baseline(wl, host, args.cpu_budget)
+
+    w = wl.R4_512
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 2),
+        "unit": "GPoints/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded uniform [-1,1])",
+        "config": {"workload": w.name, "grid": list(w.shape[::-1]),
+                   "interior": list(w.interior[::-1]), "radius": w.radius,
+                   "boundary": "halo_untouched",
+                   "device": torch.cuda.get_device_name(0)},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "kernel_ms": head["kernel_ms"],
+        "hbm_gbs_wall": head["gbs_wall"],
+        "wave_step": wave,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

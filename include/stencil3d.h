@@ -1,0 +1,179 @@
+/*
+ * stencil3d.h -- C ABI of libstencil3d.so: the 3D star stencil of radius R
+ * and the acoustic isotropic wave step on MI355X (gfx950).
+ *
+ * Grid layout ("Accelerating High-Order Stencils on GPUs", gmem kernel
+ * description): one dense flat array per field, x innermost, element
+ * (x, y, z) at index x + nx*(y + ny*z).  nx, ny, nz are the ALLOCATED
+ * extents, halo included; the written region ("interior") is
+ * x in [R, nx-R), y in [R, ny-R), z in [R, nz-R), the points whose whole
+ * stencil lies inside the array.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named in/out/u/... are DEVICE pointers (hipMalloc or torch
+ *    allocations), aligned to the element size, owned by the caller.  The
+ *    library allocates no device memory and keeps no pointer after return.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns without synchronising.
+ *  - Return value: ST_OK (0) or a negative ST_ERR_* code.  Every argument
+ *    is validated before anything is enqueued, so a failed call leaves no
+ *    partial work; no C++ exception crosses this boundary.  ST_ERR_LAUNCH
+ *    reports a HIP error seen right after the launch.
+ *  - Thread safety: calls may come from any host thread; the library holds
+ *    no mutable state besides a per-device cache of the compute-unit count.
+ */
+#ifndef STENCIL3D_H
+#define STENCIL3D_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ST_ABI_VERSION 1
+#define ST_MAX_R 4
+
+/* element types */
+#define ST_F32 0
+#define ST_F64 1
+
+/* boundary modes */
+#define ST_BC_HALO_UNTOUCHED 0  /* write the interior only                  */
+#define ST_BC_DIRICHLET_COPY 1  /* also copy every non-interior point in->out */
+
+/* status codes */
+#define ST_OK 0
+#define ST_ERR_NULL (-1)        /* a required pointer is NULL                */
+#define ST_ERR_STRUCT_SIZE (-2) /* desc->struct_size != sizeof(stencil3d_desc) */
+#define ST_ERR_DTYPE (-3)       /* dtype not ST_F32 / ST_F64                 */
+#define ST_ERR_RADIUS (-4)      /* radius outside 1..ST_MAX_R                */
+#define ST_ERR_DIMS (-5)        /* an extent < 2R+1, or a plane too large    */
+#define ST_ERR_BOUNDARY (-6)    /* unknown boundary mode                     */
+#define ST_ERR_ALIAS (-7)       /* buffers overlap where they must not       */
+#define ST_ERR_BAD_INDEX (-8)   /* source point outside the interior         */
+#define ST_ERR_COEFF (-9)       /* a weight is NaN or infinite               */
+#define ST_ERR_ARG (-10)        /* bad scalar argument (dt, h, counts)       */
+#define ST_ERR_ALIGN (-11)      /* pointer not aligned to the element size   */
+#define ST_ERR_LAUNCH (-12)     /* HIP reported an error at launch           */
+#define ST_ERR_DEVICE (-13)     /* no usable HIP device                      */
+
+/*
+ * Problem descriptor.  cx/cy/cz hold the per-axis weights: index 0 is that
+ * axis' share of the centre weight (the 3D centre weight is
+ * cx[0]+cy[0]+cz[0]), index k = 1..R the weight of the two points at
+ * offsets +k and -k on that axis.  Entries above R are ignored.
+ * 160 bytes, naturally aligned.
+ */
+typedef struct stencil3d_desc {
+    uint32_t struct_size; /* = sizeof(stencil3d_desc)                    */
+    int32_t dtype;        /* ST_F32 | ST_F64                              */
+    int64_t nx, ny, nz;   /* allocated extents incl. halo; x innermost    */
+    int32_t radius;       /* R, 1..ST_MAX_R                               */
+    int32_t boundary;     /* ST_BC_*                                      */
+    double cx[ST_MAX_R + 1];
+    double cy[ST_MAX_R + 1];
+    double cz[ST_MAX_R + 1];
+} stencil3d_desc;
+
+/* ST_ABI_VERSION of the built library. */
+int stencil3d_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *stencil3d_strerror(int code);
+
+/*
+ * Fill *d for a grid of the given extents with the standard order-2R
+ * central second-difference weights on every axis (unit spacing), so the
+ * stencil is the discrete Laplacian: R = 1 gives the 7-point rule of the
+ * "Thread Coarsening and Register Tiling" notes (Fig 8.10) with centre -6;
+ * R = 4 the 25-point rule of the acoustic isotropic kernels in
+ * "Accelerating High-Order Stencils on GPUs".  Host only; validates the
+ * result.
+ */
+int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx,
+                        int64_t ny, int64_t nz, int radius, int boundary);
+
+/*
+ * Check a descriptor without touching the GPU: struct size, dtype, radius,
+ * boundary mode, extents (each >= 2R+1; nx*ny*elem < 2^31 bytes so that
+ * in-plane offsets fit 32 bits) and finite weights.
+ */
+int stencil3d_desc_validate(const stencil3d_desc *d);
+
+/*
+ * One application of the star stencil ("Accelerating High-Order Stencils
+ * on GPUs": each output reads its point and R neighbours along each
+ * direction of each axis, 2.5D streaming of XY tiles through z):
+ *
+ *   out(p) = (cx0+cy0+cz0) in(p)
+ *            + sum_{k=1..R} [ cx_k (in(p+k ex) + in(p-k ex))
+ *                           + cy_k (in(p+k ey) + in(p-k ey))
+ *                           + cz_k (in(p+k ez) + in(p-k ez)) ]
+ *
+ * on every interior point.  ST_BC_HALO_UNTOUCHED leaves the rest of out as
+ * it was; ST_BC_DIRICHLET_COPY sets it to in (the boundary copy of the
+ * starter kernel in "3D Stencil: Rotate the Depth Window Through
+ * Registers").  in and out have d's extents and element type and must not
+ * overlap (ST_ERR_ALIAS).
+ */
+int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out,
+                    void *stream);
+
+/*
+ * Jacobi ping-pong: `sweeps` applications alternating buf0 -> buf1 ->
+ * buf0 ..., with a fixed Dirichlet boundary: buf1's non-interior points are
+ * first set from buf0, then every sweep writes the interior only.  The
+ * result is in buf0 if sweeps is even, else in buf1.  d->boundary is
+ * ignored.  sweeps >= 0 (ST_ERR_ARG); buffers must not overlap.
+ */
+int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
+                     int sweeps, void *stream);
+
+/*
+ * One time step of the acoustic isotropic wave equation with a damping
+ * sponge (the acoustic isotropic model with an absorbing eta layer of
+ * "Accelerating High-Order Stencils on GPUs", smem_u / smem_eta
+ * descriptions; the update formula is the standard leapfrog reading):
+ *
+ *   L      = star_d(u) / h^2
+ *   u_next = (2 u - (1 - eta) u_prev + vel2 dt^2 L) / (1 + eta)
+ *
+ * on every interior point; non-interior points of u_next are not written.
+ * star_d is the stencil of d with d's weights (the Laplacian with unit
+ * spacing from stencil3d_desc_init).  vel2 is in m^2/s^2, dt in s, h in m,
+ * eta dimensionless; all five arrays share d's extents and element type.
+ * u_next may be the same buffer as u_prev (each point reads u_prev only at
+ * itself), but must not overlap u, vel2 or eta.  dt, h finite, h > 0.
+ */
+int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u,
+              void *u_next, const void *vel2, const void *eta, double dt,
+              double h, void *stream);
+
+/*
+ * Point source: u[ix, iy, iz] += value (rounded to d's element type), one
+ * device thread.  (ix, iy, iz) are allocated coordinates and must be
+ * interior (ST_ERR_BAD_INDEX).
+ */
+int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix,
+                    int64_t iy, int64_t iz, double value, void *stream);
+
+/*
+ * Two-buffer leapfrog time loop: for n = 0..nsteps-1,
+ *   wave_step(u_prev -> u_prev as u_next); wave_add_source(u_prev,
+ *   src_trace[n]); swap roles of the two buffers.
+ * On return the newest field is in `u` if nsteps is even, else in `u_prev`
+ * (the other buffer holds the field one step older).  src_trace is a HOST
+ * array of nsteps values, or NULL for no source.  Same argument rules as
+ * wave_step and wave_add_source.
+ */
+int wave_run(const stencil3d_desc *d, void *u_prev, void *u,
+             const void *vel2, const void *eta, double dt, double h,
+             int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
+             const double *src_trace, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STENCIL3D_H */

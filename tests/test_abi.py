@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects every invalid argument with its own status
+code before it touches a device.  No call here reaches the HIP runtime."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from acoustic_wave_propagation_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stencil3d.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _codes():
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define (ST_ERR_\w+|ST_OK) \(?(-?\d+)\)?", _header_text())}
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libstencil3d.so not built; run "
+                    "python -m acoustic_wave_propagation_amd.build")
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text,
+                              flags=re.M))
+    declared.discard("defined")
+    assert declared == set(B.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    # and the binding uses exactly those names
+    assert all(callable(getattr(B, n, None)) or n.startswith("stencil3d_")
+               for n in B.EXPORTS)
+
+
+def test_struct_layout_and_version(L):
+    assert ctypes.sizeof(B.Desc) == 160
+    assert B.abi_version() == 1
+    d = B.desc_init("f32", (10, 11, 12), 4)
+    assert d.struct_size == 160 and d.nx == 12 and d.ny == 11 and d.nz == 10
+
+
+def test_strerror_is_distinct(L):
+    codes = _codes()
+    msgs = {c: B.strerror(v) for c, v in codes.items()}
+    assert len(set(msgs.values())) == len(msgs)
+    assert B.strerror(-999) == "unknown status code"
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_library_weights_are_the_laplacian(L, R):
+    """The library's own weight table satisfies the order-2R conditions
+    (to rounding) and agrees with the oracle's separately written table."""
+    import oracle
+    d = B.desc_init("f64", (9, 9, 9), R)
+    w = np.array(d.cx[:R + 1])
+    assert np.array_equal(w, np.array(d.cy[:R + 1]))
+    assert np.array_equal(w, np.array(d.cz[:R + 1]))
+    k = np.arange(1, R + 1, dtype=np.float64)
+    assert abs(w[0] + 2 * w[1:].sum()) < 1e-15
+    assert abs((w[1:] * k ** 2).sum() - 1) < 1e-14
+    for m in range(2, R + 1):
+        assert abs((w[1:] * k ** (2 * m)).sum()) < 1e-12 * 8 ** (2 * m)
+    assert np.array_equal(w, oracle.laplacian_weights(R))
+
+
+def _desc(**kw):
+    d = B.desc_init("f32", (20, 21, 22), 4)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_descriptor_validation(L):
+    c = _codes()
+    ok = _desc()
+    assert B.desc_validate(ok) == 0
+    assert L.stencil3d_desc_validate(None) == c["ST_ERR_NULL"]
+    assert B.desc_validate(_desc(struct_size=152)) == c["ST_ERR_STRUCT_SIZE"]
+    assert B.desc_validate(_desc(dtype=2)) == c["ST_ERR_DTYPE"]
+    assert B.desc_validate(_desc(radius=0)) == c["ST_ERR_RADIUS"]
+    assert B.desc_validate(_desc(radius=5)) == c["ST_ERR_RADIUS"]
+    assert B.desc_validate(_desc(boundary=7)) == c["ST_ERR_BOUNDARY"]
+    assert B.desc_validate(_desc(nx=8)) == c["ST_ERR_DIMS"]
+    assert B.desc_validate(_desc(nz=8)) == c["ST_ERR_DIMS"]
+    assert B.desc_validate(_desc(nx=9, ny=9, nz=9)) == 0
+    assert B.desc_validate(_desc(nx=1 << 16, ny=1 << 13)) == c["ST_ERR_DIMS"]
+    assert B.desc_validate(_desc(nx=1 << 16, ny=(1 << 13) - 1)) == 0
+    bad = _desc()
+    bad.cy[2] = math.nan
+    assert B.desc_validate(bad) == c["ST_ERR_COEFF"]
+    ign = _desc(radius=2)
+    ign.cz[4] = math.inf  # above R: ignored
+    assert B.desc_validate(ign) == 0
+    d = B.Desc()
+    assert L.stencil3d_desc_init(ctypes.byref(d), 0, 8, 8, 8, 4, 0) == \
+        c["ST_ERR_DIMS"]
+    assert L.stencil3d_desc_init(ctypes.byref(d), 0, 8, 8, 8, 6, 0) == \
+        c["ST_ERR_RADIUS"]
+
+
+def test_entry_points_reject_before_enqueue(L):
+    """Each call below fails validation, so it returns without any HIP call
+    (the fake pointers are never dereferenced)."""
+    c = _codes()
+    d = _desc()
+    by = ctypes.byref(d)
+    n = d.nx * d.ny * d.nz * 4
+    A, Bp = 0x10000000, 0x10000000 + n
+    assert L.stencil3d_apply(None, A, Bp, None) == c["ST_ERR_NULL"]
+    assert L.stencil3d_apply(by, None, Bp, None) == c["ST_ERR_NULL"]
+    assert L.stencil3d_apply(by, A + 2, Bp, None) == c["ST_ERR_ALIGN"]
+    assert L.stencil3d_apply(by, A, A, None) == c["ST_ERR_ALIAS"]
+    assert L.stencil3d_apply(by, A, A + n - 4, None) == c["ST_ERR_ALIAS"]
+    assert L.stencil3d_apply(ctypes.byref(_desc(radius=9)), A, Bp, None) == \
+        c["ST_ERR_RADIUS"]
+    assert L.stencil3d_jacobi(by, A, Bp, -1, None) == c["ST_ERR_ARG"]
+    assert L.stencil3d_jacobi(by, A, A + 4, 3, None) == c["ST_ERR_ALIAS"]
+    U = [0x20000000 + i * (n + 4096) for i in range(5)]
+    ws = L.wave_step
+    assert ws(by, U[0], U[1], U[2], U[3], U[4], math.nan, 10.0, None) == \
+        c["ST_ERR_ARG"]
+    assert ws(by, U[0], U[1], U[2], U[3], U[4], 1e-3, 0.0, None) == \
+        c["ST_ERR_ARG"]
+    assert ws(by, U[0], U[1], U[1], U[3], U[4], 1e-3, 10.0, None) == \
+        c["ST_ERR_ALIAS"]
+    assert ws(by, U[0], U[1], U[3], U[3], U[4], 1e-3, 10.0, None) == \
+        c["ST_ERR_ALIAS"]
+    assert ws(by, U[0], U[1], U[0] + 64, U[3], U[4], 1e-3, 10.0, None) == \
+        c["ST_ERR_ALIAS"]
+    assert ws(by, U[0], None, U[2], U[3], U[4], 1e-3, 10.0, None) == \
+        c["ST_ERR_NULL"]
+    src = L.wave_add_source
+    assert src(by, U[0], 3, 10, 10, 1.0, None) == c["ST_ERR_BAD_INDEX"]
+    assert src(by, U[0], 10, 10, 16, 1.0, None) == c["ST_ERR_BAD_INDEX"]
+    assert src(by, U[0], 10, 10, 10, math.inf, None) == c["ST_ERR_ARG"]
+    tr = (ctypes.c_double * 3)(0.1, 0.2, math.nan)
+    run = L.wave_run
+    assert run(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, -1, 10, 10, 10, None,
+               None) == c["ST_ERR_ARG"]
+    assert run(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, 3, 10, 10, 10, tr,
+               None) == c["ST_ERR_ARG"]
+    assert run(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, 3, 2, 10, 10, tr,
+               None) == c["ST_ERR_BAD_INDEX"]
+    assert run(by, U[0], U[0] + 8, U[3], U[4], 1e-3, 10.0, 3, 10, 10, 10,
+               None, None) == c["ST_ERR_ALIAS"]
+
+
+def test_binding_checks_tensors(L):
+    import torch
+    d = B.desc_init("f32", (9, 9, 9), 4)
+    cpu = torch.zeros(9 * 9 * 9)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.stencil3d_apply(d, cpu, cpu)
+    with pytest.raises(TypeError):
+        B.stencil3d_apply(d, np.zeros(729, np.float32), cpu)
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        B.desc_init("f16", (9, 9, 9), 1)

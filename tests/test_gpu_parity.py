@@ -1,0 +1,325 @@
+"""Parity of the HIP path with the CPU oracle on an MI355X.
+
+Every call goes through the C ABI (acoustic_wave_propagation_amd.binding).
+Inputs come from the seeded generators; expected values only from the
+oracle.  fp32 results must satisfy max|err| <= 1e-5 max|ref| per sweep /
+step (teacher-forced: the oracle's step k starts from the GPU's state after
+step k-1), fp64 results max|err| <= 1e-12 max|ref|; points outside the
+written region must keep their sentinel bits.
+"""
+import numpy as np
+import pytest
+
+from acoustic_wave_propagation_amd import binding as B
+from acoustic_wave_propagation_amd import workloads as wl
+
+from gpu_common import (F32_TOL, F64_TOL, SENTINEL, check_close,
+                        check_halo_untouched, device, interior, log, rel_err,
+                        sentinel_like, upload, upload_planes)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    d = device()
+    B.lib()
+    return torch, d
+
+
+def _tol(np_dtype):
+    return F32_TOL if np.dtype(np_dtype) == np.float32 else F64_TOL
+
+
+def _apply_case(oracle_mod, torch, u_np, R, boundary=B.HALO_UNTOUCHED,
+                weights=None, what="apply"):
+    """One stencil3d_apply on u_np (numpy), checked against the oracle."""
+    shape = u_np.shape
+    dt = "f32" if u_np.dtype == np.float32 else "f64"
+    d = B.desc_init(dt, shape, R, boundary)
+    if weights is not None:
+        for k in range(R + 1):
+            d.cx[k], d.cy[k], d.cz[k] = weights[0][k], weights[1][k], \
+                weights[2][k]
+    cx = list(d.cx[:R + 1])
+    cy = list(d.cy[:R + 1])
+    cz = list(d.cz[:R + 1])
+    inp = upload(u_np)
+    out = sentinel_like(shape, u_np.dtype)
+    B.stencil3d_apply(d, inp, out)
+    got = out.cpu().numpy()
+    ref = oracle_mod.star_apply(u_np, R, cx, cy, cz, boundary)
+    check_close(interior(got, R), interior(ref, R), _tol(u_np.dtype), what)
+    if boundary == B.HALO_UNTOUCHED:
+        check_halo_untouched(got, R, what)
+    else:
+        mask = np.ones(shape, bool)
+        mask[R:-R, R:-R, R:-R] = False
+        assert np.array_equal(got[mask], u_np[mask]), what + ": boundary copy"
+    return got
+
+
+# --------------------------------------------------------------------------
+# The five workloads at full size
+# --------------------------------------------------------------------------
+def test_r1_64cube_one_apply(oracle_mod, torch_dev):
+    torch, _ = torch_dev
+    w = wl.R1_64
+    log("case %s shape %s" % (w.name, w.shape))
+    _apply_case(oracle_mod, torch, wl.input_planes(w), 1, what=w.name)
+
+
+def test_r1_jacobi_512_ten_sweeps(oracle_mod, torch_dev):
+    torch, _ = torch_dev
+    w = wl.R1_JACOBI_512
+    log("case %s shape %s" % (w.name, w.shape))
+    u0 = wl.input_planes(w)
+    d = B.desc_init("f32", w.shape, 1, B.DIRICHLET_COPY)
+    c = list(d.cx[:2])
+    # teacher-forced: each sweep from the GPU's previous state
+    state = upload(u0)
+    for s in range(w.sweeps):
+        nxt = sentinel_like(w.shape, np.float32)
+        B.stencil3d_apply(d, state, nxt)
+        host_in = state.cpu().numpy()
+        got = nxt.cpu().numpy()
+        ref = oracle_mod.star_apply(host_in, 1, c, boundary=B.DIRICHLET_COPY)
+        check_close(got, ref, F32_TOL, "%s sweep %d" % (w.name, s))
+        state = nxt
+    chained = state.cpu().numpy()
+    # the native ping-pong entry point gives the same bits
+    b0, b1 = upload(u0), sentinel_like(w.shape, np.float32)
+    res = B.stencil3d_jacobi(d, b0, b1, w.sweeps)
+    assert res is (b0 if w.sweeps % 2 == 0 else b1)
+    assert np.array_equal(res.cpu().numpy(), chained)
+    free = rel_err(chained, oracle_mod.jacobi(u0, w.sweeps, 1, c))
+    log("%s free-running after %d sweeps: %.3e" % (w.name, w.sweeps, free))
+    assert free < 1e-4
+
+
+def test_r4_512cube_one_apply(oracle_mod, torch_dev):
+    torch, _ = torch_dev
+    w = wl.R4_512
+    log("case %s shape %s" % (w.name, w.shape))
+    _apply_case(oracle_mod, torch, wl.input_planes(w), 4, what=w.name)
+
+
+def test_r4_ragged_f64_one_apply(oracle_mod, torch_dev):
+    torch, _ = torch_dev
+    w = wl.R4_RAGGED_F64
+    log("case %s shape %s" % (w.name, w.shape))
+    _apply_case(oracle_mod, torch, wl.input_planes(w), 4, what=w.name)
+
+
+def _wave_fields(w, torch):
+    vel2 = upload_planes(lambda a, b: wl.vel2_planes(w, a, b), w.shape,
+                         w.np_dtype)
+    eta = upload_planes(lambda a, b: wl.eta_planes(w, a, b), w.shape,
+                        w.np_dtype)
+    u_prev = upload_planes(lambda a, b: wl.initial_u_planes(w, "u_prev", a, b),
+                           w.shape, w.np_dtype)
+    u = upload_planes(lambda a, b: wl.initial_u_planes(w, "u", a, b),
+                      w.shape, w.np_dtype)
+    return u_prev, u, vel2, eta
+
+
+def test_wave_1024_point_source_20_steps(oracle_mod, torch_dev):
+    """Zero start, Ricker source at the centre.  The field stays inside the
+    L1 ball of radius 4n about the source, so each step is checked on a
+    crop that holds that ball (the oracle on the crop equals the oracle on
+    the whole grid there), and every point outside it must be exactly 0."""
+    torch, _ = torch_dev
+    w = wl.WAVE_1024
+    e = w.extra
+    R = w.radius
+    log("case %s shape %s" % (w.name, w.shape))
+    u_prev, u, vel2, eta = _wave_fields(w, torch)
+    d = B.desc_init("f32", w.shape, R)
+    c = list(d.cx[:R + 1])
+    sx, sy, sz = wl.source_point(w)
+    trace = wl.source_trace(w)
+    hw = R * w.sweeps + R  # crop half width
+    zs, ys, xs = (slice(sz - hw, sz + hw + 1), slice(sy - hw, sy + hw + 1),
+                  slice(sx - hw, sx + hw + 1))
+    crop_v2 = wl.vel2_planes(w, sz - hw, sz + hw + 1)[:, ys, xs]
+    crop_eta = wl.eta_planes(w, sz - hw, sz + hw + 1)[:, ys, xs]
+    cz_ = np.arange(2 * hw + 1) - hw
+    l1 = (np.abs(cz_)[:, None, None] + np.abs(cz_)[None, :, None]
+          + np.abs(cz_)[None, None, :])
+    a, b = u_prev, u  # older, newer
+    for n in range(w.sweeps):
+        up_c = a[zs, ys, xs].cpu().numpy()
+        u_c = b[zs, ys, xs].cpu().numpy()
+        B.wave_step(d, a, b, a, vel2, eta, e["dt"], e["h"])  # in place
+        B.wave_add_source(d, a, sx, sy, sz, float(trace[n]))
+        a, b = b, a
+        got = b[zs, ys, xs].cpu().numpy()
+        ref = np.array(up_c, dtype=np.float64)  # halo of u_next = u_prev's
+        oracle_mod.wave_step(up_c, u_c, crop_v2, crop_eta, R, c, e["dt"],
+                             e["h"], out=ref)
+        ref[hw, hw, hw] += float(trace[n])
+        check_close(got, ref, F32_TOL, "%s step %d" % (w.name, n))
+        assert np.all(got[l1 > R * n] == 0), "field outside the light cone"
+        nz_all = int(torch.count_nonzero(b))
+        nz_crop = int(np.count_nonzero(got))
+        assert nz_all == nz_crop, "non-zero values outside the crop"
+    chained = b[zs, ys, xs].cpu().numpy()
+    # the native time loop from the same start gives the same bits
+    u_prev2, u2 = (torch.zeros_like(vel2), torch.zeros_like(vel2))
+    old, new = B.wave_run(d, u_prev2, u2, vel2, eta, e["dt"], e["h"],
+                          w.sweeps, (sx, sy, sz), trace)
+    assert np.array_equal(new[zs, ys, xs].cpu().numpy(), chained)
+    assert int(torch.count_nonzero(new)) == int(np.count_nonzero(chained))
+    # free-running against the fp64 oracle on the crop (reported)
+    _, ref_free = oracle_mod.wave_run(
+        np.zeros(crop_v2.shape), np.zeros(crop_v2.shape), crop_v2, crop_eta,
+        R, c, e["dt"], e["h"], w.sweeps, src=(hw, hw, hw), src_trace=trace)
+    free = rel_err(chained, ref_free)
+    log("%s free-running after %d steps: %.3e" % (w.name, w.sweeps, free))
+    assert free < 1e-4
+
+
+def test_wave_random_fields_with_sponge(oracle_mod, torch_dev):
+    """Random u_prev, u on a 128^3 interior whose 32-point sponge covers most
+    of it: every step teacher-forced on the whole grid, then free-running."""
+    torch, _ = torch_dev
+    w = wl.WAVE_128_RANDOM
+    e = w.extra
+    R = w.radius
+    log("case %s shape %s" % (w.name, w.shape))
+    u_prev, u, vel2, eta = _wave_fields(w, torch)
+    v2_h, eta_h = vel2.cpu().numpy(), eta.cpu().numpy()
+    up0, u0 = u_prev.cpu().numpy(), u.cpu().numpy()
+    d = B.desc_init("f32", w.shape, R)
+    c = list(d.cx[:R + 1])
+    src = wl.source_point(w)
+    trace = wl.source_trace(w)
+    a, b = u_prev.clone(), u.clone()
+    for n in range(w.sweeps):
+        up_h, u_h = a.cpu().numpy(), b.cpu().numpy()
+        nxt = torch.zeros_like(b)  # halo stays zero: only the interior is written
+        B.wave_step(d, a, b, nxt, vel2, eta, e["dt"], e["h"])
+        B.wave_add_source(d, nxt, *src, float(trace[n]))
+        got = nxt.cpu().numpy()
+        ref = oracle_mod.wave_step(up_h, u_h, v2_h, eta_h, R, c, e["dt"],
+                                   e["h"])
+        ref[src[2], src[1], src[0]] += float(trace[n])
+        check_close(interior(got, R), interior(ref, R), F32_TOL,
+                    "%s step %d" % (w.name, n))
+        check_halo_untouched(got, R, w.name, value=0.0)
+        # in-place (u_next = u_prev) gives the same bits
+        inpl = a.clone()
+        B.wave_step(d, inpl, b, inpl, vel2, eta, e["dt"], e["h"])
+        B.wave_add_source(d, inpl, *src, float(trace[n]))
+        assert np.array_equal(interior(inpl.cpu().numpy(), R),
+                              interior(got, R))
+        a, b = b, nxt
+    _, ref_free = oracle_mod.wave_run(up0, u0, v2_h, eta_h, R, c, e["dt"],
+                                      e["h"], w.sweeps, src=src,
+                                      src_trace=trace)
+    free = rel_err(interior(b.cpu().numpy(), R), interior(ref_free, R))
+    log("%s free-running after %d steps: %.3e" % (w.name, w.sweeps, free))
+    assert free < 1e-3
+
+
+# --------------------------------------------------------------------------
+# Edge cases: ragged tails, tiny grids, anisotropic weights, boundary copy
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_ragged_multi_tile(oracle_mod, torch_dev, R, dtype):
+    """Several tiles in x and y, several z chunks, ragged tails on all
+    three axes."""
+    torch, _ = torch_dev
+    shape = (61 + 2 * R, 77 + 2 * R, 149 + 2 * R)
+    log("case ragged R=%d %s %s" % (R, np.dtype(dtype).name, shape))
+    u = wl.uniform_planes(shape, 77 + R, -1, 1, dtype=dtype)
+    _apply_case(oracle_mod, torch, u, R, what="ragged R=%d %s" %
+                (R, np.dtype(dtype).name))
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_smallest_grid(oracle_mod, torch_dev, R, dtype):
+    """nx = ny = nz = 2R+1: one interior point; also a grid thinner than a
+    tile in x with a single interior plane."""
+    torch, _ = torch_dev
+    for shape in [(2 * R + 1,) * 3, (2 * R + 1, 2 * R + 3, 2 * R + 5),
+                  (2 * R + 4, 3 * R + 7, 2 * R + 1)]:
+        log("case smallest R=%d %s %s" % (R, np.dtype(dtype).name, shape))
+        u = wl.uniform_planes(shape, 5 + R, -1, 1, dtype=dtype)
+        _apply_case(oracle_mod, torch, u, R, what="smallest %s" % (shape,))
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_anisotropic_weights(oracle_mod, torch_dev, R):
+    torch, _ = torch_dev
+    rng = np.random.default_rng(31 + R)
+    wts = [list(rng.uniform(-1, 1, R + 1)) for _ in range(3)]
+    shape = (40, 53, 97)
+    log("case anisotropic R=%d %s" % (R, shape))
+    for dtype in (np.float32, np.float64):
+        u = wl.uniform_planes(shape, 9, -1, 1, dtype=dtype)
+        _apply_case(oracle_mod, torch, u, R, weights=wts,
+                    what="anisotropic R=%d %s" % (R, np.dtype(dtype).name))
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_dirichlet_copy(oracle_mod, torch_dev, R):
+    torch, _ = torch_dev
+    shape = (23, 70, 133)
+    log("case dirichlet R=%d %s" % (R, shape))
+    for dtype in (np.float32, np.float64):
+        u = wl.uniform_planes(shape, 11, -1, 1, dtype=dtype)
+        _apply_case(oracle_mod, torch, u, R, boundary=B.DIRICHLET_COPY,
+                    what="dirichlet R=%d" % R)
+
+
+def test_smooth_fp64_cancellation(oracle_mod, torch_dev):
+    """A smooth fp64 field whose stencil is small next to the field (the
+    ragged workload's regime) at a size the oracle finishes quickly."""
+    torch, _ = torch_dev
+    shape = (45, 67, 131)
+    u = wl.cubic_noise_planes(shape, 1234)
+    _apply_case(oracle_mod, torch, u, 4, what="smooth fp64")
+
+
+def test_deterministic_and_side_stream(oracle_mod, torch_dev):
+    """No atomics: repeated launches are bitwise identical, also on a
+    non-default stream."""
+    torch, dev = torch_dev
+    shape = (50, 66, 140)
+    u = upload(wl.uniform_planes(shape, 3, -1, 1))
+    d = B.desc_init("f32", shape, 4)
+    outs = []
+    for _ in range(3):
+        o = sentinel_like(shape, np.float32)
+        B.stencil3d_apply(d, u, o)
+        outs.append(o)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o = sentinel_like(shape, np.float32)
+        B.stencil3d_apply(d, u, o)
+    s.synchronize()
+    outs.append(o)
+    first = outs[0].cpu().numpy()
+    for o in outs[1:]:
+        assert np.array_equal(first, o.cpu().numpy())
+
+
+def test_gpu_rejects_bad_arguments(torch_dev):
+    torch, _ = torch_dev
+    shape = (12, 12, 12)
+    d = B.desc_init("f32", shape, 4)
+    a = torch.zeros(shape, device=device())
+    with pytest.raises(B.Stencil3DError) as ei:
+        B.stencil3d_apply(d, a, a)
+    assert ei.value.code == -7
+    with pytest.raises(B.Stencil3DError) as ei:
+        B.wave_add_source(d, a, 0, 6, 6, 1.0)
+    assert ei.value.code == -8
+    with pytest.raises(ValueError):
+        B.stencil3d_apply(d, a, torch.zeros((12, 12, 11), device=device()))
+    with pytest.raises(ValueError):
+        B.stencil3d_apply(d, a.double(), a.double())
