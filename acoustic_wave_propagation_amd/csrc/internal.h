@@ -16,9 +16,9 @@ struct Geometry {
     int tiles_x, tiles_y, nchunks, chunk_len, nwg;
 };
 
-// Geometry the kernel for (dtype, R) would use on a device with `cus`
+// Geometry the kernel for (dtype, R, op) would use on a device with `cus`
 // compute units.  Host only.
-Geometry plan_geometry(const stencil3d_desc &d, int cus);
+Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus);
 
 // Enqueue the streaming stencil.  wave == false: out = star(in) on the
 // interior.  wave == true: out = wave update of (u_prev, in = u, vel2, eta)

@@ -1,0 +1,533 @@
+// star2p5d_kernel.h -- device code of the 3D star stencil and the acoustic
+// wave step for gfx950.  Included by star2p5d.hip, which instantiates the
+// shipped tile configurations and launches them.
+//
+// Design (2.5D streaming, "Accelerating High-Order Stencils on GPUs",
+// st_reg_fixed description; "3D Stencil: Rotate the Depth Window Through
+// Registers"): a workgroup owns an XY tile of TX x TY outputs and walks it
+// through a chunk of z planes.  Each thread owns VX consecutive x outputs
+// on VY consecutive rows and keeps, for each of them, the values of its z
+// column in a register window: planes z-R..z+R plus D planes in flight.
+// Per z step:
+//   1. issue the loads of plane z+R+D (own columns, into the window slot
+//      that plane z-R-1 has just freed), of plane z+D's R-wide halo ring,
+//      and (wave step) of plane z+DE's u_prev, vel2 and eta;
+//   2. barrier; write plane z's own values (from the window, not re-read
+//      from HBM) and its halo ring into the one LDS tile; barrier;
+//   3. read the in-plane neighbours from LDS and the z neighbours from the
+//      window, evaluate, and store with a streaming store.
+// Each interior plane is read from HBM once per chunk; halo rings are
+// re-read by neighbouring tiles and mostly hit in L2 / the Infinity Cache.
+// D planes of loads stay in flight per thread, which is what covers the
+// HBM latency at the two or three waves per SIMD this register budget
+// allows.
+//
+// The window, halo and epilogue rings are indexed with compile-time slot
+// numbers: the z loop is unrolled by the least common multiple of the ring
+// sizes, so rotation costs no register moves (the index-rotation idea of
+// st_reg_fixed, expressed with templates).  All loads are issued through
+// buffer resources, unconditionally, so that the hardware wait counters
+// track exactly the loads a step depends on.
+//
+// gfx950 specifics: wave64; each row access of a wave is one coalesced
+// 16-byte-per-lane (dwordx4) access; LDS tile rows are padded so a group's
+// columns are 16-byte aligned (ds_read_b128 / ds_write_b128) and rows land
+// in different bank groups; workgroup ids are remapped so each XCD (own L2)
+// sweeps one contiguous band of tiles.  No MFMA: the stencil is not a
+// dense contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "stencil3d.h"
+
+namespace st {
+
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+template <typename T>
+struct StarArgs {
+    const T *in;      // stencil input (u for the wave step)
+    T *out;           // output (u_next for the wave step); may alias u_prev
+    const T *u_prev;  // wave step only
+    const T *vel2;
+    const T *eta;
+    int64_t pz;       // plane pitch in elements (nx * ny)
+    int32_t nx, ny, nz;
+    int32_t tiles_x, tiles_y, chunk_len, nwg;
+    T cc;             // centre weight, plain form
+    T ccd;            // centre weight of the difference form
+    T cx[ST_MAX_R], cy[ST_MAX_R], cz[ST_MAX_R];  // weight of offsets +-(k+1)
+};
+
+// Tile configuration: VX x VY outputs per thread, LX x LY threads per
+// workgroup, D planes of stencil-input prefetch, DE planes of wave-epilogue
+// prefetch (0: loaded in the step that uses them), LB LDS tile buffers
+// (2: one barrier per z step), alternating z direction of neighbouring
+// chunks, chunk-major (vs tile-major) order of the logical workgroup id,
+// XCD remap, nontemporal stores, nontemporal epilogue loads.
+template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, int LB_ = 2, bool ALT_ = true,
+          bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false, bool NTL_ = false>
+struct TileCfg {
+    static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
+    static constexpr bool ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_, NTL = NTL_;
+    static constexpr int NT = LX * LY, TX = LX * VX, TY = LY * VY;
+};
+
+constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
+constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
+constexpr int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+// LDS row pitch: at least `need` elements, a multiple of the group width,
+// and an odd multiple of 16 bytes so that the 16-byte accesses of lanes on
+// consecutive rows fall in different bank groups.
+template <typename T>
+constexpr int lds_pitch(int need, int vx) {
+    int p = round_up(need, vx);
+    while ((p * (int)sizeof(T)) % 16 != 0 || ((p * (int)sizeof(T)) / 16) % 2 == 0) p += vx;
+    return p;
+}
+
+// Bijection from the hardware workgroup id to a logical tile id such that
+// XCD k (which receives ids k, k+8, k+16, ...) owns one contiguous range of
+// logical ids.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    const int q = n / kXcds, r = n % kXcds;
+    const int xcd = b % kXcds, i = b / kXcds;
+    return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+}
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(std::forward<F>(f));
+    }
+}
+
+// ---- buffer addressing -----------------------------------------------------
+// Every plane is addressed through a buffer resource (V#) whose base is the
+// plane start (uniform, scalar registers) and whose num_records ends at the
+// allocation end (capped below 2^31).  Lanes carry 32-bit byte offsets that
+// stay fixed over the whole z sweep, so a load or store costs no vector
+// address arithmetic.  The hardware range check makes any access at or past
+// num_records return zeros (loads) or do nothing (stores): lanes whose data
+// is not needed use the offset kOOB, and loads that run past the end of the
+// last row of the array read zeros instead of faulting.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 family: 32-bit raw data
+constexpr uint32_t kOOB = 0x80000000u;        // >= every num_records we build
+constexpr int kAuxNT = 2;                     // cache policy: nontemporal
+
+// A plane that is not needed gets num_records = 0: its accesses are still
+// issued (so the instruction stream, and the wait counts the compiler
+// derives from it, do not depend on the chunk length) but touch no memory.
+__device__ __forceinline__ rsrc_t plane_rsrc(const void *base, int64_t bytes_left, bool needed) {
+    int64_t n = bytes_left < 0x7fffffff ? bytes_left : 0x7fffffff;
+    n = (needed && n > 0) ? n : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)n, kRsrcWord3);
+}
+
+// N consecutive elements at byte offset off (any element-aligned offset).
+template <typename T, int N, int AUX = 0>
+__device__ __forceinline__ void bload(rsrc_t r, uint32_t off, T (&v)[N]) {
+    constexpr int B = N * (int)sizeof(T);
+    static_assert(B % 4 == 0, "whole dwords");
+    uint32_t w[B / 4];
+    static_for<0, B / 16>([&](auto c) {
+        constexpr int k = decltype(c)::value;
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, AUX);
+        w[4 * k] = q.x, w[4 * k + 1] = q.y, w[4 * k + 2] = q.z, w[4 * k + 3] = q.w;
+    });
+    constexpr int done = B / 16 * 16, rem = B - done;
+    if constexpr (rem == 12) {
+        const u32x3 q = __builtin_amdgcn_raw_buffer_load_b96(r, off + done, 0, AUX);
+        w[done / 4] = q.x, w[done / 4 + 1] = q.y, w[done / 4 + 2] = q.z;
+    } else if constexpr (rem == 8) {
+        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, off + done, 0, AUX);
+        w[done / 4] = q.x, w[done / 4 + 1] = q.y;
+    } else if constexpr (rem == 4) {
+        w[done / 4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + done, 0, AUX);
+    }
+    __builtin_memcpy(v, w, B);
+}
+
+// N consecutive elements to byte offset off.
+template <typename T, int N, int AUX = 0>
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, const T (&v)[N]) {
+    constexpr int B = N * (int)sizeof(T);
+    uint32_t w[B / 4];
+    __builtin_memcpy(w, v, B);
+    static_for<0, B / 16>([&](auto c) {
+        constexpr int k = decltype(c)::value;
+        const u32x4 q = {w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(q, r, off + 16 * k, 0, AUX);
+    });
+    constexpr int done = B / 16 * 16, rem = B - done;
+    if constexpr (rem == 12) {
+        const u32x3 q = {w[done / 4], w[done / 4 + 1], w[done / 4 + 2]};
+        __builtin_amdgcn_raw_buffer_store_b96(q, r, off + done, 0, AUX);
+    } else if constexpr (rem == 8) {
+        const u32x2 q = {w[done / 4], w[done / 4 + 1]};
+        __builtin_amdgcn_raw_buffer_store_b64(q, r, off + done, 0, AUX);
+    } else if constexpr (rem == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(w[done / 4], r, off + done, 0, AUX);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void bstore1(rsrc_t r, uint32_t off, T v) {
+    T a[1] = {v};
+    bstore<T, 1>(r, off, a);
+}
+
+// Ring sizes of the kernel below, shared with the host so that z chunks can
+// be sized in whole unrolled blocks.
+template <int R, bool WAVE, class C>
+struct Rings {
+    static constexpr int D = C::D;                     // stencil-input prefetch depth
+    static constexpr int DE = WAVE ? C::DE : 0;        // epilogue prefetch depth
+    static constexpr int H = D + 1;                    // halo ring slots
+    // window slots: planes z-R..z+R plus D in flight, padded to a multiple
+    // of H so that the unroll stays short
+    static constexpr int W = round_up(2 * R + 1 + D, H);
+    static constexpr int E = DE + 1;                   // epilogue slots
+    static constexpr int U = clcm(clcm(clcm(W, H), E), C::LB);  // z-loop unroll
+};
+
+template <typename T, int R, bool WAVE, class C>
+__global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
+    constexpr int VX = C::VX, VY = C::VY, LX = C::LX;
+    constexpr int NT = C::NT, TX = C::TX, TY = C::TY;
+    using RG = Rings<R, WAVE, C>;
+    constexpr int D = RG::D, DE = RG::DE, H = RG::H, W = RG::W, E = RG::E, U = RG::U;
+    constexpr int PADL = round_up(R, VX);       // LDS column of tile x = 0
+    constexpr int LP = lds_pitch<T>(PADL + TX + R, VX);
+    constexpr int LROWS = TY + 2 * R;
+    constexpr int LTILE = LROWS * LP;           // one LDS tile buffer
+    constexpr int LDUMMY = C::LB * LTILE;       // sink for inactive halo lanes
+    constexpr int GX = TX / VX;                 // groups per tile row
+    constexpr int NYU = 2 * R * GX;             // y-halo units, VX wide
+    constexpr int NXU = 2 * TY;                 // x-halo units, R wide
+    constexpr int KY = (NYU + NT - 1) / NT;
+    constexpr int KX = (NXU + NT - 1) / NT;
+    constexpr uint32_t ES = sizeof(T);
+    constexpr int LAUX = C::NTL ? kAuxNT : 0, SAUX = C::NTS ? kAuxNT : 0;
+    // fp64: accumulate neighbour differences (u(p+-k) - u(p)), which keeps
+    // the rounding of smooth fields far below the fp64 tolerance.
+    constexpr bool DIFF = std::is_same<T, double>::value;
+    static_assert(D >= 1, "at least one plane in flight");
+    static_assert(C::LB == 1 || C::LB == 2, "one or two LDS tile buffers");
+
+    __shared__ __align__(16) T lds[LDUMMY + (VX > R ? VX : R)];
+
+    const int tid = threadIdx.x;
+    const int nx = a.nx, ny = a.ny;
+    const int wg = C::XCD ? xcd_remap(blockIdx.x, a.nwg) : (int)blockIdx.x;
+    const int ntile = a.tiles_x * a.tiles_y;
+    const int nchunks = a.nwg / ntile;
+    int chunk, trem;
+    if (C::CMAJ) {
+        chunk = wg / ntile;
+        trem = wg - chunk * ntile;
+    } else {
+        trem = wg / nchunks;
+        chunk = wg - trem * nchunks;
+    }
+    const int tyi = trem / a.tiles_x;
+    const int txi = trem - tyi * a.tiles_x;
+    const int gx0 = R + txi * TX;
+    const int gy0 = R + tyi * TY;
+    const int zs = R + chunk * a.chunk_len;
+    const int ze = min(zs + a.chunk_len, a.nz - R);
+    const int n = ze - zs;                      // planes of this chunk
+    // Odd chunks stream downwards, so two neighbouring chunks reach their
+    // shared boundary planes at the same time (both at their start, or both
+    // at their end) and the second read of those planes hits in cache.  The
+    // sums are symmetric in +-k, so the result does not depend on direction.
+    const int dir = (C::ALT && (chunk & 1)) ? -1 : 1;
+    const int z0 = dir > 0 ? zs : ze - 1;       // plane of step 0
+    const int64_t pzb = a.pz * (int64_t)ES;     // plane bytes
+    const int64_t totb = pzb * a.nz;            // allocation bytes
+    // some columns of this tile lie outside the interior (ragged x edge)
+    const bool xpart = gx0 + TX > nx - R;
+
+    // ---- own outputs: columns ox..ox+VX-1 on rows oy0..oy0+VY-1 ----------
+    const int lx = tid % LX, ly = tid / LX;
+    const int ox = gx0 + lx * VX;
+    const int oy0 = gy0 + ly * VY;
+    uint32_t ooff[VY];   // byte offset of (ox, oy0+j) in a plane
+    uint32_t soff[VY];   // same, or kOOB where row j is not written
+#pragma unroll
+    for (int j = 0; j < VY; ++j) {
+        ooff[j] = ((uint32_t)(oy0 + j) * (uint32_t)nx + (uint32_t)ox) * ES;
+        soff[j] = (oy0 + j < ny - R && ox < nx - R) ? ooff[j] : kOOB;
+    }
+    const int nvx = max(0, min(VX, nx - R - ox));  // written columns (ragged x)
+    const int lcol = PADL + lx * VX;
+    const int lrow0 = R + ly * VY;
+
+    // ---- halo ring units of this thread ----------------------------------
+    uint32_t hy_off[KY];
+    int hy_l[KY];
+#pragma unroll
+    for (int q = 0; q < KY; ++q) {
+        const int u = tid + q * NT;
+        const int uu = u < NYU ? u : 0;
+        const int rsel = uu / GX, g = uu - rsel * GX;
+        const int gy = rsel < R ? gy0 - R + rsel : gy0 + TY + (rsel - R);
+        hy_off[q] = u < NYU ? ((uint32_t)gy * (uint32_t)nx + (uint32_t)(gx0 + g * VX)) * ES : kOOB;
+        hy_l[q] = u < NYU ? (rsel < R ? rsel : TY + rsel) * LP + PADL + g * VX : -1;
+    }
+    uint32_t hx_off[KX];
+    int hx_l[KX];
+    const int ux0 = (tid - (NYU % NT) + NT) % NT;  // x units start after y
+#pragma unroll
+    for (int q = 0; q < KX; ++q) {
+        const int u = ux0 + q * NT;
+        const int uu = u < NXU ? u : 0;
+        const int side = uu / TY, row = uu - side * TY;
+        const int hx = side ? gx0 + TX : gx0 - R;
+        hx_off[q] = u < NXU ? ((uint32_t)(gy0 + row) * (uint32_t)nx + (uint32_t)hx) * ES : kOOB;
+        hx_l[q] = u < NXU ? (R + row) * LP + (side ? PADL + TX : PADL - R) : -1;
+    }
+
+    T win[W][VY][VX];
+    T hys[H][KY][VX];
+    T hxs[H][KX][R];
+    T up[E][VY][VX], v2[E][VY][VX], et[E][VY][VX];
+
+    // resource of the plane at step offset j from step k (empty if unneeded)
+    auto rsrc_at = [&](const T *base, int k, int j, bool needed) {
+        const int z = z0 + dir * (k + j);
+        return plane_rsrc((const char *)base + (int64_t)z * pzb, totb - (int64_t)z * pzb, needed);
+    };
+    // window slot s holds the plane at step offset s - R of the block start
+    auto load_window = [&](int k, int j, bool needed, auto slot_c) {
+        constexpr int s = decltype(slot_c)::value;
+        const rsrc_t r = rsrc_at(a.in, k, j, needed);
+#pragma unroll
+        for (int jj = 0; jj < VY; ++jj) bload<T, VX>(r, ooff[jj], win[s][jj]);
+    };
+    auto load_halo = [&](int k, bool needed, auto slot_c) {
+        constexpr int h = decltype(slot_c)::value;
+        const rsrc_t r = rsrc_at(a.in, k, 0, needed);
+#pragma unroll
+        for (int q = 0; q < KY; ++q) bload<T, VX>(r, hy_off[q], hys[h][q]);
+#pragma unroll
+        for (int q = 0; q < KX; ++q) bload<T, R>(r, hx_off[q], hxs[h][q]);
+    };
+    auto load_epilogue = [&](int k, bool needed, auto slot_c) {
+        constexpr int e = decltype(slot_c)::value;
+        const rsrc_t rp = rsrc_at(a.u_prev, k, 0, needed), rv = rsrc_at(a.vel2, k, 0, needed),
+                     re = rsrc_at(a.eta, k, 0, needed);
+#pragma unroll
+        for (int jj = 0; jj < VY; ++jj) {
+            bload<T, VX, LAUX>(rp, ooff[jj], up[e][jj]);
+            bload<T, VX, LAUX>(rv, ooff[jj], v2[e][jj]);
+            bload<T, VX, LAUX>(re, ooff[jj], et[e][jj]);
+        }
+    };
+
+    // prologue: window planes at step offsets -R .. R+D-1 into slots
+    // 0..2R+D-1, halo rings of steps 0..D-1, epilogue fields of steps
+    // 0..DE-1 (planes past the chunk's needs get an empty resource)
+    static_for<0, 2 * R + D>([&](auto s) {
+        constexpr int sv = decltype(s)::value;
+        load_window(0, sv - R, sv - R < n + R, s);
+    });
+    static_for<0, D>([&](auto h) {
+        constexpr int hv = decltype(h)::value;
+        load_halo(hv, hv < n, h);
+    });
+    if constexpr (WAVE)
+        static_for<0, DE>([&](auto e) {
+            constexpr int ev = decltype(e)::value;
+            load_epilogue(ev, ev < n, e);
+        });
+
+    // Whole blocks of U steps, with no exit inside a block: the instruction
+    // stream is then the same every block and the compiler's wait counts
+    // only cover loads at least D-1 steps old.  Steps past the chunk end run
+    // on empty resources (no memory traffic, stores dropped).
+    for (int k0 = 0; k0 < n; k0 += U) {
+        static_for<0, U>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr int CS = (kk + R) % W;           // window slot of step k
+            constexpr int LEAD = (kk + 2 * R + D) % W;  // slot of offset R+D
+            constexpr int HC = kk % H, HN = (kk + D) % H;
+            constexpr int EC = kk % E, EN = (kk + DE) % E;
+            constexpr int LB0 = (kk % C::LB) * LTILE;  // LDS buffer of this step
+            const int k = k0 + kk;
+            T *tile = lds + LB0;
+
+            // 1. prefetch (always issued; empty resource past the chunk)
+            load_window(k, R + D, k + D < n, std::integral_constant<int, LEAD>{});
+            load_halo(k + D, k + D < n, std::integral_constant<int, HN>{});
+            if constexpr (WAVE) load_epilogue(k + DE, k + DE < n, std::integral_constant<int, EN>{});
+
+            // 2. stage plane k in LDS: own values from the window, halo ring
+            //    from registers (inactive halo lanes write the sink).  With
+            //    one buffer, wait until last step's readers are done; with
+            //    two, the previous barrier already ordered them.
+            if constexpr (C::LB == 1) __syncthreads();
+#pragma unroll
+            for (int j = 0; j < VY; ++j)
+#pragma unroll
+                for (int i = 0; i < VX; ++i) tile[(lrow0 + j) * LP + lcol + i] = win[CS][j][i];
+#pragma unroll
+            for (int q = 0; q < KY; ++q) {
+                T *dst = hy_l[q] >= 0 ? tile + hy_l[q] : lds + LDUMMY;
+#pragma unroll
+                for (int i = 0; i < VX; ++i) dst[i] = hys[HC][q][i];
+            }
+#pragma unroll
+            for (int q = 0; q < KX; ++q) {
+                T *dst = hx_l[q] >= 0 ? tile + hx_l[q] : lds + LDUMMY;
+#pragma unroll
+                for (int i = 0; i < R; ++i) dst[i] = hxs[HC][q][i];
+            }
+            __syncthreads();
+
+            // 3. in-plane neighbours from LDS
+            T xs[VY][VX + 2 * R];  // row segment, columns ox-R .. ox+VX+R-1
+#pragma unroll
+            for (int j = 0; j < VY; ++j) {
+                const T *row = tile + (lrow0 + j) * LP + lcol;
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    xs[j][m] = row[m - R];
+                    xs[j][R + VX + m] = row[VX + m];
+                }
+#pragma unroll
+                for (int i = 0; i < VX; ++i) xs[j][R + i] = win[CS][j][i];
+            }
+            T ys[2 * R][VX];  // rows oy0-R..oy0-1 and oy0+VY..oy0+VY+R-1
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < VX; ++i) {
+                    ys[r][i] = tile[(lrow0 - R + r) * LP + lcol + i];
+                    ys[R + r][i] = tile[(lrow0 + VY + r) * LP + lcol + i];
+                }
+
+            T res[VY][VX];
+#pragma unroll
+            for (int j = 0; j < VY; ++j)
+#pragma unroll
+                for (int i = 0; i < VX; ++i) {
+                    const T ctr = win[CS][j][i];
+                    T acc = (DIFF ? a.ccd : a.cc) * ctr;
+#pragma unroll
+                    for (int kz = 1; kz <= R; ++kz) {
+                        const T zm = win[(CS + W - kz) % W][j][i];
+                        const T zp = win[(CS + kz) % W][j][i];
+                        const T xm = xs[j][R + i - kz], xp = xs[j][R + i + kz];
+                        const int qm = j - kz, qp = j + kz;
+                        const T ym = qm < 0 ? ys[R + qm][i] : win[CS][qm][i];
+                        const T yp = qp >= VY ? ys[R + qp - VY][i] : win[CS][qp][i];
+                        if constexpr (DIFF) {
+                            acc = fma(a.cz[kz - 1], (zm - ctr) + (zp - ctr), acc);
+                            acc = fma(a.cy[kz - 1], (ym - ctr) + (yp - ctr), acc);
+                            acc = fma(a.cx[kz - 1], (xm - ctr) + (xp - ctr), acc);
+                        } else {
+                            acc = fma(a.cz[kz - 1], zm + zp, acc);
+                            acc = fma(a.cy[kz - 1], ym + yp, acc);
+                            acc = fma(a.cx[kz - 1], xm + xp, acc);
+                        }
+                    }
+                    if constexpr (WAVE) {
+                        // the weights carry dt^2/h^2: acc = dt^2 * Lap(u)
+                        const T e = et[EC][j][i];
+                        acc = (T(2) * ctr - (T(1) - e) * up[EC][j][i] + v2[EC][j][i] * acc) /
+                              (T(1) + e);
+                    }
+                    res[j][i] = acc;
+                }
+
+            // 4. store the written part: rows outside the interior carry
+            //    kOOB; a tile on the ragged x edge stores element by element
+            const rsrc_t ro = rsrc_at(a.out, k, 0, k < n);
+            if (!xpart) {
+#pragma unroll
+                for (int j = 0; j < VY; ++j) bstore<T, VX, SAUX>(ro, soff[j], res[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VY; ++j)
+#pragma unroll
+                    for (int i = 0; i < VX; ++i)
+                        bstore1<T>(ro, i < nvx ? soff[j] + i * ES : kOOB, res[j][i]);
+            }
+        });
+    }
+}
+
+// out = in on every non-interior point; one wave per (y, z) row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+    shell_copy_kernel(const T *__restrict__ in, T *__restrict__ out, int nx, int ny, int nz,
+                      int R) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t rows = (int64_t)ny * nz;
+    for (int64_t row = wave; row < rows; row += nwaves) {
+        const int z = (int)(row / ny), y = (int)(row - (int64_t)z * ny);
+        const T *s = in + row * nx;
+        T *d = out + row * nx;
+        if (z < R || z >= nz - R || y < R || y >= ny - R) {
+            for (int x = lane; x < nx; x += 64) d[x] = s[x];
+        } else if (lane < 2 * R) {
+            const int x = lane < R ? lane : nx - 2 * R + lane;
+            d[x] = s[x];
+        }
+    }
+}
+
+template <typename T>
+__global__ void add_source_kernel(T *u, int64_t idx, T value) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) u[idx] += value;
+}
+
+// Fill StarArgs from a descriptor: weights combined in fp64, scaled by
+// wscale (1, or dt^2/h^2 for the wave step) and rounded once to T.
+template <typename T, int R>
+StarArgs<T> make_args(const stencil3d_desc &d, const void *in, void *out, const void *u_prev,
+                      const void *vel2, const void *eta, double wscale, int tiles_x,
+                      int tiles_y, int chunk_len, int nwg) {
+    StarArgs<T> a;
+    a.in = static_cast<const T *>(in);
+    a.out = static_cast<T *>(out);
+    a.u_prev = static_cast<const T *>(u_prev);
+    a.vel2 = static_cast<const T *>(vel2);
+    a.eta = static_cast<const T *>(eta);
+    a.pz = d.nx * d.ny;
+    a.nx = (int32_t)d.nx;
+    a.ny = (int32_t)d.ny;
+    a.nz = (int32_t)d.nz;
+    a.tiles_x = tiles_x;
+    a.tiles_y = tiles_y;
+    a.chunk_len = chunk_len;
+    a.nwg = nwg;
+    const double cc = d.cx[0] + d.cy[0] + d.cz[0];
+    double ksum = 0.0;
+    for (int k = 1; k <= R; ++k) ksum += d.cx[k] + d.cy[k] + d.cz[k];
+    a.cc = (T)(wscale * cc);
+    a.ccd = (T)(wscale * (cc + 2.0 * ksum));
+    for (int k = 0; k < ST_MAX_R; ++k) {
+        const bool on = k < R;
+        a.cx[k] = on ? (T)(wscale * d.cx[k + 1]) : T(0);
+        a.cy[k] = on ? (T)(wscale * d.cy[k + 1]) : T(0);
+        a.cz[k] = on ? (T)(wscale * d.cz[k + 1]) : T(0);
+    }
+    return a;
+}
+
+}  // namespace st

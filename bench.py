@@ -19,7 +19,6 @@ but the timed stencil launches (for profiler runs).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -34,20 +33,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
           "R=4 25-pt stencil at 512³ fp32")
-KERNEL_SOURCES = ["acoustic_wave_propagation_amd/csrc/star2p5d.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "star2p5d_r4_512cube_traffic.md")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel: str):
@@ -59,6 +49,7 @@ def recorded_traffic(kernel: str):
     m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
     t = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
                   re.escape(kernel), text)
+    from acoustic_wave_propagation_amd.profiling import kernel_hash
     if not m or not t or m.group(1) != kernel_hash():
         return None
     return float(t.group(1))
