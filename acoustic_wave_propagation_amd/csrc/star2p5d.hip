@@ -10,24 +10,26 @@
 namespace st {
 namespace {
 
-// Shipped configurations per element type, chosen by timing on MI355X
-// (tile sweep over outputs per thread, threads per workgroup, prefetch
-// depth, LDS buffering and z chunking):
-//   fp32: 4 x 2 outputs per thread, 32 x 16 threads -> 128 x 32 tile
-//   fp64: 2 x 2 outputs per thread, 32 x 16 threads ->  64 x 32 tile
-// two planes of stencil-input prefetch, one of wave-epilogue prefetch, two
-// LDS tile buffers (one barrier per z step).
+// Shipped configurations per element type, chosen by timing and traffic
+// counters on MI355X (sweep over outputs per thread, threads per workgroup,
+// prefetch depth, halo timing, LDS buffering, chunking, store policy):
+//   fp32 apply: 4 x 2 outputs per thread, 64 x 8 threads  -> 256 x 16 tile,
+//               nontemporal stores
+//   fp32 wave:  4 x 2 outputs per thread, 32 x 16 threads -> 128 x 32 tile
+//   fp64:       2 x 2 outputs per thread, 32 x 16 threads ->  64 x 32 tile
+// one plane of stencil-input prefetch, halo ring loaded with the window's
+// leading plane, two LDS tile buffers (one barrier per z step).
 template <typename T>
 struct Shipped;
 template <>
 struct Shipped<float> {
-    using Apply = TileCfg<4, 2, 32, 16, 2, 0>;
-    using Wave = TileCfg<4, 2, 32, 16, 2, 1>;
+    using Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
+    using Wave = TileCfg<4, 2, 32, 16, 1, 0>;
 };
 template <>
 struct Shipped<double> {
-    using Apply = TileCfg<2, 2, 32, 16, 2, 0>;
-    using Wave = TileCfg<2, 2, 32, 16, 2, 1>;
+    using Apply = TileCfg<2, 2, 32, 16, 1, 0>;
+    using Wave = TileCfg<2, 2, 32, 16, 1, 0>;
 };
 
 template <typename T, int R>

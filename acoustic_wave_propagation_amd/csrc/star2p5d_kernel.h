@@ -10,14 +10,15 @@
 // column in a register window: planes z-R..z+R plus D planes in flight.
 // Per z step:
 //   1. issue the loads of plane z+R+D (own columns, into the window slot
-//      that plane z-R-1 has just freed), of plane z+D's R-wide halo ring,
-//      and (wave step) of plane z+DE's u_prev, vel2 and eta;
+//      that plane z-R-1 has just freed) and of the same plane's R-wide halo
+//      ring, and (wave step) of plane z+DE's u_prev, vel2 and eta;
 //   2. barrier; write plane z's own values (from the window, not re-read
 //      from HBM) and its halo ring into the one LDS tile; barrier;
 //   3. read the in-plane neighbours from LDS and the z neighbours from the
 //      window, evaluate, and store with a streaming store.
-// Each interior plane is read from HBM once per chunk; halo rings are
-// re-read by neighbouring tiles and mostly hit in L2 / the Infinity Cache.
+// Each interior plane is read from HBM once per chunk; a tile's halo ring
+// is loaded in the same step in which the neighbouring tiles (same XCD)
+// load those rows as their own window, so the ring is served from L2.
 // D planes of loads stay in flight per thread, which is what covers the
 // HBM latency at the two or three waves per SIMD this register budget
 // allows.
@@ -66,15 +67,21 @@ struct StarArgs {
 
 // Tile configuration: VX x VY outputs per thread, LX x LY threads per
 // workgroup, D planes of stencil-input prefetch, DE planes of wave-epilogue
-// prefetch (0: loaded in the step that uses them), LB LDS tile buffers
+// prefetch (0: loaded in the step that uses them), halo ring loaded in the
+// same step as the window's leading load of that plane (HLA) or D steps
+// ahead of its use, LB LDS tile buffers
 // (2: one barrier per z step), alternating z direction of neighbouring
 // chunks, chunk-major (vs tile-major) order of the logical workgroup id,
-// XCD remap, nontemporal stores, nontemporal epilogue loads.
-template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, int LB_ = 2, bool ALT_ = true,
-          bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false, bool NTL_ = false>
+// XCD remap, nontemporal stores, nontemporal epilogue loads, minimum waves
+// per SIMD the register allocation must allow.
+template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
+          bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
+          bool NTL_ = false, int MINW_ = 1>
 struct TileCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
-    static constexpr bool ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_, NTL = NTL_;
+    static constexpr int MINW = MINW_;  // register budget for >= MINW waves per SIMD
+    static constexpr bool HLA = HLA_, ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_,
+                          NTL = NTL_;
     static constexpr int NT = LX * LY, TX = LX * VX, TY = LY * VY;
 };
 
@@ -194,7 +201,12 @@ template <int R, bool WAVE, class C>
 struct Rings {
     static constexpr int D = C::D;                     // stencil-input prefetch depth
     static constexpr int DE = WAVE ? C::DE : 0;        // epilogue prefetch depth
-    static constexpr int H = D + 1;                    // halo ring slots
+    // Halo lead: steps between loading a plane's halo ring and staging it.
+    // R + D loads it together with the window's leading load of the same
+    // plane -- the step in which the neighbouring tiles load that plane's
+    // rows as their own window -- so the ring is served from L2.
+    static constexpr int HL = C::HLA ? R + D : D;
+    static constexpr int H = HL + 1;                   // halo ring slots
     // window slots: planes z-R..z+R plus D in flight, padded to a multiple
     // of H so that the unroll stays short
     static constexpr int W = round_up(2 * R + 1 + D, H);
@@ -203,21 +215,25 @@ struct Rings {
 };
 
 template <typename T, int R, bool WAVE, class C>
-__global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
+star2p5d_kernel(StarArgs<T> a) {
     constexpr int VX = C::VX, VY = C::VY, LX = C::LX;
     constexpr int NT = C::NT, TX = C::TX, TY = C::TY;
     using RG = Rings<R, WAVE, C>;
-    constexpr int D = RG::D, DE = RG::DE, H = RG::H, W = RG::W, E = RG::E, U = RG::U;
-    constexpr int PADL = round_up(R, VX);       // LDS column of tile x = 0
-    constexpr int LP = lds_pitch<T>(PADL + TX + R, VX);
+    constexpr int D = RG::D, DE = RG::DE, HL = RG::HL, H = RG::H, W = RG::W, E = RG::E,
+                  U = RG::U;
+    // Halo ring in units of VX elements: R rows above and below the tile,
+    // and XW units (XW*VX >= R columns) left and right of each tile row.
+    constexpr int XW = (R + VX - 1) / VX;
+    constexpr int PADL = XW * VX;               // LDS column of tile x = 0
+    constexpr int LP = lds_pitch<T>(PADL + TX + XW * VX, VX);
     constexpr int LROWS = TY + 2 * R;
     constexpr int LTILE = LROWS * LP;           // one LDS tile buffer
     constexpr int LDUMMY = C::LB * LTILE;       // sink for inactive halo lanes
     constexpr int GX = TX / VX;                 // groups per tile row
-    constexpr int NYU = 2 * R * GX;             // y-halo units, VX wide
-    constexpr int NXU = 2 * TY;                 // x-halo units, R wide
-    constexpr int KY = (NYU + NT - 1) / NT;
-    constexpr int KX = (NXU + NT - 1) / NT;
+    constexpr int NYU = 2 * R * GX;             // y-halo units
+    constexpr int NXU = 2 * TY * XW;            // x-halo units
+    constexpr int KH = (NYU + NXU + NT - 1) / NT;  // halo units per thread
     constexpr uint32_t ES = sizeof(T);
     constexpr int LAUX = C::NTL ? kAuxNT : 0, SAUX = C::NTS ? kAuxNT : 0;
     // fp64: accumulate neighbour differences (u(p+-k) - u(p)), which keeps
@@ -226,7 +242,7 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
     static_assert(D >= 1, "at least one plane in flight");
     static_assert(C::LB == 1 || C::LB == 2, "one or two LDS tile buffers");
 
-    __shared__ __align__(16) T lds[LDUMMY + (VX > R ? VX : R)];
+    __shared__ __align__(16) T lds[LDUMMY + VX];
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny;
@@ -275,33 +291,35 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
     const int lrow0 = R + ly * VY;
 
     // ---- halo ring units of this thread ----------------------------------
-    uint32_t hy_off[KY];
-    int hy_l[KY];
+    // unit u: [0, NYU) rows above/below, [NYU, NYU+NXU) left/right columns,
+    // beyond: inactive (offset kOOB, LDS sink)
+    uint32_t h_off[KH];
+    int h_l[KH];
 #pragma unroll
-    for (int q = 0; q < KY; ++q) {
+    for (int q = 0; q < KH; ++q) {
         const int u = tid + q * NT;
-        const int uu = u < NYU ? u : 0;
-        const int rsel = uu / GX, g = uu - rsel * GX;
-        const int gy = rsel < R ? gy0 - R + rsel : gy0 + TY + (rsel - R);
-        hy_off[q] = u < NYU ? ((uint32_t)gy * (uint32_t)nx + (uint32_t)(gx0 + g * VX)) * ES : kOOB;
-        hy_l[q] = u < NYU ? (rsel < R ? rsel : TY + rsel) * LP + PADL + g * VX : -1;
-    }
-    uint32_t hx_off[KX];
-    int hx_l[KX];
-    const int ux0 = (tid - (NYU % NT) + NT) % NT;  // x units start after y
-#pragma unroll
-    for (int q = 0; q < KX; ++q) {
-        const int u = ux0 + q * NT;
-        const int uu = u < NXU ? u : 0;
-        const int side = uu / TY, row = uu - side * TY;
-        const int hx = side ? gx0 + TX : gx0 - R;
-        hx_off[q] = u < NXU ? ((uint32_t)(gy0 + row) * (uint32_t)nx + (uint32_t)hx) * ES : kOOB;
-        hx_l[q] = u < NXU ? (R + row) * LP + (side ? PADL + TX : PADL - R) : -1;
+        if (u < NYU) {
+            const int rsel = u / GX, g = u - rsel * GX;
+            const int gy = rsel < R ? gy0 - R + rsel : gy0 + TY + (rsel - R);
+            h_off[q] = ((uint32_t)gy * (uint32_t)nx + (uint32_t)(gx0 + g * VX)) * ES;
+            h_l[q] = (rsel < R ? rsel : TY + rsel) * LP + PADL + g * VX;
+        } else if (u < NYU + NXU) {
+            const int xu = u - NYU;
+            const int side = xu / (TY * XW), rem = xu - side * (TY * XW);
+            const int row = rem / XW, c = rem - row * XW;
+            // left units start PADL >= R columns before the tile (columns
+            // left of x = 0 land in LDS columns nothing reads)
+            const int gx = side ? gx0 + TX + c * VX : gx0 - PADL + c * VX;
+            h_off[q] = ((uint32_t)(gy0 + row) * (uint32_t)nx + (uint32_t)gx) * ES;
+            h_l[q] = (R + row) * LP + (side ? PADL + TX : 0) + c * VX;
+        } else {
+            h_off[q] = kOOB;
+            h_l[q] = -1;
+        }
     }
 
     T win[W][VY][VX];
-    T hys[H][KY][VX];
-    T hxs[H][KX][R];
+    T hs[H][KH][VX];
     T up[E][VY][VX], v2[E][VY][VX], et[E][VY][VX];
 
     // resource of the plane at step offset j from step k (empty if unneeded)
@@ -320,9 +338,7 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
         constexpr int h = decltype(slot_c)::value;
         const rsrc_t r = rsrc_at(a.in, k, 0, needed);
 #pragma unroll
-        for (int q = 0; q < KY; ++q) bload<T, VX>(r, hy_off[q], hys[h][q]);
-#pragma unroll
-        for (int q = 0; q < KX; ++q) bload<T, R>(r, hx_off[q], hxs[h][q]);
+        for (int q = 0; q < KH; ++q) bload<T, VX>(r, h_off[q], hs[h][q]);
     };
     auto load_epilogue = [&](int k, bool needed, auto slot_c) {
         constexpr int e = decltype(slot_c)::value;
@@ -337,13 +353,13 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
     };
 
     // prologue: window planes at step offsets -R .. R+D-1 into slots
-    // 0..2R+D-1, halo rings of steps 0..D-1, epilogue fields of steps
+    // 0..2R+D-1, halo rings of steps 0..HL-1, epilogue fields of steps
     // 0..DE-1 (planes past the chunk's needs get an empty resource)
     static_for<0, 2 * R + D>([&](auto s) {
         constexpr int sv = decltype(s)::value;
         load_window(0, sv - R, sv - R < n + R, s);
     });
-    static_for<0, D>([&](auto h) {
+    static_for<0, HL>([&](auto h) {
         constexpr int hv = decltype(h)::value;
         load_halo(hv, hv < n, h);
     });
@@ -362,7 +378,7 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
             constexpr int kk = decltype(kc)::value;
             constexpr int CS = (kk + R) % W;           // window slot of step k
             constexpr int LEAD = (kk + 2 * R + D) % W;  // slot of offset R+D
-            constexpr int HC = kk % H, HN = (kk + D) % H;
+            constexpr int HC = kk % H, HN = (kk + HL) % H;
             constexpr int EC = kk % E, EN = (kk + DE) % E;
             constexpr int LB0 = (kk % C::LB) * LTILE;  // LDS buffer of this step
             const int k = k0 + kk;
@@ -370,7 +386,7 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
 
             // 1. prefetch (always issued; empty resource past the chunk)
             load_window(k, R + D, k + D < n, std::integral_constant<int, LEAD>{});
-            load_halo(k + D, k + D < n, std::integral_constant<int, HN>{});
+            load_halo(k + HL, k + HL < n, std::integral_constant<int, HN>{});
             if constexpr (WAVE) load_epilogue(k + DE, k + DE < n, std::integral_constant<int, EN>{});
 
             // 2. stage plane k in LDS: own values from the window, halo ring
@@ -383,16 +399,10 @@ __global__ void __launch_bounds__(C::NT) star2p5d_kernel(StarArgs<T> a) {
 #pragma unroll
                 for (int i = 0; i < VX; ++i) tile[(lrow0 + j) * LP + lcol + i] = win[CS][j][i];
 #pragma unroll
-            for (int q = 0; q < KY; ++q) {
-                T *dst = hy_l[q] >= 0 ? tile + hy_l[q] : lds + LDUMMY;
+            for (int q = 0; q < KH; ++q) {
+                T *dst = h_l[q] >= 0 ? tile + h_l[q] : lds + LDUMMY;
 #pragma unroll
-                for (int i = 0; i < VX; ++i) dst[i] = hys[HC][q][i];
-            }
-#pragma unroll
-            for (int q = 0; q < KX; ++q) {
-                T *dst = hx_l[q] >= 0 ? tile + hx_l[q] : lds + LDUMMY;
-#pragma unroll
-                for (int i = 0; i < R; ++i) dst[i] = hxs[HC][q][i];
+                for (int i = 0; i < VX; ++i) dst[i] = hs[HC][q][i];
             }
             __syncthreads();
 
