@@ -323,3 +323,122 @@ def test_gpu_rejects_bad_arguments(torch_dev):
         B.stencil3d_apply(d, a, torch.zeros((12, 12, 11), device=device()))
     with pytest.raises(ValueError):
         B.stencil3d_apply(d, a.double(), a.double())
+
+
+# --------------------------------------------------------------------------
+# More paths: fp64 wave, other radii, loop entry points, degenerate weights,
+# the largest plane the 32-bit in-plane offsets allow
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,R", [(np.float64, 4), (np.float32, 1),
+                                     (np.float32, 2), (np.float64, 3)])
+def test_wave_step_dtypes_and_radii(oracle_mod, torch_dev, dtype, R):
+    torch, _ = torch_dev
+    shape = (23 + 2 * R, 41 + 2 * R, 139 + 2 * R)
+    log("case wave R=%d %s %s" % (R, np.dtype(dtype).name, shape))
+    up = wl.uniform_planes(shape, 61, -1, 1, dtype=dtype)
+    uc = wl.uniform_planes(shape, 62, -1, 1, dtype=dtype)
+    v2 = wl.uniform_planes(shape, 63, 1.5e3 ** 2, 4.5e3 ** 2, dtype=dtype)
+    et = wl.uniform_planes(shape, 64, 0.0, 0.1, dtype=dtype)
+    d = B.desc_init("f32" if dtype == np.float32 else "f64", shape, R)
+    t = [upload(a) for a in (up, uc, v2, et)]
+    out = sentinel_like(shape, dtype)
+    B.wave_step(d, t[0], t[1], out, t[2], t[3], 1e-3, 10.0)
+    got = out.cpu().numpy()
+    ref = oracle_mod.wave_step(up, uc, v2, et, R, list(d.cx[:R + 1]), 1e-3,
+                               10.0)
+    check_close(interior(got, R), interior(ref, R), _tol(dtype),
+                "wave R=%d %s" % (R, np.dtype(dtype).name))
+    check_halo_untouched(got, R, "wave")
+
+
+def test_jacobi_zero_one_sweeps(oracle_mod, torch_dev):
+    torch, _ = torch_dev
+    shape = (20, 33, 70)
+    u = wl.uniform_planes(shape, 71, -1, 1)
+    d = B.desc_init("f32", shape, 1, B.DIRICHLET_COPY)
+    b0, b1 = upload(u), sentinel_like(shape, np.float32)
+    assert B.stencil3d_jacobi(d, b0, b1, 0) is b0
+    assert np.array_equal(b0.cpu().numpy(), u)
+    mask = np.ones(shape, bool)
+    mask[1:-1, 1:-1, 1:-1] = False
+    assert np.array_equal(b1.cpu().numpy()[mask], u[mask])  # boundary set
+    b0, b1 = upload(u), sentinel_like(shape, np.float32)
+    res = B.stencil3d_jacobi(d, b0, b1, 1)
+    assert res is b1
+    ref = oracle_mod.jacobi(u, 1, 1, list(d.cx[:2]))
+    check_close(res.cpu().numpy(), ref, F32_TOL, "jacobi 1 sweep")
+
+
+@pytest.mark.parametrize("nsteps", [0, 1, 3])
+def test_wave_run_buffer_roles(oracle_mod, torch_dev, nsteps):
+    """wave_run leaves the newest field in u for even step counts and in
+    u_prev for odd ones, bit-identical to explicit steps."""
+    torch, _ = torch_dev
+    R = 4
+    shape = (30, 35, 77)
+    up0 = wl.uniform_planes(shape, 81, -1, 1)
+    u0 = wl.uniform_planes(shape, 82, -1, 1)
+    v2 = upload(wl.uniform_planes(shape, 83, 1.5e3 ** 2, 4.5e3 ** 2))
+    et = upload(wl.uniform_planes(shape, 84, 0.0, 0.1))
+    d = B.desc_init("f32", shape, R)
+    src = (40, 17, 15)
+    trace = [0.3, -0.2, 0.1]
+    a, b = upload(up0), upload(u0)
+    for n in range(nsteps):
+        B.wave_step(d, a, b, a, v2, et, 1e-3, 10.0)
+        B.wave_add_source(d, a, *src, trace[n])
+        a, b = b, a
+    pa, pb = upload(up0), upload(u0)
+    old, new = B.wave_run(d, pa, pb, v2, et, 1e-3, 10.0, nsteps, src, trace)
+    assert (new is pb) == (nsteps % 2 == 0)
+    assert np.array_equal(new.cpu().numpy(), b.cpu().numpy())
+    assert np.array_equal(old.cpu().numpy(), a.cpu().numpy())
+    if nsteps == 0:
+        assert np.array_equal(new.cpu().numpy(), u0)
+
+
+def test_zero_weights_give_zero(torch_dev):
+    torch, _ = torch_dev
+    shape = (14, 19, 37)
+    d = B.desc_init("f32", shape, 4)
+    for k in range(5):
+        d.cx[k] = d.cy[k] = d.cz[k] = 0.0
+    u = upload(wl.uniform_planes(shape, 91, -1, 1))
+    out = sentinel_like(shape, np.float32)
+    B.stencil3d_apply(d, u, out)
+    got = out.cpu().numpy()
+    assert np.all(interior(got, 4) == 0.0)
+    check_halo_untouched(got, 4, "zero weights")
+
+
+def test_largest_plane(oracle_mod, torch_dev):
+    """nx*ny*4 bytes just under 2^31 (the limit of the 32-bit in-plane
+    offsets): R=1, three planes.  Checked on oracle-computed regions at the
+    plane's corners, edges and centre."""
+    torch, _ = torch_dev
+    nz, ny, nx = 3, 16383, 32768
+    assert nx * ny * 4 < 2 ** 31
+    shape = (nz, ny, nx)
+    log("case largest plane %s" % (shape,))
+    u = upload_planes(lambda a, b: wl.uniform_planes(shape, 95, -1, 1, a, b),
+                      shape, np.float32, slab=1)
+    d = B.desc_init("f32", shape, 1)
+    out = torch.full(shape, SENTINEL, dtype=torch.float32, device=device())
+    B.stencil3d_apply(d, u, out)
+    torch.cuda.synchronize()
+    c = list(d.cx[:2])
+    h = 40
+    for y0 in (0, ny // 2, ny - h):
+        for x0 in (0, nx // 2 - 7, nx - h):
+            region_in = u[:, y0:y0 + h, x0:x0 + h].cpu().numpy()
+            ref = oracle_mod.star_apply(region_in, 1, c)
+            got = out[:, y0:y0 + h, x0:x0 + h].cpu().numpy()
+            # compare where the region's interior is also the grid interior
+            sl = (slice(1, 2), slice(1, h - 1), slice(1, h - 1))
+            check_close(got[sl], ref[sl], F32_TOL,
+                        "largest plane at (%d,%d)" % (y0, x0))
+            if y0 == 0:
+                assert np.all(got[:, 0, :] == np.float32(SENTINEL))
+            if x0 == nx - h:
+                assert np.all(got[:, :, -1] == np.float32(SENTINEL))
+    assert np.all(out[0].cpu().numpy() == np.float32(SENTINEL))
