@@ -32,7 +32,8 @@ class Desc(ctypes.Structure):
                 ("boundary", ctypes.c_int32),
                 ("cx", ctypes.c_double * (ST_MAX_R + 1)),
                 ("cy", ctypes.c_double * (ST_MAX_R + 1)),
-                ("cz", ctypes.c_double * (ST_MAX_R + 1))]
+                ("cz", ctypes.c_double * (ST_MAX_R + 1)),
+                ("pml_width", ctypes.c_int64)]
 
     @property
     def shape(self):

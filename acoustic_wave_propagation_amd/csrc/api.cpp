@@ -127,6 +127,7 @@ int stencil3d_desc_validate(const stencil3d_desc *d) {
     for (int k = 0; k <= d->radius; ++k)
         if (!isfinite(d->cx[k]) || !isfinite(d->cy[k]) || !isfinite(d->cz[k]))
             return ST_ERR_COEFF;
+    if (d->pml_width < 0) return ST_ERR_ARG;
     return ST_OK;
 }
 

@@ -60,6 +60,7 @@ struct StarArgs {
     int64_t pz;       // plane pitch in elements (nx * ny)
     int32_t nx, ny, nz;
     int32_t tiles_x, tiles_y, chunk_len, nwg;
+    int32_t pml;      // eta is zero this far inside the interior (0: no claim)
     T cc;             // centre weight, plain form
     T ccd;            // centre weight of the difference form
     T cx[ST_MAX_R], cy[ST_MAX_R], cz[ST_MAX_R];  // weight of offsets +-(k+1)
@@ -76,10 +77,11 @@ struct StarArgs {
 // per SIMD the register allocation must allow.
 template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
           bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
-          bool NTL_ = false, int MINW_ = 1>
+          bool NTL_ = false, int MINW_ = 1, bool ETILE_ = false>
 struct TileCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
     static constexpr int MINW = MINW_;  // register budget for >= MINW waves per SIMD
+    static constexpr bool ETILE = ETILE_;  // data-region skip per tile (else per lane)
     static constexpr bool HLA = HLA_, ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_,
                           NTL = NTL_;
     static constexpr int NT = LX * LY, TX = LX * VX, TY = LY * VY;
@@ -274,6 +276,15 @@ star2p5d_kernel(StarArgs<T> a) {
     const int64_t totb = pzb * a.nz;            // allocation bytes
     // some columns of this tile lie outside the interior (ragged x edge)
     const bool xpart = gx0 + TX > nx - R;
+    // Data regions of the wave step: on planes and rows where the caller
+    // guarantees eta = 0 (at least pml points inside the interior), a lane
+    // whose columns are all inside too reads eta at offset kOOB -- the load
+    // returns 0, the value it would have read, without a memory request.
+    const int pml = a.pml;
+    const int zin0 = R + pml, zin1 = a.nz - R - pml;  // inner planes
+    const bool tile_inner = pml > 0 && gx0 >= R + pml && gy0 >= R + pml &&
+                            min(gx0 + TX, nx - R) <= nx - R - pml &&
+                            min(gy0 + TY, ny - R) <= ny - R - pml;
 
     // ---- own outputs: columns ox..ox+VX-1 on rows oy0..oy0+VY-1 ----------
     const int lx = tid % LX, ly = tid / LX;
@@ -287,6 +298,13 @@ star2p5d_kernel(StarArgs<T> a) {
         soff[j] = (oy0 + j < ny - R && ox < nx - R) ? ooff[j] : kOOB;
     }
     const int nvx = max(0, min(VX, nx - R - ox));  // written columns (ragged x)
+    uint32_t eoff[VY];   // eta offset on inner planes: kOOB where eta = 0
+    const bool x_inner = ox >= R + pml && ox + VX <= nx - R - pml;
+#pragma unroll
+    for (int j = 0; j < VY; ++j) {
+        const bool y_inner = oy0 + j >= R + pml && oy0 + j < ny - R - pml;
+        eoff[j] = (pml > 0 && x_inner && y_inner) ? kOOB : ooff[j];
+    }
     const int lcol = PADL + lx * VX;
     const int lrow0 = R + ly * VY;
 
@@ -342,13 +360,15 @@ star2p5d_kernel(StarArgs<T> a) {
     };
     auto load_epilogue = [&](int k, bool needed, auto slot_c) {
         constexpr int e = decltype(slot_c)::value;
+        const int z = z0 + dir * k;
+        const bool z_inner = z >= zin0 && z < zin1;
         const rsrc_t rp = rsrc_at(a.u_prev, k, 0, needed), rv = rsrc_at(a.vel2, k, 0, needed),
-                     re = rsrc_at(a.eta, k, 0, needed);
+                     re = rsrc_at(a.eta, k, 0, needed && !(C::ETILE && tile_inner && z_inner));
 #pragma unroll
         for (int jj = 0; jj < VY; ++jj) {
             bload<T, VX, LAUX>(rp, ooff[jj], up[e][jj]);
             bload<T, VX, LAUX>(rv, ooff[jj], v2[e][jj]);
-            bload<T, VX, LAUX>(re, ooff[jj], et[e][jj]);
+            bload<T, VX, LAUX>(re, (!C::ETILE && z_inner) ? eoff[jj] : ooff[jj], et[e][jj]);
         }
     };
 
@@ -526,6 +546,7 @@ StarArgs<T> make_args(const stencil3d_desc &d, const void *in, void *out, const 
     a.tiles_y = tiles_y;
     a.chunk_len = chunk_len;
     a.nwg = nwg;
+    a.pml = d.pml_width > 0x3fffffff ? 0x3fffffff : (int32_t)d.pml_width;
     const double cc = d.cx[0] + d.cy[0] + d.cz[0];
     double ksum = 0.0;
     for (int k = 1; k <= R; ++k) ksum += d.cx[k] + d.cy[k] + d.cz[k];

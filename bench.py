@@ -135,6 +135,8 @@ def bench_wave(torch, B, wl, args):
     u_prev = torch.zeros_like(vel2)
     u = torch.zeros_like(vel2)
     d = B.desc_init("f32", shp, w.radius)
+    # eta is read everywhere: the data-region split (pml_width) reads less
+    # but measured slower on MI355X
     src = wl.source_point(w)
     trace = wl.source_trace(w)
     fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
@@ -143,6 +145,8 @@ def bench_wave(torch, B, wl, args):
     wall, durs = timed_launches(torch, fn, runs, 1)
     pts = w.interior_points * w.sweeps
     per_step = float(durs.mean()) / w.sweeps
+    # one read and one write per field: u (with its face slabs), u_prev,
+    # vel2, eta read, u_next written
     nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
     achieved = nbytes / per_step / 1e9
     del vel2, eta, u_prev, u
@@ -154,8 +158,8 @@ def bench_wave(torch, B, wl, args):
                               peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(achieved / PEAK_HBM_GBS, 4),
                               algorithmic_bytes_per_step=nbytes,
-                              note="per-step mean incl. the 1-thread "
-                                   "source kernel"))
+                              note="per-step mean incl. the 1-thread source "
+                                   "kernel"))
 
 
 def cpu_baseline(wl, host, budget_s):

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ST_ABI_VERSION 1
+#define ST_ABI_VERSION 2
 #define ST_MAX_R 4
 
 /* element types */
@@ -63,7 +63,16 @@ extern "C" {
  * axis' share of the centre weight (the 3D centre weight is
  * cx[0]+cy[0]+cz[0]), index k = 1..R the weight of the two points at
  * offsets +k and -k on that axis.  Entries above R are ignored.
- * 160 bytes, naturally aligned.
+ *
+ * pml_width describes the data regions of the wave step ("Accelerating
+ * High-Order Stencils on GPUs": one kernel for the inner region, another
+ * for the PML region, where only the latter reads eta).  If pml_width > 0
+ * the caller guarantees that eta is exactly 0 at every interior point whose
+ * distance (in points, along any axis) from the nearest interior face is
+ * at least pml_width; the wave entry points then read eta only on the PML
+ * region.  The results are bit-identical to pml_width = 0 under that
+ * guarantee.  0 (the default) reads eta everywhere.  Ignored by the plain
+ * stencil.  168 bytes, naturally aligned.
  */
 typedef struct stencil3d_desc {
     uint32_t struct_size; /* = sizeof(stencil3d_desc)                    */
@@ -74,6 +83,7 @@ typedef struct stencil3d_desc {
     double cx[ST_MAX_R + 1];
     double cy[ST_MAX_R + 1];
     double cz[ST_MAX_R + 1];
+    int64_t pml_width;    /* eta is zero this far inside; 0 = no claim    */
 } stencil3d_desc;
 
 /* ST_ABI_VERSION of the built library. */
@@ -97,7 +107,8 @@ int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx,
 /*
  * Check a descriptor without touching the GPU: struct size, dtype, radius,
  * boundary mode, extents (each >= 2R+1; nx*ny*elem < 2^31 bytes so that
- * in-plane offsets fit 32 bits) and finite weights.
+ * in-plane offsets fit 32 bits), finite weights and pml_width >= 0
+ * (ST_ERR_ARG).
  */
 int stencil3d_desc_validate(const stencil3d_desc *d);
 
@@ -145,6 +156,7 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
  * eta dimensionless; all five arrays share d's extents and element type.
  * u_next may be the same buffer as u_prev (each point reads u_prev only at
  * itself), but must not overlap u, vel2 or eta.  dt, h finite, h > 0.
+ * With d->pml_width > 0, eta is read only where it may be non-zero.
  */
 int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u,
               void *u_next, const void *vel2, const void *eta, double dt,

@@ -47,10 +47,11 @@ def test_exports_every_declared_function(L):
 
 
 def test_struct_layout_and_version(L):
-    assert ctypes.sizeof(B.Desc) == 160
-    assert B.abi_version() == 1
+    assert ctypes.sizeof(B.Desc) == 168
+    assert B.abi_version() == 2
     d = B.desc_init("f32", (10, 11, 12), 4)
-    assert d.struct_size == 160 and d.nx == 12 and d.ny == 11 and d.nz == 10
+    assert d.struct_size == 168 and d.nx == 12 and d.ny == 11 and d.nz == 10
+    assert d.pml_width == 0
 
 
 def test_strerror_is_distinct(L):
@@ -89,7 +90,7 @@ def test_descriptor_validation(L):
     ok = _desc()
     assert B.desc_validate(ok) == 0
     assert L.stencil3d_desc_validate(None) == c["ST_ERR_NULL"]
-    assert B.desc_validate(_desc(struct_size=152)) == c["ST_ERR_STRUCT_SIZE"]
+    assert B.desc_validate(_desc(struct_size=160)) == c["ST_ERR_STRUCT_SIZE"]
     assert B.desc_validate(_desc(dtype=2)) == c["ST_ERR_DTYPE"]
     assert B.desc_validate(_desc(radius=0)) == c["ST_ERR_RADIUS"]
     assert B.desc_validate(_desc(radius=5)) == c["ST_ERR_RADIUS"]
@@ -105,6 +106,8 @@ def test_descriptor_validation(L):
     ign = _desc(radius=2)
     ign.cz[4] = math.inf  # above R: ignored
     assert B.desc_validate(ign) == 0
+    assert B.desc_validate(_desc(pml_width=-1)) == c["ST_ERR_ARG"]
+    assert B.desc_validate(_desc(pml_width=1 << 40)) == 0
     d = B.Desc()
     assert L.stencil3d_desc_init(ctypes.byref(d), 0, 8, 8, 8, 4, 0) == \
         c["ST_ERR_DIMS"]

@@ -171,6 +171,14 @@ def test_wave_1024_point_source_20_steps(oracle_mod, torch_dev):
                           w.sweeps, (sx, sy, sz), trace)
     assert np.array_equal(new[zs, ys, xs].cpu().numpy(), chained)
     assert int(torch.count_nonzero(new)) == int(np.count_nonzero(chained))
+    # the data-region split (eta read only on the 32-point sponge) too
+    dp = B.desc_init("f32", w.shape, R)
+    dp.pml_width = e["sponge"]
+    u_prev2.zero_(), u2.zero_()
+    old, new = B.wave_run(dp, u_prev2, u2, vel2, eta, e["dt"], e["h"],
+                          w.sweeps, (sx, sy, sz), trace)
+    assert np.array_equal(new[zs, ys, xs].cpu().numpy(), chained)
+    assert int(torch.count_nonzero(new)) == int(np.count_nonzero(chained))
     # free-running against the fp64 oracle on the crop (reported)
     _, ref_free = oracle_mod.wave_run(
         np.zeros(crop_v2.shape), np.zeros(crop_v2.shape), crop_v2, crop_eta,
@@ -442,3 +450,34 @@ def test_largest_plane(oracle_mod, torch_dev):
             if x0 == nx - h:
                 assert np.all(got[:, :, -1] == np.float32(SENTINEL))
     assert np.all(out[0].cpu().numpy() == np.float32(SENTINEL))
+
+
+def test_wave_pml_regions(oracle_mod, torch_dev):
+    """With eta = 0 beyond the 32-point sponge, pml_width = 32 (exact) or 40
+    (conservative) or one larger than half the interior gives bit-identical
+    steps to pml_width = 0 while eta is read only on the sponge; a false
+    claim (16) changes the result, so the skip is really taken."""
+    torch, _ = torch_dev
+    w = wl.WAVE_128_RANDOM
+    e = w.extra
+    R = w.radius
+    u_prev, u, vel2, eta = _wave_fields(w, torch)
+    runs = {}
+    for pml in (0, 32, 40, 70, 16):
+        d = B.desc_init("f32", w.shape, R)
+        d.pml_width = pml
+        a, b = u_prev.clone(), u.clone()
+        for n in range(3):
+            B.wave_step(d, a, b, a, vel2, eta, e["dt"], e["h"])
+            a, b = b, a
+        runs[pml] = b.cpu().numpy()
+    for pml in (32, 40, 70):
+        assert np.array_equal(runs[pml], runs[0]), pml
+    assert not np.array_equal(runs[16], runs[0])
+    # and the pml_width = 0 result is the oracle's (teacher-forced above;
+    # here three free steps, fp32 vs fp64)
+    c = oracle_mod.laplacian_weights(R)
+    _, ref = oracle_mod.wave_run(u_prev.cpu().numpy(), u.cpu().numpy(),
+                                 vel2.cpu().numpy(), eta.cpu().numpy(), R, c,
+                                 e["dt"], e["h"], 3)
+    check_close(interior(runs[0], R), interior(ref, R), 1e-4, "3 free steps")
