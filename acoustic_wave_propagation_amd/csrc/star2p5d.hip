@@ -4,32 +4,42 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "star2p5d_kernel.h"
 
 namespace st {
 namespace {
 
-// Shipped configurations per element type, chosen by timing and traffic
-// counters on MI355X (sweep over outputs per thread, threads per workgroup,
-// prefetch depth, halo timing, LDS buffering, chunking, store policy):
-//   fp32 apply: 4 x 2 outputs per thread, 64 x 8 threads  -> 256 x 16 tile,
-//               nontemporal stores
-//   fp32 wave:  4 x 2 outputs per thread, 32 x 16 threads -> 128 x 32 tile
-//   fp64:       2 x 2 outputs per thread, 32 x 16 threads ->  64 x 32 tile
-// one plane of stencil-input prefetch, halo ring loaded with the window's
-// leading plane, two LDS tile buffers (one barrier per z step).
-template <typename T>
-struct Shipped;
-template <>
-struct Shipped<float> {
-    using Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
-    using Wave = TileCfg<4, 2, 32, 16, 1, 0>;
-};
-template <>
-struct Shipped<double> {
-    using Apply = TileCfg<2, 2, 32, 16, 1, 0>;
-    using Wave = TileCfg<2, 2, 32, 16, 1, 0>;
+// Shipped configurations per element type and radius, chosen by timing
+// and traffic counters on MI355X (sweeps over outputs per thread, threads
+// per workgroup, prefetch depth, halo timing, LDS buffering, chunking and
+// store policy).  All use 512-thread workgroups, one plane of stencil-input
+// prefetch, the halo ring loaded with the window's leading plane and two LDS
+// tile buffers (one barrier per z step):
+//   fp32 apply, R >= 2: 4 x 2 outputs per thread, 64 x 8 threads -> 256 x 16
+//                        tile, nontemporal stores
+//   fp32 apply, R = 1:   4 x 4 outputs per thread (the short window leaves
+//                        registers for more rows) -> 256 x 32 tile
+//   fp32 wave:           4 x 2 per thread, 32 x 16 threads -> 128 x 32 tile
+//   fp64 apply:          2 x 2 per thread, 64 x 8 threads -> 128 x 16 tile,
+//                        nontemporal stores
+//   fp64 wave:           2 x 2 per thread, 32 x 16 threads ->  64 x 32 tile
+using F32Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
+using F32ApplyR1 = TileCfg<4, 4, 64, 8, 1, 0, true, 2, false, true, true, true>;
+using F32Wave = TileCfg<4, 2, 32, 16, 1, 0>;
+using F64Apply = TileCfg<2, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
+using F64Wave = TileCfg<2, 2, 32, 16, 1, 0>;
+
+template <typename T, int R, bool WAVE>
+struct Shipped {
+    using Cfg = typename std::conditional<
+        std::is_same<T, double>::value,
+        typename std::conditional<WAVE, F64Wave, F64Apply>::type,
+        typename std::conditional<WAVE, F32Wave,
+                                  typename std::conditional<R == 1, F32ApplyR1,
+                                                            F32Apply>::type>::type>::type;
 };
 
 template <typename T, int R>
@@ -40,11 +50,11 @@ int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, voi
                                           g.tiles_y, g.chunk_len, g.nwg);
     const dim3 grid(g.nwg), block(g.threads);
     if (wave)
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, true, typename Shipped<T>::Wave>), grid,
-                           block, 0, stream, a);
+        hipLaunchKernelGGL((star2p5d_kernel<T, R, true, typename Shipped<T, R, true>::Cfg>),
+                           grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, typename Shipped<T>::Apply>), grid,
-                           block, 0, stream, a);
+        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, typename Shipped<T, R, false>::Cfg>),
+                           grid, block, 0, stream, a);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }
 
@@ -61,67 +71,68 @@ int launch_r(const stencil3d_desc &d, const Geometry &g, const void *in, void *o
     return ST_ERR_RADIUS;
 }
 
-template <class C>
-void tile_of(Geometry &g) {
-    g.tile_x = C::TX;
-    g.tile_y = C::TY;
-    g.threads = C::NT;
+// Tile shape, threads and z unroll of the shipped kernel for (T, R, WAVE).
+struct Shape {
+    int tile_x, tile_y, threads, unroll, prologue;
+};
+
+template <typename T, int R, bool WAVE>
+Shape shape_of() {
+    using C = typename Shipped<T, R, WAVE>::Cfg;
+    using RG = Rings<R, WAVE, C>;
+    return Shape{C::TX, C::TY, C::NT, RG::U, 2 * R + RG::D};
 }
 
-template <bool WAVE, class C>
-int unroll_of(int R) {
+template <typename T, bool WAVE>
+Shape shape_r(int R) {
     switch (R) {
-    case 1: return Rings<1, WAVE, C>::U;
-    case 2: return Rings<2, WAVE, C>::U;
-    case 3: return Rings<3, WAVE, C>::U;
-    default: return Rings<4, WAVE, C>::U;
+    case 1: return shape_of<T, 1, WAVE>();
+    case 2: return shape_of<T, 2, WAVE>();
+    case 3: return shape_of<T, 3, WAVE>();
+    default: return shape_of<T, 4, WAVE>();
     }
 }
 
 }  // namespace
 
 Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus) {
+    const Shape sh = d.dtype == ST_F64
+                         ? (wave ? shape_r<double, true>(d.radius) : shape_r<double, false>(d.radius))
+                         : (wave ? shape_r<float, true>(d.radius) : shape_r<float, false>(d.radius));
     Geometry g;
-    int unroll;
-    if (d.dtype == ST_F64) {
-        if (wave) {
-            tile_of<Shipped<double>::Wave>(g);
-            unroll = unroll_of<true, Shipped<double>::Wave>(d.radius);
-        } else {
-            tile_of<Shipped<double>::Apply>(g);
-            unroll = unroll_of<false, Shipped<double>::Apply>(d.radius);
-        }
-    } else {
-        if (wave) {
-            tile_of<Shipped<float>::Wave>(g);
-            unroll = unroll_of<true, Shipped<float>::Wave>(d.radius);
-        } else {
-            tile_of<Shipped<float>::Apply>(g);
-            unroll = unroll_of<false, Shipped<float>::Apply>(d.radius);
-        }
-    }
+    g.tile_x = sh.tile_x;
+    g.tile_y = sh.tile_y;
+    g.threads = sh.threads;
     const int R = d.radius;
     const int64_t ix = d.nx - 2 * R, iy = d.ny - 2 * R, iz = d.nz - 2 * R;
     g.tiles_x = (int)((ix + g.tile_x - 1) / g.tile_x);
     g.tiles_y = (int)((iy + g.tile_y - 1) / g.tile_y);
     const int64_t tiles = (int64_t)g.tiles_x * g.tiles_y;
-    // About 512 threads per compute unit (one 512-thread workgroup: the
-    // register window allows two waves per SIMD); split z into chunks only
-    // as far as needed for that, and never below 4R planes per chunk (each
-    // chunk re-reads 2R planes of z halo).  Chunk lengths are whole blocks
-    // of the kernel's z unroll (the kernel runs whole blocks).
-    const int64_t per_cu = g.threads >= 512 ? 1 : 512 / g.threads;
-    const int64_t target = per_cu * (int64_t)(cus > 0 ? cus : 256);
-    int64_t nch = (target + tiles - 1) / tiles;
+    // Split z into chunks.  About 512 threads run per compute unit (the
+    // register window allows two waves per SIMD), so `cap` workgroups run at
+    // once and the launch takes ceil(workgroups / cap) rounds; each round
+    // lasts a chunk's planes plus its pipeline fill.  Pick the chunk count
+    // that minimises rounds * (chunk + fill); never below 4R planes per
+    // chunk; chunk lengths are whole blocks of the kernel's z unroll (the
+    // kernel runs whole blocks).
+    const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * (g.threads >= 512 ? 1 : 512 / g.threads);
     const int64_t maxch = iz / (4 * R) > 0 ? iz / (4 * R) : 1;
-    if (nch > maxch) nch = maxch;
-    if (nch < 1) nch = 1;
-    int64_t len = (iz + nch - 1) / nch;
-    len = (len + unroll - 1) / unroll * unroll;
-    nch = (iz + len - 1) / len;  // every chunk non-empty
-    g.chunk_len = (int)len;
-    g.nchunks = (int)nch;
-    g.nwg = (int)(tiles * nch);
+    int64_t best_len = 0, best_nch = 1, best_cost = -1;
+    for (int64_t nch = 1; nch <= maxch; ++nch) {
+        int64_t len = (iz + nch - 1) / nch;
+        len = (len + sh.unroll - 1) / sh.unroll * sh.unroll;
+        const int64_t n = (iz + len - 1) / len;
+        const int64_t rounds = (tiles * n + cap - 1) / cap;
+        const int64_t cost = rounds * (len + sh.prologue + 4);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_len = len;
+            best_nch = n;
+        }
+    }
+    g.chunk_len = (int)best_len;
+    g.nchunks = (int)best_nch;
+    g.nwg = (int)(tiles * best_nch);
     return g;
 }
 
