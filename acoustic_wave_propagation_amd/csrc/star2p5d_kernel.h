@@ -77,11 +77,12 @@ struct StarArgs {
 // per SIMD the register allocation must allow.
 template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
           bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
-          bool NTL_ = false, int MINW_ = 1, bool ETILE_ = false>
+          bool NTL_ = false, int MINW_ = 1, bool ETILE_ = false, bool NTI_ = false>
 struct TileCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
     static constexpr int MINW = MINW_;  // register budget for >= MINW waves per SIMD
     static constexpr bool ETILE = ETILE_;  // data-region skip per tile (else per lane)
+    static constexpr bool NTI = NTI_;      // nontemporal stencil-input loads
     static constexpr bool HLA = HLA_, ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_,
                           NTL = NTL_;
     static constexpr int NT = LX * LY, TX = LX * VX, TY = LY * VY;
@@ -238,6 +239,7 @@ star2p5d_kernel(StarArgs<T> a) {
     constexpr int KH = (NYU + NXU + NT - 1) / NT;  // halo units per thread
     constexpr uint32_t ES = sizeof(T);
     constexpr int LAUX = C::NTL ? kAuxNT : 0, SAUX = C::NTS ? kAuxNT : 0;
+    constexpr int IAUX = C::NTI ? kAuxNT : 0;
     // fp64: accumulate neighbour differences (u(p+-k) - u(p)), which keeps
     // the rounding of smooth fields far below the fp64 tolerance.
     constexpr bool DIFF = std::is_same<T, double>::value;
@@ -350,13 +352,13 @@ star2p5d_kernel(StarArgs<T> a) {
         constexpr int s = decltype(slot_c)::value;
         const rsrc_t r = rsrc_at(a.in, k, j, needed);
 #pragma unroll
-        for (int jj = 0; jj < VY; ++jj) bload<T, VX>(r, ooff[jj], win[s][jj]);
+        for (int jj = 0; jj < VY; ++jj) bload<T, VX, IAUX>(r, ooff[jj], win[s][jj]);
     };
     auto load_halo = [&](int k, bool needed, auto slot_c) {
         constexpr int h = decltype(slot_c)::value;
         const rsrc_t r = rsrc_at(a.in, k, 0, needed);
 #pragma unroll
-        for (int q = 0; q < KH; ++q) bload<T, VX>(r, h_off[q], hs[h][q]);
+        for (int q = 0; q < KH; ++q) bload<T, VX, IAUX>(r, h_off[q], hs[h][q]);
     };
     auto load_epilogue = [&](int k, bool needed, auto slot_c) {
         constexpr int e = decltype(slot_c)::value;
