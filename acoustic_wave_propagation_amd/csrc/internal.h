@@ -14,6 +14,7 @@ namespace st {
 struct Geometry {
     int tile_x, tile_y, threads;
     int tiles_x, tiles_y, nchunks, chunk_len, nwg;
+    int variant;  // 0: the primary tile shape, 1: the row-wide one
 };
 
 // Geometry the kernel for (dtype, R, op) would use on a device with `cus`

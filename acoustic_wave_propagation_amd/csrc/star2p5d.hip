@@ -21,13 +21,17 @@ namespace {
 //   fp32 apply, R >= 2: 4 x 2 outputs per thread, 64 x 8 threads -> 256 x 16
 //                        tile, nontemporal stores
 //   fp32 apply, R = 1:   4 x 4 outputs per thread (the short window leaves
-//                        registers for more rows) -> 256 x 32 tile
+//                        registers for more rows) -> 256 x 32 tile, or
+//                        512 x 16 when one such tile spans and nearly
+//                        fills an interior row (449..512 points; on 2 KB row
+//                        pitches whole-row tiles run ~13% faster)
 //   fp32 wave:           4 x 2 per thread, 32 x 16 threads -> 128 x 32 tile
 //   fp64 apply:          2 x 2 per thread, 64 x 8 threads -> 128 x 16 tile,
 //                        nontemporal stores
 //   fp64 wave:           2 x 2 per thread, 32 x 16 threads ->  64 x 32 tile
 using F32Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
 using F32ApplyR1 = TileCfg<4, 4, 64, 8, 1, 0, true, 2, false, true, true, true>;
+using F32ApplyR1Wide = TileCfg<4, 4, 128, 4, 1, 0, true, 2, false, true, true, true>;
 using F32Wave = TileCfg<4, 2, 32, 16, 1, 0>;
 using F64Apply = TileCfg<2, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
 using F64Wave = TileCfg<2, 2, 32, 16, 1, 0>;
@@ -40,7 +44,15 @@ struct Shipped {
         typename std::conditional<WAVE, F32Wave,
                                   typename std::conditional<R == 1, F32ApplyR1,
                                                             F32Apply>::type>::type>::type;
+    // row-wide alternative (void: none)
+    using Wide = typename std::conditional<!WAVE && R == 1 && std::is_same<T, float>::value,
+                                           F32ApplyR1Wide, void>::type;
 };
+
+template <typename T, int R, bool WAVE, int V>
+using CfgOf = typename std::conditional<V == 1 && !std::is_void<typename Shipped<T, R, WAVE>::Wide>::value,
+                                        typename Shipped<T, R, WAVE>::Wide,
+                                        typename Shipped<T, R, WAVE>::Cfg>::type;
 
 template <typename T, int R>
 int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, void *out,
@@ -50,11 +62,14 @@ int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, voi
                                           g.tiles_y, g.chunk_len, g.nwg);
     const dim3 grid(g.nwg), block(g.threads);
     if (wave)
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, true, typename Shipped<T, R, true>::Cfg>),
-                           grid, block, 0, stream, a);
+        hipLaunchKernelGGL((star2p5d_kernel<T, R, true, CfgOf<T, R, true, 0>>), grid, block, 0,
+                           stream, a);
+    else if (g.variant == 1)
+        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, CfgOf<T, R, false, 1>>), grid, block,
+                           0, stream, a);
     else
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, typename Shipped<T, R, false>::Cfg>),
-                           grid, block, 0, stream, a);
+        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, CfgOf<T, R, false, 0>>), grid, block,
+                           0, stream, a);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }
 
@@ -76,30 +91,46 @@ struct Shape {
     int tile_x, tile_y, threads, unroll, prologue;
 };
 
-template <typename T, int R, bool WAVE>
+template <typename T, int R, bool WAVE, int V>
 Shape shape_of() {
-    using C = typename Shipped<T, R, WAVE>::Cfg;
+    using C = CfgOf<T, R, WAVE, V>;
     using RG = Rings<R, WAVE, C>;
     return Shape{C::TX, C::TY, C::NT, RG::U, 2 * R + RG::D};
 }
 
-template <typename T, bool WAVE>
+template <typename T, bool WAVE, int V>
 Shape shape_r(int R) {
     switch (R) {
-    case 1: return shape_of<T, 1, WAVE>();
-    case 2: return shape_of<T, 2, WAVE>();
-    case 3: return shape_of<T, 3, WAVE>();
-    default: return shape_of<T, 4, WAVE>();
+    case 1: return shape_of<T, 1, WAVE, V>();
+    case 2: return shape_of<T, 2, WAVE, V>();
+    case 3: return shape_of<T, 3, WAVE, V>();
+    default: return shape_of<T, 4, WAVE, V>();
     }
+}
+
+Shape shape_for(const stencil3d_desc &d, bool wave, int variant) {
+    if (d.dtype == ST_F64)
+        return wave ? shape_r<double, true, 0>(d.radius)
+                    : (variant ? shape_r<double, false, 1>(d.radius)
+                               : shape_r<double, false, 0>(d.radius));
+    return wave ? shape_r<float, true, 0>(d.radius)
+                : (variant ? shape_r<float, false, 1>(d.radius) : shape_r<float, false, 0>(d.radius));
 }
 
 }  // namespace
 
 Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus) {
-    const Shape sh = d.dtype == ST_F64
-                         ? (wave ? shape_r<double, true>(d.radius) : shape_r<double, false>(d.radius))
-                         : (wave ? shape_r<float, true>(d.radius) : shape_r<float, false>(d.radius));
+    // The row-wide variant (if this kernel has one) is taken when one of its
+    // tiles spans an interior row that needs two of the primary tiles and
+    // fills at least 7/8 of it (measured: 510 and 512 wide rows gain 5-13%,
+    // a 300 wide row loses a third).
+    const int64_t ixr = d.nx - 2 * (int64_t)d.radius;
+    const Shape prim = shape_for(d, wave, 0), wide = shape_for(d, wave, 1);
+    const int variant = (wide.tile_x > prim.tile_x && ixr > prim.tile_x &&
+                         8 * ixr > 7 * (int64_t)wide.tile_x && ixr <= wide.tile_x);
+    const Shape sh = variant ? wide : prim;
     Geometry g;
+    g.variant = variant;
     g.tile_x = sh.tile_x;
     g.tile_y = sh.tile_y;
     g.threads = sh.threads;

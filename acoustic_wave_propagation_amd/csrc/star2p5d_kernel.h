@@ -12,16 +12,17 @@
 //   1. issue the loads of plane z+R+D (own columns, into the window slot
 //      that plane z-R-1 has just freed) and of the same plane's R-wide halo
 //      ring, and (wave step) of plane z+DE's u_prev, vel2 and eta;
-//   2. barrier; write plane z's own values (from the window, not re-read
-//      from HBM) and its halo ring into the one LDS tile; barrier;
+//   2. write plane z's own values (from the window, not re-read from HBM)
+//      and its halo ring into one of two LDS tile buffers; barrier (the
+//      other buffer lets the next step write while this one is read);
 //   3. read the in-plane neighbours from LDS and the z neighbours from the
-//      window, evaluate, and store with a streaming store.
+//      window, evaluate, and store.
 // Each interior plane is read from HBM once per chunk; a tile's halo ring
 // is loaded in the same step in which the neighbouring tiles (same XCD)
 // load those rows as their own window, so the ring is served from L2.
-// D planes of loads stay in flight per thread, which is what covers the
-// HBM latency at the two or three waves per SIMD this register budget
-// allows.
+// The loads of the next D planes (halo: R+D) stay in flight per thread,
+// which covers the HBM latency at the two waves per SIMD this register
+// budget allows.
 //
 // The window, halo and epilogue rings are indexed with compile-time slot
 // numbers: the z loop is unrolled by the least common multiple of the ring
@@ -70,11 +71,13 @@ struct StarArgs {
 // workgroup, D planes of stencil-input prefetch, DE planes of wave-epilogue
 // prefetch (0: loaded in the step that uses them), halo ring loaded in the
 // same step as the window's leading load of that plane (HLA) or D steps
-// ahead of its use, LB LDS tile buffers
-// (2: one barrier per z step), alternating z direction of neighbouring
-// chunks, chunk-major (vs tile-major) order of the logical workgroup id,
-// XCD remap, nontemporal stores, nontemporal epilogue loads, minimum waves
-// per SIMD the register allocation must allow.
+// ahead of its use, LB LDS tile buffers (2: one barrier per z step),
+// alternating z direction of neighbouring chunks, chunk-major (vs
+// tile-major) order of the logical workgroup id, XCD remap, nontemporal
+// stores, nontemporal epilogue loads, minimum waves per SIMD the register
+// allocation must allow, data-region skip per tile (vs per lane),
+// nontemporal stencil-input loads.  The shipped choices are in
+// star2p5d.hip; the others are kept for measurement.
 template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
           bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
           bool NTL_ = false, int MINW_ = 1, bool ETILE_ = false, bool NTI_ = false>

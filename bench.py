@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the 25-point (R = 4) star stencil on a 512^3 fp32 interior
 (520^3 allocated with a 4-point halo) on one MI355X, plus the acoustic wave
-step on a 1024^3 interior as a secondary figure.
+step on a 1024^3 interior, the R = 1 Jacobi sweeps on 512^3 and the fp64
+ragged grid as secondary figures.
 
-    python bench.py [--steps K] [--warmup W] [--no-wave] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-wave] [--no-others]
+                    [--no-cpu]
 
 Prints ONE JSON line.  A step is one stencil3d_apply over the whole grid
 (input already resident in HBM).  `value` = interior points * K / wall time
@@ -162,6 +164,56 @@ def bench_wave(torch, B, wl, args):
                                    "kernel"))
 
 
+def bench_others(torch, B, wl, args):
+    """The remaining workloads, each timed the same way as the headline:
+    10-sweep Jacobi with the R = 1 7-point stencil on 512^3, and one R = 4
+    fp64 application on the ragged 1001 x 603 x 297 grid."""
+    dev = torch.device("cuda:0")
+    res = {}
+    runs = max(1, min(args.steps, 10))
+
+    w = wl.R1_JACOBI_512
+    log("generating %s %s" % (w.name, w.shape))
+    a = torch.from_numpy(wl.input_planes(w)).to(dev)
+    b = torch.empty_like(a)
+    d = B.desc_init("f32", w.shape, w.radius, B.DIRICHLET_COPY)
+    wall, durs = timed_launches(
+        torch, lambda: B.stencil3d_jacobi(d, a, b, w.sweeps), runs, 1)
+    per = float(durs.mean()) / w.sweeps
+    nbytes = star_bytes(w.interior, w.radius, 4)
+    res[w.name] = dict(
+        value=round(w.interior_points * w.sweeps * runs / wall / 1e9, 2),
+        unit="GPoints/s", ms_per_sweep=round(per * 1e3, 5),
+        sweeps_per_run=w.sweeps, runs=runs,
+        roofline=dict(bound="hbm", achieved=round(nbytes / per / 1e9, 1),
+                      peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
+                      algorithmic_bytes_per_sweep=nbytes,
+                      note="per-sweep mean incl. the one boundary copy"))
+    del a, b
+
+    w = wl.R4_RAGGED_F64
+    log("generating %s %s" % (w.name, w.shape))
+    inp = torch.from_numpy(wl.input_planes(w)).to(dev)
+    out = torch.zeros_like(inp)
+    d = B.desc_init("f64", w.shape, w.radius)
+    wall, durs = timed_launches(
+        torch, lambda: B.stencil3d_apply(d, inp, out), args.steps,
+        args.warmup)
+    per = float(durs.mean())
+    nbytes = star_bytes(w.interior, w.radius, 8)
+    res[w.name] = dict(
+        value=round(w.interior_points * args.steps / wall / 1e9, 2),
+        unit="GPoints/s", kernel_ms=round(per * 1e3, 5),
+        roofline=dict(bound="hbm", achieved=round(nbytes / per / 1e9, 1),
+                      peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
+                      algorithmic_bytes=nbytes))
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, host, budget_s):
     """The oracle as it stands, on the host cores: whole 520^3 applications
     repeated until the time budget is spent (at least one)."""
@@ -203,6 +255,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-wave", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
@@ -234,6 +287,11 @@ def main():
         log("wave: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % (wave["value"], wave["ms_per_step"],
                wave["roofline"]["achieved"]))
+    others = None if args.no_others else bench_others(torch, B, wl, args)
+    if others:
+        for k, v in others.items():
+            log("%s: %.1f GPoints/s, %.1f GB/s"
+                % (k, v["value"], v["roofline"]["achieved"]))
     cpu = None if args.no_cpu else cpu_baseline(wl, host, args.cpu_budget)
 
     w = wl.R4_512
@@ -259,6 +317,7 @@ def main():
         "kernel_ms": head["kernel_ms"],
         "hbm_gbs_wall": head["gbs_wall"],
         "wave_step": wave,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
 

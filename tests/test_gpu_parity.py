@@ -247,6 +247,18 @@ def test_ragged_multi_tile(oracle_mod, torch_dev, R, dtype):
                 (R, np.dtype(dtype).name))
 
 
+@pytest.mark.parametrize("ix", [383, 449, 510, 512, 513])
+def test_row_wide_tile(oracle_mod, torch_dev, ix):
+    """fp32 R = 1 interior rows of 449..512 points run one row-wide tile per
+    row band (ragged below 512); 383 and 513 take the narrower tiles (513
+    with a one-point tail)."""
+    torch, _ = torch_dev
+    shape = (23, 45, ix + 2)
+    log("case row-wide R=1 f32 %s" % (shape,))
+    u = wl.uniform_planes(shape, 900 + ix, -1, 1, dtype=np.float32)
+    _apply_case(oracle_mod, torch, u, 1, what="row-wide ix=%d" % ix)
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 @pytest.mark.parametrize("R", [1, 2, 3, 4])
 def test_smallest_grid(oracle_mod, torch_dev, R, dtype):
