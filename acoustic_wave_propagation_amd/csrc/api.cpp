@@ -13,6 +13,7 @@
 #include <atomic>
 
 #include "internal.h"
+#include "pass_plan.h"
 #include "stencil3d.h"
 
 namespace {
@@ -177,12 +178,24 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, int sweeps
     stencil3d_desc di = *d;
     di.boundary = ST_BC_HALO_UNTOUCHED;
     if ((st = st::launch_shell_copy(di, buf0, buf1, s))) return st;
+    // Passes of several fused sweeps (temporal blocking) where a fused
+    // kernel exists; each pass reads one buffer and writes the other's
+    // interior.  Bit-identical to one sweep per pass.
+    const int maxns = st::fused_max_sweeps(di);
+    const st::PassPlan plan = st::plan_passes(sweeps, maxns, st::fused_pass_costs(di));
     void *b[2] = {buf0, buf1};
-    for (int i = 0; i < sweeps; ++i) {
-        st = st::launch_star(di, b[i & 1], b[(i + 1) & 1], nullptr, nullptr, nullptr, false,
-                             1.0, cus, s);
-        if (st) return st;
-    }
+    int cur = 0;
+    auto pass = [&](int ns) {
+        const int r = ns == 1 ? st::launch_star(di, b[cur], b[cur ^ 1], nullptr, nullptr, nullptr,
+                                                false, 1.0, cus, s)
+                              : st::launch_sweeps_fused(di, b[cur], b[cur ^ 1], ns, cus, s);
+        cur ^= 1;
+        return r;
+    };
+    for (int64_t k = 0; k < plan.bulk; ++k)
+        if ((st = pass(plan.bulk_ns))) return st;
+    for (int k = 0; k < plan.ntail; ++k)
+        if ((st = pass(plan.tail[k]))) return st;
     return ST_OK;
 }
 

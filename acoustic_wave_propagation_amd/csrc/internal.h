@@ -29,6 +29,22 @@ int launch_star(const stencil3d_desc &d, const void *in, void *out,
                 const void *u_prev, const void *vel2, const void *eta,
                 bool wave, double wscale, int cus, hipStream_t stream);
 
+// Largest number of sweeps one fused pass can do for d (1: no fused kernel
+// for this radius and element type).
+int fused_max_sweeps(const stencil3d_desc &d);
+
+// Relative time of a pass of ns sweeps, ns = 1..fused_max_sweeps(d) (one
+// single sweep = 1).
+const double *fused_pass_costs(const stencil3d_desc &d);
+
+// One pass of ns fused Jacobi sweeps (2 <= ns <= fused_max_sweeps(d)): out's
+// interior = ns applications of the stencil to in, with in's non-interior
+// points held fixed.  out's non-interior points are not written.  in and
+// out must not overlap.  Returns ST_OK, ST_ERR_ARG (unsupported ns or
+// radius) or ST_ERR_LAUNCH.
+int launch_sweeps_fused(const stencil3d_desc &d, const void *in, void *out, int ns, int cus,
+                        hipStream_t stream);
+
 // out = in on every non-interior point.
 int launch_shell_copy(const stencil3d_desc &d, const void *in, void *out,
                       hipStream_t stream);

@@ -1,0 +1,127 @@
+// sweeps_fused.hip -- instantiates and launches the fused-sweep (temporally
+// blocked) Jacobi kernel of sweeps_fused_kernel.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "internal.h"
+#include "sweeps_fused_kernel.h"
+
+namespace st {
+namespace {
+
+// R = 1 only: the extended tile grows by NS*R points per side, so larger
+// radii would spend most of the work on the overlap.  Output tiles are
+// 128 x 16 (fp32) and 64 x 16 (fp64) for every NS; the extended tile adds
+// whole 16-byte groups in x and NS rows in y on each side.  4 x 2 (fp32) or
+// 2 x 2 (fp64) points per thread keep the input window and the NS-1
+// intermediate rings within two waves per SIMD.  Up to 4 sweeps two sets of
+// LDS tiles fit (one barrier per z step); 5 and 6 sweeps use one set.
+// Measured on 512^3 fp32, ms per pass for NS = 2..6: 0.330, 0.399, 0.467,
+// 0.622, 0.702 (one single sweep: 0.231).
+template <typename T, int NS>
+struct FusedShipped;
+template <int NS>
+struct FusedShipped<float, NS> {
+    static constexpr int XE = (NS + 3) / 4 * 4;
+    using Cfg = FusedCfg<4, 2, (128 + 2 * XE) / 4, (16 + 2 * NS) / 2, 1, NS <= 4 ? 2 : 1>;
+};
+template <int NS>
+struct FusedShipped<double, NS> {
+    static constexpr int XE = (NS + 1) / 2 * 2;
+    using Cfg = FusedCfg<2, 2, (64 + 2 * XE) / 2, (16 + 2 * NS) / 2>;
+};
+
+struct FusedPlan {
+    int tiles_x, tiles_y, chunk_len, nwg, threads;
+};
+
+template <typename T, int NS>
+FusedPlan plan_fused(const stencil3d_desc &d, int cus) {
+    using C = typename FusedShipped<T, NS>::Cfg;
+    using FS = FusedShape<1, NS, C>;
+    FusedPlan p;
+    const int64_t ix = d.nx - 2, iy = d.ny - 2, iz = d.nz - 2;
+    p.tiles_x = (int)((ix + FS::TX - 1) / FS::TX);
+    p.tiles_y = (int)((iy + FS::TY - 1) / FS::TY);
+    p.threads = C::NT;
+    const int64_t tiles = (int64_t)p.tiles_x * p.tiles_y;
+    // one workgroup per compute unit (LDS and registers); minimise
+    // rounds * (chunk + pipeline fill), as for the single-sweep kernel
+    const int64_t cap = cus > 0 ? cus : 256;
+    const int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
+    int64_t best_len = iz, best_n = 1, best_cost = -1;
+    for (int64_t nch = 1; nch <= maxch; ++nch) {
+        int64_t len = (iz + nch - 1) / nch;
+        len = (len + FS::U - 1) / FS::U * FS::U;
+        const int64_t n = (iz + len - 1) / len;
+        const int64_t rounds = (tiles * n + cap - 1) / cap;
+        const int64_t cost = rounds * (len + FS::PROLOGUE + 4);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_len = len;
+            best_n = n;
+        }
+    }
+    p.chunk_len = (int)best_len;
+    p.nwg = (int)(tiles * best_n);
+    return p;
+}
+
+template <typename T, int NS>
+int launch_ns(const stencil3d_desc &d, const void *in, void *out, int cus, hipStream_t s) {
+    using C = typename FusedShipped<T, NS>::Cfg;
+    const FusedPlan p = plan_fused<T, NS>(d, cus);
+    const StarArgs<T> a = make_args<T, 1>(d, in, out, nullptr, nullptr, nullptr, 1.0, p.tiles_x,
+                                          p.tiles_y, p.chunk_len, p.nwg);
+    hipLaunchKernelGGL((sweeps_fused_kernel<T, 1, NS, C>), dim3(p.nwg), dim3(p.threads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
+}
+
+int launch_f32(const stencil3d_desc &d, const void *in, void *out, int ns, int cus,
+               hipStream_t s) {
+    switch (ns) {
+    case 2: return launch_ns<float, 2>(d, in, out, cus, s);
+    case 3: return launch_ns<float, 3>(d, in, out, cus, s);
+    case 4: return launch_ns<float, 4>(d, in, out, cus, s);
+    case 5: return launch_ns<float, 5>(d, in, out, cus, s);
+    case 6: return launch_ns<float, 6>(d, in, out, cus, s);
+    }
+    return ST_ERR_ARG;
+}
+
+int launch_f64(const stencil3d_desc &d, const void *in, void *out, int ns, int cus,
+               hipStream_t s) {
+    switch (ns) {
+    case 2: return launch_ns<double, 2>(d, in, out, cus, s);
+    case 3: return launch_ns<double, 3>(d, in, out, cus, s);
+    case 4: return launch_ns<double, 4>(d, in, out, cus, s);
+    }
+    return ST_ERR_ARG;
+}
+
+}  // namespace
+
+int fused_max_sweeps(const stencil3d_desc &d) {
+    if (d.radius != 1) return 1;
+    return d.dtype == ST_F64 ? 4 : 6;
+}
+
+const double *fused_pass_costs(const stencil3d_desc &d) {
+    // time of a pass of ns sweeps relative to one single sweep (index ns),
+    // measured on 512^3 grids
+    static const double f32[] = {0.0, 1.0, 1.43, 1.73, 2.02, 2.69, 3.04};
+    static const double f64[] = {0.0, 1.0, 1.11, 1.40, 1.71};
+    return d.dtype == ST_F64 ? f64 : f32;
+}
+
+int launch_sweeps_fused(const stencil3d_desc &d, const void *in, void *out, int ns, int cus,
+                        hipStream_t stream) {
+    if (d.radius != 1 || ns < 2 || ns > fused_max_sweeps(d)) return ST_ERR_ARG;
+    if (d.dtype == ST_F64) return launch_f64(d, in, out, ns, cus, stream);
+    return launch_f32(d, in, out, ns, cus, stream);
+}
+
+}  // namespace st

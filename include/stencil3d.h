@@ -132,11 +132,19 @@ int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out,
                     void *stream);
 
 /*
- * Jacobi ping-pong: `sweeps` applications alternating buf0 -> buf1 ->
- * buf0 ..., with a fixed Dirichlet boundary: buf1's non-interior points are
- * first set from buf0, then every sweep writes the interior only.  The
- * result is in buf0 if sweeps is even, else in buf1.  d->boundary is
- * ignored.  sweeps >= 0 (ST_ERR_ARG); buffers must not overlap.
+ * Jacobi ping-pong: `sweeps` applications of the stencil with a fixed
+ * Dirichlet boundary (the iterated application of the starter kernel in
+ * "3D Stencil: Rotate the Depth Window Through Registers"): buf1's
+ * non-interior points are first set from buf0, then the sweeps alternate
+ * between the buffers, writing interiors only.  The result is in buf0 if
+ * sweeps is even, else in buf1 -- bit-identical to one stencil3d_apply
+ * (ST_BC_DIRICHLET_COPY) per sweep.  For R = 1 the library fuses up to 6
+ * (fp32) or 4 (fp64) sweeps into one pass over HBM (temporal blocking,
+ * "Accelerating High-Order Stencils on GPUs", which lists it among the ways
+ * past the one-read-one-write floor); the buffer that does not hold the
+ * result then holds an earlier sweep, not necessarily sweeps-1.
+ * d->boundary is ignored.  sweeps >= 0 (ST_ERR_ARG); buffers must not
+ * overlap.
  */
 int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
                      int sweeps, void *stream);

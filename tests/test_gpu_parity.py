@@ -389,6 +389,39 @@ def test_jacobi_zero_one_sweeps(oracle_mod, torch_dev):
     check_close(res.cpu().numpy(), ref, F32_TOL, "jacobi 1 sweep")
 
 
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_jacobi_fused_passes_match_single_sweeps(oracle_mod, torch_dev, dtype):
+    """stencil3d_jacobi runs several sweeps per pass over HBM (R = 1); the
+    result must equal one stencil3d_apply per sweep bit for bit, for sweep
+    counts that give every pass size and both parities, on a grid with
+    ragged tiles in x, y and z.  The first count is also checked against the
+    oracle."""
+    torch, _ = torch_dev
+    shape = (53, 45, 263)  # (nz, ny, nx): 3 tiles in x, ragged in x and y
+    dt = "f32" if dtype == np.float32 else "f64"
+    u = wl.uniform_planes(shape, 515, -1, 1, dtype=dtype)
+    d = B.desc_init(dt, shape, 1, B.DIRICHLET_COPY)
+    c = list(d.cx[:2])
+    chain = [upload(u)]
+    for s in range(13):
+        nxt = sentinel_like(shape, dtype)
+        B.stencil3d_apply(d, chain[-1], nxt)
+        chain.append(nxt)
+    for sweeps in (2, 3, 4, 5, 6, 7, 9, 10, 13):
+        log("case jacobi fused %s sweeps=%d" % (dt, sweeps))
+        b0, b1 = upload(u), sentinel_like(shape, dtype)
+        res = B.stencil3d_jacobi(d, b0, b1, sweeps)
+        assert res is (b0 if sweeps % 2 == 0 else b1)
+        got = res.cpu().numpy()
+        want = chain[sweeps].cpu().numpy()
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), \
+            "%s sweeps=%d: %d points differ" % (dt, sweeps,
+                                               int((got != want).sum()))
+        if sweeps == 2:
+            ref = oracle_mod.jacobi(u, sweeps, 1, c)
+            check_close(got, ref, 2 * _tol(dtype), "jacobi fused 2 sweeps")
+
+
 @pytest.mark.parametrize("nsteps", [0, 1, 3])
 def test_wave_run_buffer_roles(oracle_mod, torch_dev, nsteps):
     """wave_run leaves the newest field in u for even step counts and in
