@@ -4,6 +4,8 @@
     python -m acoustic_wave_propagation_amd.profiling traffic FETCH_DB WRITE_DB \
         --kernel star2p5d_kernel --name star2p5d_r4_f32 --calib-bytes 1073741824 \
         --cmd-fetch "..." --cmd-write "..."
+    python -m acoustic_wave_propagation_amd.profiling counters DB [DB ...] \
+        --kernel star2p5d_kernel --cmd "..." [--cmd "..."]
 
 `trace` prints the per-kernel call count and duration statistics of a
 `--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
@@ -11,6 +13,8 @@
 dispatch) is scaled by the bytes a plain device copy of known size moved,
 divided by what the same counter read for that copy (the copy is the
 runtime's copyBuffer kernel that the benchmark's --calib flag launches).
+`counters` tabulates the mean per dispatch of every counter of any number of
+`--pmc` runs for one kernel, with L2 hit rate and LDS ratios derived.
 The output also records a hash of the kernel sources, so a consumer can tell
 whether the figures still describe the current kernel.
 """
@@ -47,15 +51,26 @@ def _db(path):
 
 
 def kernel_stats(path):
-    """[(name, calls, total_us, avg_us, min_us, max_us)] by total time."""
+    """[(name, calls, total_us, avg_us, min_us, max_us)] by total time.
+    Instantiations that share a (truncated) name are told apart by their
+    kernel id and labelled with workgroups x threads, LDS bytes and VGPRs."""
     db = _db(path)
     rows = db.execute(
         "select name, count(*), sum(duration), avg(duration), min(duration), "
-        "max(duration) from kernels group by name order by sum(duration) desc"
+        "max(duration), max(grid_x / workgroup_x), max(workgroup_x), "
+        "max(lds_size), max(vgpr_count), count(distinct kernel_id) from "
+        "kernels group by name, kernel_id order by sum(duration) desc"
     ).fetchall()
+    names = {}
+    for r in rows:
+        names[r[0]] = names.get(r[0], 0) + 1
+    out = []
     # durations are in ns
-    return [(n, c, t / 1e3, a / 1e3, mn / 1e3, mx / 1e3)
-            for n, c, t, a, mn, mx in rows]
+    for n, c, t, a, mn, mx, wgs, thr, lds, vg, _ in rows:
+        label = n if names[n] == 1 else "%s [%d x %d, LDS %d, %d VGPRs]" % (
+            n, wgs, thr, lds, vg)
+        out.append((label, c, t / 1e3, a / 1e3, mn / 1e3, mx / 1e3))
+    return out
 
 
 def counter_means(path, counter):
@@ -117,6 +132,47 @@ def traffic_md(fetch, write, kernel, name, calib_bytes, cmd_fetch,
     return "\n".join(out)
 
 
+# derived ratios shown under the counter table, when their inputs are there
+RATIOS = [
+    ("L2 hit rate", "TCC_HIT_sum", ("TCC_HIT_sum", "TCC_MISS_sum")),
+    ("LDS bank-conflict cycles per LDS-active cycle", "SQ_LDS_BANK_CONFLICT",
+     ("SQ_LDS_IDX_ACTIVE",)),
+    ("VALU instructions per wave", "SQ_INSTS_VALU", ("SQ_WAVES",)),
+    ("LDS instructions per wave", "SQ_INSTS_LDS", ("SQ_WAVES",)),
+]
+
+
+def counters_md(dbs, kernel, cmds) -> str:
+    """Mean value per dispatch of every counter recorded for `kernel` in the
+    given --pmc runs, plus a few derived ratios."""
+    vals = {}
+    for db in dbs:
+        # a counter may be reported per hardware instance (SE, XCD): sum the
+        # instances of each dispatch, then average over dispatches
+        rows = _db(db).execute(
+            "select counter_name, count(*), avg(total) from (select "
+            "dispatch_id, counter_name, sum(counter_value) as total from "
+            "pmc_events where name like ? group by dispatch_id, counter_name) "
+            "group by counter_name", (kernel + "%",)).fetchall()
+        for c, cnt, v in rows:
+            vals[c] = (cnt, v)
+    if not vals:
+        raise RuntimeError("kernel %s not found in the runs" % kernel)
+    out = ["# Counters of %s" % kernel, "", "Runs:", ""]
+    out += ["    " + c for c in cmds]
+    out += ["", "| counter | dispatches | mean per dispatch |", "|---|---|---|"]
+    for c in sorted(vals):
+        out.append("| %s | %d | %.0f |" % (c, vals[c][0], vals[c][1]))
+    out.append("")
+    for label, num, den in RATIOS:
+        if num in vals and all(d in vals for d in den):
+            d = sum(vals[x][1] for x in den)
+            if d > 0:
+                out.append("* %s: %.3f" % (label, vals[num][1] / d))
+    out += ["", "kernel_source_sha256_16: " + kernel_hash(), ""]
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -132,9 +188,15 @@ def main(argv=None):
     r.add_argument("--algorithmic", type=int, default=None)
     r.add_argument("--cmd-fetch", required=True)
     r.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
     if a.mode == "trace":
         sys.stdout.write(trace_md(a.db, a.cmd))
+    elif a.mode == "counters":
+        sys.stdout.write(counters_md(a.dbs, a.kernel, a.cmd))
     else:
         sys.stdout.write(traffic_md(a.fetch_db, a.write_db, a.kernel, a.name,
                                     a.calib_bytes, a.cmd_fetch, a.cmd_write,

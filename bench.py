@@ -16,7 +16,8 @@ bounded number of whole-grid applications.
 
 --calib adds a plain device copy of known size (for the counter runs that
 turn FETCH_SIZE / WRITE_SIZE into bytes); --only-headline skips everything
-but the timed stencil launches (for profiler runs).
+but the timed stencil launches, --only-others runs only the Jacobi and fp64
+workloads (both for profiler runs).
 """
 from __future__ import annotations
 
@@ -78,6 +79,46 @@ def timed_launches(torch, fn, steps, warmup):
     return wall, durs
 
 
+def flushed_launches(torch, fn, steps, flush_bytes=1 << 30):
+    """Launch durations with 1 GiB of scratch read before each launch, so
+    that no part of the inputs can still sit in the 256 MB Infinity Cache (or
+    L2) from the previous launch.  Reading (not writing) leaves clean lines,
+    so evicting them costs the launch nothing."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.float32,
+                         device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        sink += scratch.sum()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in ev])
+    del scratch, sink
+    torch.cuda.empty_cache()
+    return dict(mean=float(durs.mean()), median=float(np.median(durs)),
+                min=float(durs.min()), launches=steps,
+                flush="1 GiB scratch read before each launch")
+
+
+def cpu_rate(fn, points, budget_s):
+    """Run fn (one oracle evaluation over `points` outputs) until the budget
+    is spent (at least once); GPoints/s from the median duration."""
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    med = float(np.median(times))
+    return points / med / 1e9, len(times), med
+
+
 def star_bytes(interior, R, elem):
     """One read of the interior plus its 2R-deep face slabs, one write of
     the interior (edges and corners of the halo are never read)."""
@@ -101,11 +142,15 @@ def bench_headline(torch, B, wl, args):
     nbytes = star_bytes(w.interior, w.radius, 4)
     mean = float(durs.mean())
     achieved = nbytes / mean / 1e9
+    flushed = None if args.only_headline else flushed_launches(
+        torch, fn, min(args.steps, 20))
     res = dict(
         value=pts * args.steps / wall / 1e9,
         ms_per_step=wall / args.steps * 1e3,
         kernel_ms=dict(mean=mean * 1e3, median=float(np.median(durs)) * 1e3,
-                       min=float(durs.min()) * 1e3),
+                       min=float(durs.min()) * 1e3,
+                       p90=float(np.percentile(durs, 90)) * 1e3),
+        kernel_ms_cache_flushed=flushed,
         roofline=dict(bound="hbm", achieved=round(achieved, 1),
                       peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=round(achieved / PEAK_HBM_GBS, 4),
@@ -153,7 +198,9 @@ def bench_wave(torch, B, wl, args):
     achieved = nbytes / per_step / 1e9
     del vel2, eta, u_prev, u
     torch.cuda.empty_cache()
+    cpu = None if args.no_cpu else cpu_wave_slab(wl, w, args.cpu_budget / 4)
     return dict(workload=w.name, value=pts * runs / wall / 1e9,
+                cpu_baseline=cpu,
                 unit="GPoints/s", ms_per_step=per_step * 1e3,
                 steps_per_run=w.sweeps, runs=runs,
                 roofline=dict(bound="hbm", achieved=round(achieved, 1),
@@ -162,6 +209,34 @@ def bench_wave(torch, B, wl, args):
                               algorithmic_bytes_per_step=nbytes,
                               note="per-step mean incl. the 1-thread source "
                                    "kernel"))
+
+
+def cpu_wave_slab(wl, w, budget_s, planes=64):
+    """The oracle's wave step on a slab of the 1032^3 workload: `planes`
+    interior z planes (plus the R halo planes on each side) of the real
+    fields, mid-simulation values for u and u_prev (seeded uniform), the
+    real vel2 and eta."""
+    import oracle
+    e = w.extra
+    R = w.radius
+    z0 = w.shape[0] // 2 - planes // 2 - R
+    z1 = z0 + planes + 2 * R
+    v2 = wl.vel2_planes(w, z0, z1)
+    et = wl.eta_planes(w, z0, z1)
+    shp = (z1 - z0,) + tuple(w.shape[1:])
+    u = wl.uniform_planes(shp, w.seed + 17, -1, 1)
+    up = wl.uniform_planes(shp, w.seed + 18, -1, 1)
+    c = oracle.laplacian_weights(R)
+    out = np.zeros(shp, np.float64)
+    npts = planes * (w.shape[1] - 2 * R) * (w.shape[2] - 2 * R)
+    rate, nrun, med = cpu_rate(
+        lambda: oracle.wave_step(up, u, v2, et, R, c, e["dt"], e["h"], out=out),
+        npts, budget_s)
+    return dict(value=round(rate, 4), unit="GPoints/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample="%d wave steps on a %d-plane z slab of the 1032^3 "
+                       "grid (fp64 oracle), median %.2f s each"
+                       % (nrun, planes, med))
 
 
 def bench_others(torch, B, wl, args):
@@ -174,7 +249,8 @@ def bench_others(torch, B, wl, args):
 
     w = wl.R1_JACOBI_512
     log("generating %s %s" % (w.name, w.shape))
-    a = torch.from_numpy(wl.input_planes(w)).to(dev)
+    host_j = wl.input_planes(w)
+    a = torch.from_numpy(host_j).to(dev)
     b = torch.empty_like(a)
     d = B.desc_init("f32", w.shape, w.radius, B.DIRICHLET_COPY)
     wall, durs = timed_launches(
@@ -194,10 +270,23 @@ def bench_others(torch, B, wl, args):
                            "HBM (temporal blocking), so the per-sweep rate "
                            "can exceed the one-read-one-write floor"))
     del a, b
+    if not args.no_cpu:
+        import oracle
+        c = list(d.cx[:2])
+        out = np.zeros(host_j.shape, np.float64)
+        rate, nrun, med = cpu_rate(
+            lambda: oracle.star_apply(host_j, 1, c, boundary=1, out=out),
+            w.interior_points, args.cpu_budget / 4)
+        res[w.name]["cpu_baseline"] = dict(
+            value=round(rate, 4), unit="GPoints/s", cores=oracle.num_threads(),
+            kind="oracle", sample="%d single sweeps of the 512^3 grid "
+            "(fp64 oracle), median %.2f s each" % (nrun, med))
+    del host_j
 
     w = wl.R4_RAGGED_F64
     log("generating %s %s" % (w.name, w.shape))
-    inp = torch.from_numpy(wl.input_planes(w)).to(dev)
+    host_f = wl.input_planes(w)
+    inp = torch.from_numpy(host_f).to(dev)
     out = torch.zeros_like(inp)
     d = B.desc_init("f64", w.shape, w.radius)
     wall, durs = timed_launches(
@@ -214,6 +303,17 @@ def bench_others(torch, B, wl, args):
                       algorithmic_bytes=nbytes))
     del inp, out
     torch.cuda.empty_cache()
+    if not args.no_cpu:
+        import oracle
+        c = oracle.laplacian_weights(w.radius)
+        out = np.zeros(host_f.shape, np.float64)
+        rate, nrun, med = cpu_rate(
+            lambda: oracle.star_apply(host_f, w.radius, c, out=out),
+            w.interior_points, args.cpu_budget / 4)
+        res[w.name]["cpu_baseline"] = dict(
+            value=round(rate, 4), unit="GPoints/s", cores=oracle.num_threads(),
+            kind="oracle", sample="%d applications of the whole ragged fp64 "
+            "grid (fp64 oracle), median %.2f s each" % (nrun, med))
     return res
 
 
@@ -262,6 +362,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only-others", action="store_true",
+                    help="run only the Jacobi and fp64 workloads (profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -277,6 +379,11 @@ def main():
         sys.exit(1)
     B.lib()  # fail loudly if the library is missing
 
+    if args.only_others:
+        for k, v in bench_others(torch, B, wl, args).items():
+            log("%s: %.1f GPoints/s, %.1f GB/s"
+                % (k, v["value"], v["roofline"]["achieved"]))
+        return
     head, host = bench_headline(torch, B, wl, args)
     log("headline: %.1f GPoints/s, kernel %.4f ms, %.1f GB/s"
         % (head["value"], head["kernel_ms"]["mean"],
@@ -318,6 +425,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "kernel_ms": head["kernel_ms"],
+        "kernel_ms_cache_flushed": head["kernel_ms_cache_flushed"],
         "hbm_gbs_wall": head["gbs_wall"],
         "wave_step": wave,
         "other_workloads": others,
