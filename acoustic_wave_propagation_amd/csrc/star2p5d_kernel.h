@@ -201,6 +201,26 @@ __device__ __forceinline__ void bstore1(rsrc_t r, uint32_t off, T v) {
     bstore<T, 1>(r, off, a);
 }
 
+// ---- LDS group access --------------------------------------------------------
+// A group of N elements (16 bytes for the shipped tiles) at a 16-byte aligned
+// LDS address, moved as one access (ds_read_b128 / ds_write_b128).  Lanes of
+// a wave touch consecutive 16-byte groups, which the LDS serves without bank
+// conflicts; element-wise (or pairwise) accesses at that lane stride make
+// several lanes hit the same bank.
+template <typename T, int N>
+__device__ __forceinline__ void lds_load_group(const T *p, T (&v)[N]) {
+    static_assert(N * sizeof(T) % 16 == 0, "whole 16-byte groups");
+    const T *q = static_cast<const T *>(__builtin_assume_aligned(p, 16));
+    __builtin_memcpy(v, q, N * sizeof(T));
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void lds_store_group(T *p, const T (&v)[N]) {
+    static_assert(N * sizeof(T) % 16 == 0, "whole 16-byte groups");
+    T *q = static_cast<T *>(__builtin_assume_aligned(p, 16));
+    __builtin_memcpy(q, v, N * sizeof(T));
+}
+
 // Ring sizes of the kernel below, shared with the host so that z chunks can
 // be sized in whole unrolled blocks.
 template <int R, bool WAVE, class C>
@@ -420,9 +440,7 @@ star2p5d_kernel(StarArgs<T> a) {
             //    two, the previous barrier already ordered them.
             if constexpr (C::LB == 1) __syncthreads();
 #pragma unroll
-            for (int j = 0; j < VY; ++j)
-#pragma unroll
-                for (int i = 0; i < VX; ++i) tile[(lrow0 + j) * LP + lcol + i] = win[CS][j][i];
+            for (int j = 0; j < VY; ++j) lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, win[CS][j]);
 #pragma unroll
             for (int q = 0; q < KH; ++q) {
                 T *dst = h_l[q] >= 0 ? tile + h_l[q] : lds + LDUMMY;

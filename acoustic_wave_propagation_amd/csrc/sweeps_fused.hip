@@ -19,8 +19,9 @@ namespace {
 // 2 x 2 (fp64) points per thread keep the input window and the NS-1
 // intermediate rings within two waves per SIMD.  Up to 4 sweeps two sets of
 // LDS tiles fit (one barrier per z step); 5 and 6 sweeps use one set.
-// Measured on 512^3 fp32, ms per pass for NS = 2..6: 0.330, 0.399, 0.467,
-// 0.622, 0.702 (one single sweep: 0.231).
+// Measured on 512^3 fp32, ms per pass for NS = 2..6: 0.328, 0.379, 0.444,
+// 0.574, 0.676 (one single sweep: 0.231); fp64 NS = 2..4: 0.547, 0.694,
+// 0.865 (one sweep: ~0.49).
 template <typename T, int NS>
 struct FusedShipped;
 template <int NS>
@@ -112,8 +113,8 @@ int fused_max_sweeps(const stencil3d_desc &d) {
 const double *fused_pass_costs(const stencil3d_desc &d) {
     // time of a pass of ns sweeps relative to one single sweep (index ns),
     // measured on 512^3 grids
-    static const double f32[] = {0.0, 1.0, 1.43, 1.73, 2.02, 2.69, 3.04};
-    static const double f64[] = {0.0, 1.0, 1.11, 1.40, 1.71};
+    static const double f32[] = {0.0, 1.0, 1.42, 1.64, 1.92, 2.48, 2.93};
+    static const double f64[] = {0.0, 1.0, 1.12, 1.42, 1.77};
     return d.dtype == ST_F64 ? f64 : f32;
 }
 

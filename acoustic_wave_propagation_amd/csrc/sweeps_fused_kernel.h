@@ -171,14 +171,12 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                 constexpr int s = decltype(sc)::value;
                 T *tile = lds + (SET + s) * LTILE;
 #pragma unroll
-                for (int j = 0; j < VY; ++j)
-#pragma unroll
-                    for (int i = 0; i < VX; ++i) {
-                        if constexpr (s == 0)
-                            tile[(lrow0 + j) * LP + lcol + i] = w0[CS][j][i];
-                        else
-                            tile[(lrow0 + j) * LP + lcol + i] = ws[s - 1][CC][j][i];
-                    }
+                for (int j = 0; j < VY; ++j) {
+                    if constexpr (s == 0)
+                        lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, w0[CS][j]);
+                    else
+                        lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, ws[s - 1][CC][j]);
+                }
             });
             __syncthreads();
 
@@ -198,13 +196,30 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                         return ws[s - 1][((CC + dz) % WS + WS) % WS][j][i];
                 };
                 T xs[VY][VX + 2 * R];  // row segment, columns ex-R .. ex+VX+R-1
+                // With R < VX only part of each neighbouring group is needed;
+                // the whole groups are still read (one conflict-free 16-byte
+                // access each) and kept alive until the stage's end, where an
+                // empty asm statement uses them, so the loads are not narrowed
+                // to the single elements (which, at a 16-byte lane stride,
+                // would make lanes collide on LDS banks).
+                T lg[VY][VX], rg[VY][VX];
 #pragma unroll
                 for (int j = 0; j < VY; ++j) {
                     const T *row = tile + (lrow0 + j) * LP + lcol;
+                    if constexpr (R <= VX) {
+                        lds_load_group<T, VX>(row - VX, lg[j]);
+                        lds_load_group<T, VX>(row + VX, rg[j]);
 #pragma unroll
-                    for (int m = 0; m < R; ++m) {
-                        xs[j][m] = row[m - R];
-                        xs[j][R + VX + m] = row[VX + m];
+                        for (int m = 0; m < R; ++m) {
+                            xs[j][m] = lg[j][VX - R + m];
+                            xs[j][R + VX + m] = rg[j][m];
+                        }
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < R; ++m) {
+                            xs[j][m] = row[m - R];
+                            xs[j][R + VX + m] = row[VX + m];
+                        }
                     }
 #pragma unroll
                     for (int i = 0; i < VX; ++i) xs[j][R + i] = zv(std::integral_constant<int, 0>{}, j, i);
@@ -245,6 +260,12 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                         // the boundary keeps its value in every sweep
                         res[j][i] = (zin && rin[j] && cin[i]) ? acc : ctr;
                     }
+                if constexpr (R < VX) {
+#pragma unroll
+                    for (int j = 0; j < VY; ++j)
+#pragma unroll
+                        for (int i = 0; i < VX; ++i) asm volatile("" ::"v"(lg[j][i]), "v"(rg[j][i]));
+                }
 
                 if constexpr (s < NS - 1) {
 #pragma unroll
