@@ -1,0 +1,65 @@
+"""Rewrite the rocprofv3 summaries under profiles/ from the raw output of
+one profiling session (the databases the commands below leave under
+gpurun_out/, relative to the repository root).
+
+    python -m acoustic_wave_propagation_amd.profiles_refresh [RAW_DIR]
+
+Each summary records the exact command that produced its database; the
+commands are run from /tmp with TMPDIR=/tmp and the repository at $REPO.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+from . import profiling as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PRE = "cd /tmp && TMPDIR=/tmp rocprofv3 "
+BENCH = " -- python3 $REPO/bench.py "
+SQ = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+      "SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES SQ_WAIT_INST_LDS")
+CMDS = {
+    "trace": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_trace -o trace"
+    + BENCH + "--only-headline --steps 50 --warmup 10",
+    "fetch": PRE + "--pmc FETCH_SIZE -T -d $REPO/gpurun_out/pmc_fetch -o fetch"
+    + BENCH + "--only-headline --calib --steps 5 --warmup 2",
+    "write": PRE + "--pmc WRITE_SIZE -T -d $REPO/gpurun_out/pmc_write -o write"
+    + BENCH + "--only-headline --calib --steps 5 --warmup 2",
+    "others": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_others -o others"
+    + BENCH + "--only-others --no-cpu --steps 20 --warmup 5",
+    "sq": PRE + "--pmc " + SQ + " -T -d $REPO/gpurun_out/pmc_sq -o sq"
+    + BENCH + "--only-headline --steps 5 --warmup 2",
+    "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $REPO/gpurun_out/pmc_tcc -o tcc"
+    + BENCH + "--only-headline --steps 5 --warmup 2",
+}
+HEADLINE_BYTES = 1098907648  # algorithmic bytes of one 512^3 R=4 fp32 apply
+
+
+def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    raw = argv[0] if argv else os.path.join(ROOT, "gpurun_out")
+    prof = os.path.join(ROOT, "profiles")
+    db = lambda d, n: os.path.join(raw, d, n + "_results.db")
+    out = {
+        "star2p5d_r4_512cube_trace.md":
+            P.trace_md(db("prof_trace", "trace"), CMDS["trace"]),
+        "star2p5d_r4_512cube_traffic.md":
+            P.traffic_md(db("pmc_fetch", "fetch"), db("pmc_write", "write"),
+                         "star2p5d_kernel", "star2p5d_r4_f32", 1 << 30,
+                         CMDS["fetch"], CMDS["write"], HEADLINE_BYTES),
+        "jacobi_r1_512cube_and_f64_ragged_trace.md":
+            P.trace_md(db("prof_others", "others"), CMDS["others"]),
+        "star2p5d_r4_512cube_counters.md":
+            P.counters_md([db("pmc_sq", "sq"), db("pmc_tcc", "tcc")],
+                          "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
+    }
+    for name, text in out.items():
+        with open(os.path.join(prof, name), "w") as f:
+            f.write(text)
+        print("wrote profiles/" + name)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
