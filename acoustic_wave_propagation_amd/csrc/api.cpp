@@ -81,6 +81,41 @@ const double *second_difference(int R) {
     return nullptr;
 }
 
+// The wave update on the interior.  When the descriptor states a sponge
+// width p (eta = 0 at least p points inside every interior face) and the
+// eta-free kernel exists, the interior is launched as data regions -- an
+// inner box at distance >= p from every face, which does not read eta, and
+// six slabs that do ("Accelerating High-Order Stencils on GPUs": one kernel
+// for the inner region, another for the PML region).  Every point is
+// written by exactly one launch with the same arithmetic, so the result is
+// bit-identical to one launch over the interior.
+int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void *u_prev,
+                const void *vel2, const void *eta, double wscale, int cus, hipStream_t s) {
+    const st::Box in = st::interior_box(d);
+    const int64_t p = d.pml_width;
+    auto fits = [p](int64_t lo, int64_t hi) { return p < hi - lo && 2 * p < hi - lo; };
+    const bool split = p > 0 && st::kind_available(d, st::Kind::WaveNoEta) &&
+                       fits(in.x0, in.x1) && fits(in.y0, in.y1) && fits(in.z0, in.z1);
+    if (!split)
+        return st::launch_star(d, in, st::Kind::Wave, u, u_next, u_prev, vel2, eta, wscale, cus,
+                               s);
+    const st::Box c{in.x0 + p, in.x1 - p, in.y0 + p, in.y1 - p, in.z0 + p, in.z1 - p};
+    const st::Box slabs[6] = {
+        {in.x0, in.x1, in.y0, in.y1, in.z0, c.z0},  // below the inner box in z
+        {in.x0, in.x1, in.y0, in.y1, c.z1, in.z1},  // above
+        {in.x0, in.x1, in.y0, c.y0, c.z0, c.z1},    // in its z range: y < inner
+        {in.x0, in.x1, c.y1, in.y1, c.z0, c.z1},    // y > inner
+        {in.x0, c.x0, c.y0, c.y1, c.z0, c.z1},      // inner y, z: x < inner
+        {c.x1, in.x1, c.y0, c.y1, c.z0, c.z1},      // x > inner
+    };
+    int st = st::launch_star(d, c, st::Kind::WaveNoEta, u, u_next, u_prev, vel2, eta, wscale,
+                             cus, s);
+    for (int i = 0; i < 6 && st == ST_OK; ++i)
+        st = st::launch_star(d, slabs[i], st::Kind::Wave, u, u_next, u_prev, vel2, eta, wscale,
+                             cus, s);
+    return st;
+}
+
 int wave_checks(const stencil3d_desc *d, double dt, double h) {
     if (!isfinite(dt) || !isfinite(h) || !(h > 0.0)) return ST_ERR_ARG;
     (void)d;
@@ -158,7 +193,8 @@ int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out, void *st
     const int cus = current_cus(&st);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = st::launch_star(*d, in, out, nullptr, nullptr, nullptr, false, 1.0, cus, s);
+    st = st::launch_star(*d, st::interior_box(*d), st::Kind::Apply, in, out, nullptr, nullptr,
+                         nullptr, 1.0, cus, s);
     if (st == ST_OK && d->boundary == ST_BC_DIRICHLET_COPY)
         st = st::launch_shell_copy(*d, in, out, s);
     return st;
@@ -186,8 +222,8 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, int sweeps
     void *b[2] = {buf0, buf1};
     int cur = 0;
     auto pass = [&](int ns) {
-        const int r = ns == 1 ? st::launch_star(di, b[cur], b[cur ^ 1], nullptr, nullptr, nullptr,
-                                                false, 1.0, cus, s)
+        const int r = ns == 1 ? st::launch_star(di, st::interior_box(di), st::Kind::Apply, b[cur],
+                                                b[cur ^ 1], nullptr, nullptr, nullptr, 1.0, cus, s)
                               : st::launch_sweeps_fused(di, b[cur], b[cur ^ 1], ns, cus, s);
         cur ^= 1;
         return r;
@@ -222,8 +258,8 @@ int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
-    return st::launch_star(*d, u, u_next, u_prev, vel2, eta, true, (dt * dt) / (h * h), cus,
-                           static_cast<hipStream_t>(stream));
+    return launch_wave(*d, u, u_next, u_prev, vel2, eta, (dt * dt) / (h * h), cus,
+                       static_cast<hipStream_t>(stream));
 }
 
 int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, int64_t iz,
@@ -256,7 +292,7 @@ int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2, c
     const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
     void *a = u_prev, *b = u;  // a: older, b: newer
     for (int n = 0; n < nsteps; ++n) {
-        st = st::launch_star(*d, b, a, a, vel2, eta, true, wscale, cus, s);
+        st = launch_wave(*d, b, a, a, vel2, eta, wscale, cus, s);
         if (st) return st;
         if (src_trace && (st = st::launch_add_source(*d, a, idx, src_trace[n], s))) return st;
         void *t = a;

@@ -9,25 +9,48 @@
 
 namespace st {
 
-// Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs,
-// each streamed through a z-chunk of chunk_len interior planes.
-struct Geometry {
-    int tile_x, tile_y, threads;
-    int tiles_x, tiles_y, nchunks, chunk_len, nwg;
-    int variant;  // 0: the primary tile shape, 1: the row-wide one
+// An output box [x0,x1) x [y0,y1) x [z0,z1) in allocated coordinates.
+struct Box {
+    int64_t x0, x1, y0, y1, z0, z1;
 };
 
-// Geometry the kernel for (dtype, R, op) would use on a device with `cus`
-// compute units.  Host only.
-Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus);
+// The interior of d: every point whose whole stencil lies in the array.
+inline Box interior_box(const stencil3d_desc &d) {
+    const int64_t R = d.radius;
+    return Box{R, d.nx - R, R, d.ny - R, R, d.nz - R};
+}
 
-// Enqueue the streaming stencil.  wave == false: out = star(in) on the
-// interior.  wave == true: out = wave update of (u_prev, in = u, vel2, eta)
-// with the weights scaled by wscale = dt^2/h^2.  Arguments are validated by
-// the caller.  Returns ST_OK or ST_ERR_LAUNCH.
-int launch_star(const stencil3d_desc &d, const void *in, void *out,
-                const void *u_prev, const void *vel2, const void *eta,
-                bool wave, double wscale, int cus, hipStream_t stream);
+// Variants of the streaming kernel.  Apply: out = star(in).  Wave: the
+// wave update of (u_prev, in = u, vel2, eta).  The planner may replace
+// Apply by ApplyWide (row-wide tiles) and Wave by WaveNarrow (32-column
+// tiles) where those fit the box better; WaveNoEta is the wave update for a
+// box where eta is zero (no eta stream).
+enum class Kind { Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta };
+
+// Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs
+// covering the output box, each streamed through a z chunk of chunk_len
+// planes.
+struct Geometry {
+    Kind kind;
+    Box box;
+    int tile_x, tile_y, threads;
+    int tiles_x, tiles_y, nchunks, chunk_len, nwg;
+};
+
+// Whether the kernel variant is instantiated for d's type and radius.
+bool kind_available(const stencil3d_desc &d, Kind k);
+
+// Geometry of a launch of `kind` over `box` (inside d's interior) on a
+// device with `cus` compute units.  Host only.
+Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int cus);
+
+// Enqueue the streaming stencil on the output box (inside the interior;
+// empty boxes enqueue nothing).  Wave variants scale the weights by wscale
+// = dt^2/h^2.  Arguments are validated by the caller.  Returns ST_OK,
+// ST_ERR_ARG (variant not instantiated) or ST_ERR_LAUNCH.
+int launch_star(const stencil3d_desc &d, const Box &box, Kind kind, const void *in, void *out,
+                const void *u_prev, const void *vel2, const void *eta, double wscale, int cus,
+                hipStream_t stream);
 
 // Largest number of sweeps one fused pass can do for d (1: no fused kernel
 // for this radius and element type).

@@ -36,108 +36,153 @@ using F32Wave = TileCfg<4, 2, 32, 16, 1, 0>;
 using F64Apply = TileCfg<2, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
 using F64Wave = TileCfg<2, 2, 32, 16, 1, 0>;
 
-template <typename T, int R, bool WAVE>
-struct Shipped {
+// Narrow tiles for the thin x slabs of the wave step's sponge (32 columns):
+// 4 x 2 (fp32) or 2 x 2 (fp64) per thread, 8 x 64 or 16 x 32 threads ->
+// 32 x 128 or 32 x 64 tiles.  On a full 1024^3 step they run 7% slower than
+// the primary tiles; on a 32-wide box they avoid three quarters idle lanes.
+using F32WaveNarrow = TileCfg<4, 2, 8, 64, 1, 0>;
+using F64WaveNarrow = TileCfg<2, 2, 16, 32, 1, 0>;
+
+// Kernel variant of a launch: its tile configuration and template flags.
+template <typename T, int R, Kind K>
+struct KindCfg {
+    static constexpr bool f64 = std::is_same<T, double>::value;
+    static constexpr bool wave = K == Kind::Wave || K == Kind::WaveNarrow || K == Kind::WaveNoEta;
+    static constexpr bool eta = K != Kind::WaveNoEta;
+    using Apply = typename std::conditional<f64, F64Apply,
+                  typename std::conditional<R == 1, F32ApplyR1, F32Apply>::type>::type;
     using Cfg = typename std::conditional<
-        std::is_same<T, double>::value,
-        typename std::conditional<WAVE, F64Wave, F64Apply>::type,
-        typename std::conditional<WAVE, F32Wave,
-                                  typename std::conditional<R == 1, F32ApplyR1,
-                                                            F32Apply>::type>::type>::type;
-    // row-wide alternative (void: none)
-    using Wide = typename std::conditional<!WAVE && R == 1 && std::is_same<T, float>::value,
-                                           F32ApplyR1Wide, void>::type;
+        K == Kind::ApplyWide && R == 1 && !f64, F32ApplyR1Wide,
+        typename std::conditional<
+            K == Kind::WaveNarrow, typename std::conditional<f64, F64WaveNarrow, F32WaveNarrow>::type,
+            typename std::conditional<wave, typename std::conditional<f64, F64Wave, F32Wave>::type,
+                                      Apply>::type>::type>::type;
 };
 
-template <typename T, int R, bool WAVE, int V>
-using CfgOf = typename std::conditional<V == 1 && !std::is_void<typename Shipped<T, R, WAVE>::Wide>::value,
-                                        typename Shipped<T, R, WAVE>::Wide,
-                                        typename Shipped<T, R, WAVE>::Cfg>::type;
+// Variants that exist for radius R (the others fall back to the primary
+// ones): the row-wide apply for fp32 R = 1, the narrow and eta-free wave
+// kernels for R = 4, the radius of the acoustic model with a sponge.
+template <typename T, int R>
+constexpr bool kind_exists(Kind k) {
+    return k == Kind::Apply || k == Kind::Wave ||
+           (k == Kind::ApplyWide && R == 1 && std::is_same<T, float>::value) ||
+           ((k == Kind::WaveNarrow || k == Kind::WaveNoEta) && R == 4);
+}
+
+template <typename T, int R, Kind K>
+int launch_kind(const StarArgs<T> &a, int nwg, hipStream_t stream) {
+    using KC = KindCfg<T, R, K>;
+    hipLaunchKernelGGL((star2p5d_kernel<T, R, KC::wave, typename KC::Cfg, KC::eta>), dim3(nwg),
+                       dim3(KC::Cfg::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
+}
 
 template <typename T, int R>
 int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, void *out,
-                 const void *u_prev, const void *vel2, const void *eta, bool wave,
-                 double wscale, hipStream_t stream) {
-    const StarArgs<T> a = make_args<T, R>(d, in, out, u_prev, vel2, eta, wscale, g.tiles_x,
+                 const void *u_prev, const void *vel2, const void *eta, double wscale,
+                 hipStream_t stream) {
+    const StarArgs<T> a = make_args<T, R>(d, g.box, in, out, u_prev, vel2, eta, wscale, g.tiles_x,
                                           g.tiles_y, g.chunk_len, g.nwg);
-    const dim3 grid(g.nwg), block(g.threads);
-    if (wave)
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, true, CfgOf<T, R, true, 0>>), grid, block, 0,
-                           stream, a);
-    else if (g.variant == 1)
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, CfgOf<T, R, false, 1>>), grid, block,
-                           0, stream, a);
-    else
-        hipLaunchKernelGGL((star2p5d_kernel<T, R, false, CfgOf<T, R, false, 0>>), grid, block,
-                           0, stream, a);
-    return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
+    switch (g.kind) {
+    case Kind::ApplyWide:
+        if constexpr (kind_exists<T, R>(Kind::ApplyWide))
+            return launch_kind<T, R, Kind::ApplyWide>(a, g.nwg, stream);
+        break;
+    case Kind::Wave: return launch_kind<T, R, Kind::Wave>(a, g.nwg, stream);
+    case Kind::WaveNarrow:
+        if constexpr (kind_exists<T, R>(Kind::WaveNarrow))
+            return launch_kind<T, R, Kind::WaveNarrow>(a, g.nwg, stream);
+        break;
+    case Kind::WaveNoEta:
+        if constexpr (kind_exists<T, R>(Kind::WaveNoEta))
+            return launch_kind<T, R, Kind::WaveNoEta>(a, g.nwg, stream);
+        break;
+    default: return launch_kind<T, R, Kind::Apply>(a, g.nwg, stream);
+    }
+    return ST_ERR_ARG;  // the planner never picks a variant that does not exist
 }
 
 template <typename T>
 int launch_r(const stencil3d_desc &d, const Geometry &g, const void *in, void *out,
-             const void *u_prev, const void *vel2, const void *eta, bool wave, double wscale,
+             const void *u_prev, const void *vel2, const void *eta, double wscale,
              hipStream_t s) {
     switch (d.radius) {
-    case 1: return launch_typed<T, 1>(d, g, in, out, u_prev, vel2, eta, wave, wscale, s);
-    case 2: return launch_typed<T, 2>(d, g, in, out, u_prev, vel2, eta, wave, wscale, s);
-    case 3: return launch_typed<T, 3>(d, g, in, out, u_prev, vel2, eta, wave, wscale, s);
-    case 4: return launch_typed<T, 4>(d, g, in, out, u_prev, vel2, eta, wave, wscale, s);
+    case 1: return launch_typed<T, 1>(d, g, in, out, u_prev, vel2, eta, wscale, s);
+    case 2: return launch_typed<T, 2>(d, g, in, out, u_prev, vel2, eta, wscale, s);
+    case 3: return launch_typed<T, 3>(d, g, in, out, u_prev, vel2, eta, wscale, s);
+    case 4: return launch_typed<T, 4>(d, g, in, out, u_prev, vel2, eta, wscale, s);
     }
     return ST_ERR_RADIUS;
 }
 
-// Tile shape, threads and z unroll of the shipped kernel for (T, R, WAVE).
+// Tile shape, threads and z unroll of a kernel variant.
 struct Shape {
     int tile_x, tile_y, threads, unroll, prologue;
+    bool exists;
 };
 
-template <typename T, int R, bool WAVE, int V>
+template <typename T, int R, Kind K>
 Shape shape_of() {
-    using C = CfgOf<T, R, WAVE, V>;
-    using RG = Rings<R, WAVE, C>;
-    return Shape{C::TX, C::TY, C::NT, RG::U, 2 * R + RG::D};
+    using KC = KindCfg<T, R, K>;
+    using C = typename KC::Cfg;
+    using RG = Rings<R, KC::wave, C>;
+    return Shape{C::TX, C::TY, C::NT, RG::U, 2 * R + RG::D, kind_exists<T, R>(K)};
 }
 
-template <typename T, bool WAVE, int V>
-Shape shape_r(int R) {
-    switch (R) {
-    case 1: return shape_of<T, 1, WAVE, V>();
-    case 2: return shape_of<T, 2, WAVE, V>();
-    case 3: return shape_of<T, 3, WAVE, V>();
-    default: return shape_of<T, 4, WAVE, V>();
+template <typename T, int R>
+Shape shape_k(Kind k) {
+    switch (k) {
+    case Kind::ApplyWide: return shape_of<T, R, Kind::ApplyWide>();
+    case Kind::Wave: return shape_of<T, R, Kind::Wave>();
+    case Kind::WaveNarrow: return shape_of<T, R, Kind::WaveNarrow>();
+    case Kind::WaveNoEta: return shape_of<T, R, Kind::WaveNoEta>();
+    default: return shape_of<T, R, Kind::Apply>();
     }
 }
 
-Shape shape_for(const stencil3d_desc &d, bool wave, int variant) {
-    if (d.dtype == ST_F64)
-        return wave ? shape_r<double, true, 0>(d.radius)
-                    : (variant ? shape_r<double, false, 1>(d.radius)
-                               : shape_r<double, false, 0>(d.radius));
-    return wave ? shape_r<float, true, 0>(d.radius)
-                : (variant ? shape_r<float, false, 1>(d.radius) : shape_r<float, false, 0>(d.radius));
+template <typename T>
+Shape shape_t(int R, Kind k) {
+    switch (R) {
+    case 1: return shape_k<T, 1>(k);
+    case 2: return shape_k<T, 2>(k);
+    case 3: return shape_k<T, 3>(k);
+    default: return shape_k<T, 4>(k);
+    }
+}
+
+Shape shape_for(const stencil3d_desc &d, Kind k) {
+    return d.dtype == ST_F64 ? shape_t<double>(d.radius, k) : shape_t<float>(d.radius, k);
 }
 
 }  // namespace
 
-Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus) {
-    // The row-wide variant (if this kernel has one) is taken when one of its
-    // tiles spans an interior row that needs two of the primary tiles and
-    // fills at least 7/8 of it (measured: 510 and 512 wide rows gain 5-13%,
-    // a 300 wide row loses a third).
-    const int64_t ixr = d.nx - 2 * (int64_t)d.radius;
-    const Shape prim = shape_for(d, wave, 0), wide = shape_for(d, wave, 1);
-    const int variant = (wide.tile_x > prim.tile_x && ixr > prim.tile_x &&
-                         8 * ixr > 7 * (int64_t)wide.tile_x && ixr <= wide.tile_x);
-    const Shape sh = variant ? wide : prim;
+bool kind_available(const stencil3d_desc &d, Kind k) { return shape_for(d, k).exists; }
+
+Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int cus) {
+    const int64_t bx = box.x1 - box.x0, by = box.y1 - box.y0, bz = box.z1 - box.z0;
+    if (kind == Kind::Apply) {
+        // The row-wide variant (if this kernel has one) is taken when one of
+        // its tiles spans a box row that needs two of the primary tiles and
+        // fills at least 7/8 of it (measured: 510 and 512 wide rows gain
+        // 5-13%, a 300 wide row loses a third).
+        const Shape prim = shape_for(d, Kind::Apply), wide = shape_for(d, Kind::ApplyWide);
+        if (wide.exists && wide.tile_x > prim.tile_x && bx > prim.tile_x &&
+            8 * bx > 7 * (int64_t)wide.tile_x && bx <= wide.tile_x)
+            kind = Kind::ApplyWide;
+    } else if (kind == Kind::Wave) {
+        // a box no wider than the narrow wave tile (the sponge's x slabs)
+        const Shape prim = shape_for(d, Kind::Wave), nar = shape_for(d, Kind::WaveNarrow);
+        if (nar.exists && nar.tile_x < prim.tile_x && bx <= nar.tile_x) kind = Kind::WaveNarrow;
+    }
+    const Shape sh = shape_for(d, kind);
     Geometry g;
-    g.variant = variant;
+    g.kind = kind;
+    g.box = box;
     g.tile_x = sh.tile_x;
     g.tile_y = sh.tile_y;
     g.threads = sh.threads;
-    const int R = d.radius;
-    const int64_t ix = d.nx - 2 * R, iy = d.ny - 2 * R, iz = d.nz - 2 * R;
-    g.tiles_x = (int)((ix + g.tile_x - 1) / g.tile_x);
-    g.tiles_y = (int)((iy + g.tile_y - 1) / g.tile_y);
+    g.tiles_x = (int)((bx + g.tile_x - 1) / g.tile_x);
+    g.tiles_y = (int)((by + g.tile_y - 1) / g.tile_y);
     const int64_t tiles = (int64_t)g.tiles_x * g.tiles_y;
     // Split z into chunks.  About 512 threads run per compute unit (the
     // register window allows two waves per SIMD), so `cap` workgroups run at
@@ -146,13 +191,14 @@ Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus) {
     // that minimises rounds * (chunk + fill); never below 4R planes per
     // chunk; chunk lengths are whole blocks of the kernel's z unroll (the
     // kernel runs whole blocks).
+    const int R = d.radius;
     const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * (g.threads >= 512 ? 1 : 512 / g.threads);
-    const int64_t maxch = iz / (4 * R) > 0 ? iz / (4 * R) : 1;
+    const int64_t maxch = bz / (4 * R) > 0 ? bz / (4 * R) : 1;
     int64_t best_len = 0, best_nch = 1, best_cost = -1;
     for (int64_t nch = 1; nch <= maxch; ++nch) {
-        int64_t len = (iz + nch - 1) / nch;
+        int64_t len = (bz + nch - 1) / nch;
         len = (len + sh.unroll - 1) / sh.unroll * sh.unroll;
-        const int64_t n = (iz + len - 1) / len;
+        const int64_t n = (bz + len - 1) / len;
         const int64_t rounds = (tiles * n + cap - 1) / cap;
         const int64_t cost = rounds * (len + sh.prologue + 4);
         if (best_cost < 0 || cost < best_cost) {
@@ -167,13 +213,14 @@ Geometry plan_geometry(const stencil3d_desc &d, bool wave, int cus) {
     return g;
 }
 
-int launch_star(const stencil3d_desc &d, const void *in, void *out, const void *u_prev,
-                const void *vel2, const void *eta, bool wave, double wscale, int cus,
+int launch_star(const stencil3d_desc &d, const Box &box, Kind kind, const void *in, void *out,
+                const void *u_prev, const void *vel2, const void *eta, double wscale, int cus,
                 hipStream_t stream) {
-    const Geometry g = plan_geometry(d, wave, cus);
+    if (box.x1 <= box.x0 || box.y1 <= box.y0 || box.z1 <= box.z0) return ST_OK;  // empty
+    const Geometry g = plan_geometry(d, box, kind, cus);
     if (d.dtype == ST_F64)
-        return launch_r<double>(d, g, in, out, u_prev, vel2, eta, wave, wscale, stream);
-    return launch_r<float>(d, g, in, out, u_prev, vel2, eta, wave, wscale, stream);
+        return launch_r<double>(d, g, in, out, u_prev, vel2, eta, wscale, stream);
+    return launch_r<float>(d, g, in, out, u_prev, vel2, eta, wscale, stream);
 }
 
 int launch_shell_copy(const stencil3d_desc &d, const void *in, void *out, hipStream_t stream) {

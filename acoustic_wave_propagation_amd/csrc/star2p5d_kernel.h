@@ -45,6 +45,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "internal.h"
 #include "stencil3d.h"
 
 namespace st {
@@ -61,7 +62,9 @@ struct StarArgs {
     int64_t pz;       // plane pitch in elements (nx * ny)
     int32_t nx, ny, nz;
     int32_t tiles_x, tiles_y, chunk_len, nwg;
-    int32_t pml;      // eta is zero this far inside the interior (0: no claim)
+    // output box [bx0,bx1) x [by0,by1) x [bz0,bz1): inside the interior; the
+    // tiles and z chunks cover it, and only its points are written
+    int32_t bx0, bx1, by0, by1, bz0, bz1;
     T cc;             // centre weight, plain form
     T ccd;            // centre weight of the difference form
     T cx[ST_MAX_R], cy[ST_MAX_R], cz[ST_MAX_R];  // weight of offsets +-(k+1)
@@ -75,16 +78,14 @@ struct StarArgs {
 // alternating z direction of neighbouring chunks, chunk-major (vs
 // tile-major) order of the logical workgroup id, XCD remap, nontemporal
 // stores, nontemporal epilogue loads, minimum waves per SIMD the register
-// allocation must allow, data-region skip per tile (vs per lane),
-// nontemporal stencil-input loads.  The shipped choices are in
-// star2p5d.hip; the others are kept for measurement.
+// allocation must allow, nontemporal stencil-input loads.  The shipped
+// choices are in star2p5d.hip; the others are kept for measurement.
 template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
           bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
-          bool NTL_ = false, int MINW_ = 1, bool ETILE_ = false, bool NTI_ = false>
+          bool NTL_ = false, int MINW_ = 1, bool NTI_ = false>
 struct TileCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
     static constexpr int MINW = MINW_;  // register budget for >= MINW waves per SIMD
-    static constexpr bool ETILE = ETILE_;  // data-region skip per tile (else per lane)
     static constexpr bool NTI = NTI_;      // nontemporal stencil-input loads
     static constexpr bool HLA = HLA_, ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_,
                           NTL = NTL_;
@@ -240,7 +241,11 @@ struct Rings {
     static constexpr int U = clcm(clcm(clcm(W, H), E), C::LB);  // z-loop unroll
 };
 
-template <typename T, int R, bool WAVE, class C>
+// WAVE: fused wave epilogue.  ETA (wave only): read eta; without it the
+// kernel evaluates the same update with eta = 0 (no eta stream, and the
+// factors 1 - eta and 1 / (1 + eta) fold away exactly), for boxes where the
+// caller guarantees eta = 0.
+template <typename T, int R, bool WAVE, class C, bool ETA = true>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
 star2p5d_kernel(StarArgs<T> a) {
     constexpr int VX = C::VX, VY = C::VY, LX = C::LX;
@@ -286,10 +291,10 @@ star2p5d_kernel(StarArgs<T> a) {
     }
     const int tyi = trem / a.tiles_x;
     const int txi = trem - tyi * a.tiles_x;
-    const int gx0 = R + txi * TX;
-    const int gy0 = R + tyi * TY;
-    const int zs = R + chunk * a.chunk_len;
-    const int ze = min(zs + a.chunk_len, a.nz - R);
+    const int gx0 = a.bx0 + txi * TX;
+    const int gy0 = a.by0 + tyi * TY;
+    const int zs = a.bz0 + chunk * a.chunk_len;
+    const int ze = min(zs + a.chunk_len, a.bz1);
     const int n = ze - zs;                      // planes of this chunk
     // Odd chunks stream downwards, so two neighbouring chunks reach their
     // shared boundary planes at the same time (both at their start, or both
@@ -299,17 +304,8 @@ star2p5d_kernel(StarArgs<T> a) {
     const int z0 = dir > 0 ? zs : ze - 1;       // plane of step 0
     const int64_t pzb = a.pz * (int64_t)ES;     // plane bytes
     const int64_t totb = pzb * a.nz;            // allocation bytes
-    // some columns of this tile lie outside the interior (ragged x edge)
-    const bool xpart = gx0 + TX > nx - R;
-    // Data regions of the wave step: on planes and rows where the caller
-    // guarantees eta = 0 (at least pml points inside the interior), a lane
-    // whose columns are all inside too reads eta at offset kOOB -- the load
-    // returns 0, the value it would have read, without a memory request.
-    const int pml = a.pml;
-    const int zin0 = R + pml, zin1 = a.nz - R - pml;  // inner planes
-    const bool tile_inner = pml > 0 && gx0 >= R + pml && gy0 >= R + pml &&
-                            min(gx0 + TX, nx - R) <= nx - R - pml &&
-                            min(gy0 + TY, ny - R) <= ny - R - pml;
+    // some columns of this tile lie outside the box (ragged x edge)
+    const bool xpart = gx0 + TX > a.bx1;
 
     // ---- own outputs: columns ox..ox+VX-1 on rows oy0..oy0+VY-1 ----------
     const int lx = tid % LX, ly = tid / LX;
@@ -320,16 +316,9 @@ star2p5d_kernel(StarArgs<T> a) {
 #pragma unroll
     for (int j = 0; j < VY; ++j) {
         ooff[j] = ((uint32_t)(oy0 + j) * (uint32_t)nx + (uint32_t)ox) * ES;
-        soff[j] = (oy0 + j < ny - R && ox < nx - R) ? ooff[j] : kOOB;
+        soff[j] = (oy0 + j < a.by1 && ox < a.bx1) ? ooff[j] : kOOB;
     }
-    const int nvx = max(0, min(VX, nx - R - ox));  // written columns (ragged x)
-    uint32_t eoff[VY];   // eta offset on inner planes: kOOB where eta = 0
-    const bool x_inner = ox >= R + pml && ox + VX <= nx - R - pml;
-#pragma unroll
-    for (int j = 0; j < VY; ++j) {
-        const bool y_inner = oy0 + j >= R + pml && oy0 + j < ny - R - pml;
-        eoff[j] = (pml > 0 && x_inner && y_inner) ? kOOB : ooff[j];
-    }
+    const int nvx = max(0, min(VX, a.bx1 - ox));  // written columns (ragged x)
     const int lcol = PADL + lx * VX;
     const int lrow0 = R + ly * VY;
 
@@ -385,15 +374,16 @@ star2p5d_kernel(StarArgs<T> a) {
     };
     auto load_epilogue = [&](int k, bool needed, auto slot_c) {
         constexpr int e = decltype(slot_c)::value;
-        const int z = z0 + dir * k;
-        const bool z_inner = z >= zin0 && z < zin1;
-        const rsrc_t rp = rsrc_at(a.u_prev, k, 0, needed), rv = rsrc_at(a.vel2, k, 0, needed),
-                     re = rsrc_at(a.eta, k, 0, needed && !(C::ETILE && tile_inner && z_inner));
+        const rsrc_t rp = rsrc_at(a.u_prev, k, 0, needed), rv = rsrc_at(a.vel2, k, 0, needed);
 #pragma unroll
         for (int jj = 0; jj < VY; ++jj) {
             bload<T, VX, LAUX>(rp, ooff[jj], up[e][jj]);
             bload<T, VX, LAUX>(rv, ooff[jj], v2[e][jj]);
-            bload<T, VX, LAUX>(re, (!C::ETILE && z_inner) ? eoff[jj] : ooff[jj], et[e][jj]);
+        }
+        if constexpr (ETA) {
+            const rsrc_t re = rsrc_at(a.eta, k, 0, needed);
+#pragma unroll
+            for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(re, ooff[jj], et[e][jj]);
         }
     };
 
@@ -498,25 +488,31 @@ star2p5d_kernel(StarArgs<T> a) {
                     }
                     if constexpr (WAVE) {
                         // the weights carry dt^2/h^2: acc = dt^2 * Lap(u)
-                        const T e = et[EC][j][i];
+                        const T e = ETA ? et[EC][j][i] : T(0);
                         acc = (T(2) * ctr - (T(1) - e) * up[EC][j][i] + v2[EC][j][i] * acc) /
                               (T(1) + e);
                     }
                     res[j][i] = acc;
                 }
 
-            // 4. store the written part: rows outside the interior carry
-            //    kOOB; a tile on the ragged x edge stores element by element
+            // 4. store the written part: rows outside the box carry kOOB.  In
+            //    a tile on the ragged x edge of the box, lanes whose group is
+            //    whole store it in one access and the (at most one) partial
+            //    group of a row is stored element by element; the other
+            //    lanes' accesses of each kind are dropped (kOOB), so no lane
+            //    branches and every wave issues the same instructions.
             const rsrc_t ro = rsrc_at(a.out, k, 0, k < n);
             if (!xpart) {
 #pragma unroll
                 for (int j = 0; j < VY; ++j) bstore<T, VX, SAUX>(ro, soff[j], res[j]);
             } else {
 #pragma unroll
-                for (int j = 0; j < VY; ++j)
+                for (int j = 0; j < VY; ++j) {
+                    bstore<T, VX, SAUX>(ro, nvx == VX ? soff[j] : kOOB, res[j]);
 #pragma unroll
-                    for (int i = 0; i < VX; ++i)
-                        bstore1<T>(ro, i < nvx ? soff[j] + i * ES : kOOB, res[j][i]);
+                    for (int i = 0; i < VX - 1; ++i)
+                        bstore1<T>(ro, i < nvx && nvx < VX ? soff[j] + i * ES : kOOB, res[j][i]);
+                }
             }
         });
     }
@@ -552,9 +548,9 @@ __global__ void add_source_kernel(T *u, int64_t idx, T value) {
 // Fill StarArgs from a descriptor: weights combined in fp64, scaled by
 // wscale (1, or dt^2/h^2 for the wave step) and rounded once to T.
 template <typename T, int R>
-StarArgs<T> make_args(const stencil3d_desc &d, const void *in, void *out, const void *u_prev,
-                      const void *vel2, const void *eta, double wscale, int tiles_x,
-                      int tiles_y, int chunk_len, int nwg) {
+StarArgs<T> make_args(const stencil3d_desc &d, const Box &b, const void *in, void *out,
+                      const void *u_prev, const void *vel2, const void *eta, double wscale,
+                      int tiles_x, int tiles_y, int chunk_len, int nwg) {
     StarArgs<T> a;
     a.in = static_cast<const T *>(in);
     a.out = static_cast<T *>(out);
@@ -569,7 +565,12 @@ StarArgs<T> make_args(const stencil3d_desc &d, const void *in, void *out, const 
     a.tiles_y = tiles_y;
     a.chunk_len = chunk_len;
     a.nwg = nwg;
-    a.pml = d.pml_width > 0x3fffffff ? 0x3fffffff : (int32_t)d.pml_width;
+    a.bx0 = (int32_t)b.x0;
+    a.bx1 = (int32_t)b.x1;
+    a.by0 = (int32_t)b.y0;
+    a.by1 = (int32_t)b.y1;
+    a.bz0 = (int32_t)b.z0;
+    a.bz1 = (int32_t)b.z1;
     const double cc = d.cx[0] + d.cy[0] + d.cz[0];
     double ksum = 0.0;
     for (int k = 1; k <= R; ++k) ksum += d.cx[k] + d.cy[k] + d.cz[k];

@@ -75,8 +75,8 @@ template <typename T, int NS>
 int launch_ns(const stencil3d_desc &d, const void *in, void *out, int cus, hipStream_t s) {
     using C = typename FusedShipped<T, NS>::Cfg;
     const FusedPlan p = plan_fused<T, NS>(d, cus);
-    const StarArgs<T> a = make_args<T, 1>(d, in, out, nullptr, nullptr, nullptr, 1.0, p.tiles_x,
-                                          p.tiles_y, p.chunk_len, p.nwg);
+    const StarArgs<T> a = make_args<T, 1>(d, interior_box(d), in, out, nullptr, nullptr, nullptr,
+                                          1.0, p.tiles_x, p.tiles_y, p.chunk_len, p.nwg);
     hipLaunchKernelGGL((sweeps_fused_kernel<T, 1, NS, C>), dim3(p.nwg), dim3(p.threads), 0, s, a);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }

@@ -281,11 +281,16 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
 #pragma unroll
                         for (int j = 0; j < VY; ++j) bstore<T, VX, SAUX>(ro, soff[j], res[j]);
                     } else {
+                        // whole groups in one access, the partial group of a
+                        // row element by element (as in star2p5d_kernel)
 #pragma unroll
-                        for (int j = 0; j < VY; ++j)
+                        for (int j = 0; j < VY; ++j) {
+                            bstore<T, VX, SAUX>(ro, nvx == VX ? soff[j] : kOOB, res[j]);
 #pragma unroll
-                            for (int i = 0; i < VX; ++i)
-                                bstore1<T>(ro, i < nvx ? soff[j] + i * ES : kOOB, res[j][i]);
+                            for (int i = 0; i < VX - 1; ++i)
+                                bstore1<T>(ro, i < nvx && nvx < VX ? soff[j] + i * ES : kOOB,
+                                           res[j][i]);
+                        }
                     }
                 }
             });

@@ -182,8 +182,8 @@ def bench_wave(torch, B, wl, args):
     u_prev = torch.zeros_like(vel2)
     u = torch.zeros_like(vel2)
     d = B.desc_init("f32", shp, w.radius)
-    # eta is read everywhere: the data-region split (pml_width) reads less
-    # but measured slower on MI355X
+    # pml_width stays 0: one launch reading eta everywhere is faster on this
+    # grid than the data-region launches (thin x slabs of the sponge)
     src = wl.source_point(w)
     trace = wl.source_trace(w)
     fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
@@ -208,7 +208,9 @@ def bench_wave(torch, B, wl, args):
                               frac=round(achieved / PEAK_HBM_GBS, 4),
                               algorithmic_bytes_per_step=nbytes,
                               note="per-step mean incl. the 1-thread source "
-                                   "kernel"))
+                                   "kernel; bytes in the one-read-one-write "
+                                   "convention for all five fields (20.09 "
+                                   "B/point)"))
 
 
 def cpu_wave_slab(wl, w, budget_s, planes=64):

@@ -526,3 +526,42 @@ def test_wave_pml_regions(oracle_mod, torch_dev):
                                  vel2.cpu().numpy(), eta.cpu().numpy(), R, c,
                                  e["dt"], e["h"], 3)
     check_close(interior(runs[0], R), interior(ref, R), 1e-4, "3 free steps")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_wave_data_regions_ragged(oracle_mod, torch_dev, dtype):
+    """The data-region launch (an eta-free inner box plus six slabs that
+    read eta, for R = 4) on a ragged non-cubic grid with a 12-point sponge,
+    through wave_run: pml_width 12 (exact) and 30 (conservative) split the
+    interior and give the same bits as 0; 40 cannot split (the inner box
+    would be empty in y) and is the single launch; 1 is a false claim and
+    must change the result.  Also checked against the oracle."""
+    import dataclasses
+    torch, _ = torch_dev
+    dt = "f32" if dtype == np.float32 else "f64"
+    base = wl.WAVE_128_RANDOM
+    w = dataclasses.replace(base, shape=(82, 75, 141), dtype=dt,
+                            extra=dict(base.extra, sponge=12))
+    e = w.extra
+    R = w.radius
+    u_prev, u, vel2, eta = _wave_fields(w, torch)
+    runs = {}
+    for pml in (0, 12, 30, 40, 1):
+        log("case data regions %s pml_width=%d" % (dt, pml))
+        d = B.desc_init(dt, w.shape, R)
+        d.pml_width = pml
+        a, b = u_prev.clone(), u.clone()
+        older, newest = B.wave_run(d, a, b, vel2, eta, e["dt"], e["h"], 3)
+        runs[pml] = newest.cpu().numpy()
+    for pml in (12, 30, 40):
+        assert np.array_equal(runs[pml].view(np.uint8),
+                              runs[0].view(np.uint8)), pml
+    assert not np.array_equal(runs[1], runs[0])
+    c = oracle_mod.laplacian_weights(R)
+    _, ref = oracle_mod.wave_run(u_prev.cpu().numpy(), u.cpu().numpy(),
+                                 vel2.cpu().numpy(), eta.cpu().numpy(), R, c,
+                                 e["dt"], e["h"], 3)
+    tol = 1e-4 if dtype == np.float32 else 1e-11
+    check_close(interior(runs[12], R), interior(ref, R), tol,
+                "3 free steps, data regions")
+
