@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-variable",
+    "-Wall", "-Wno-unused-variable", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

@@ -124,11 +124,15 @@ int wave_checks(const stencil3d_desc *d, double dt, double h) {
 
 }  // namespace
 
+// The library is built with hidden symbols; only the functions of
+// stencil3d.h are exported.
+#define ST_EXPORT __attribute__((visibility("default")))
+
 extern "C" {
 
-int stencil3d_abi_version(void) { return ST_ABI_VERSION; }
+ST_EXPORT int stencil3d_abi_version(void) { return ST_ABI_VERSION; }
 
-const char *stencil3d_strerror(int code) {
+ST_EXPORT const char *stencil3d_strerror(int code) {
     switch (code) {
     case ST_OK: return "ok";
     case ST_ERR_NULL: return "required pointer is NULL";
@@ -148,7 +152,7 @@ const char *stencil3d_strerror(int code) {
     return "unknown status code";
 }
 
-int stencil3d_desc_validate(const stencil3d_desc *d) {
+ST_EXPORT int stencil3d_desc_validate(const stencil3d_desc *d) {
     if (!d) return ST_ERR_NULL;
     if (d->struct_size != sizeof(stencil3d_desc)) return ST_ERR_STRUCT_SIZE;
     if (d->dtype != ST_F32 && d->dtype != ST_F64) return ST_ERR_DTYPE;
@@ -167,7 +171,7 @@ int stencil3d_desc_validate(const stencil3d_desc *d) {
     return ST_OK;
 }
 
-int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx, int64_t ny, int64_t nz,
+ST_EXPORT int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx, int64_t ny, int64_t nz,
                         int radius, int boundary) {
     if (!d) return ST_ERR_NULL;
     memset(d, 0, sizeof(*d));
@@ -184,7 +188,7 @@ int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx, int64_t ny, in
     return stencil3d_desc_validate(d);
 }
 
-int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out, void *stream) {
+ST_EXPORT int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out, void *stream) {
     int st = stencil3d_desc_validate(d);
     if (st) return st;
     if ((st = check_ptr(d, in)) || (st = check_ptr(d, out))) return st;
@@ -200,7 +204,7 @@ int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out, void *st
     return st;
 }
 
-int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, int sweeps,
+ST_EXPORT int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, int sweeps,
                      void *stream) {
     int st = stencil3d_desc_validate(d);
     if (st) return st;
@@ -252,7 +256,7 @@ static int wave_validate(const stencil3d_desc *d, const void *u_prev, const void
     return ST_OK;
 }
 
-int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
+ST_EXPORT int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
               const void *vel2, const void *eta, double dt, double h, void *stream) {
     int st = wave_validate(d, u_prev, u, u_next, vel2, eta, dt, h);
     if (st) return st;
@@ -262,7 +266,7 @@ int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *
                        static_cast<hipStream_t>(stream));
 }
 
-int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, int64_t iz,
+ST_EXPORT int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, int64_t iz,
                     double value, void *stream) {
     int st = stencil3d_desc_validate(d);
     if (st) return st;
@@ -273,7 +277,7 @@ int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, in
     return st::launch_add_source(*d, u, idx, value, static_cast<hipStream_t>(stream));
 }
 
-int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2, const void *eta,
+ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2, const void *eta,
              double dt, double h, int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
              const double *src_trace, void *stream) {
     int st = wave_validate(d, u_prev, u, u_prev, vel2, eta, dt, h);

@@ -46,6 +46,23 @@ def test_exports_every_declared_function(L):
                for n in B.EXPORTS)
 
 
+def test_exports_nothing_else(L):
+    """The library exports exactly the header's functions, besides the
+    symbols the HIP runtime itself needs (kernel entry stubs and module ids);
+    internal C++ helpers stay hidden."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("no nm")
+    out = subprocess.run([nm, "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    runtime = {n for n in names if n.startswith("__hip_") or
+               re.match(r"_ZN2st\d+\w*_kernelI", n)}
+    assert names - runtime == set(B.EXPORTS), sorted(names - runtime)
+
+
 def test_struct_layout_and_version(L):
     assert ctypes.sizeof(B.Desc) == 168
     assert B.abi_version() == 2
