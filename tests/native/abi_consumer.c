@@ -1,0 +1,86 @@
+/*
+ * A plain C99 consumer of libstencil3d.so: no Python, no torch.  Device
+ * memory comes from the HIP runtime's C API.
+ *
+ *   abi_consumer cpu            argument validation only (no device needed)
+ *   abi_consumer gpu OUT.bin    one R = 2 fp32 apply on a 19x23x41 grid;
+ *                               writes the input and output arrays to OUT.bin
+ *                               (raw float32, input first) for comparison
+ *                               with the oracle
+ */
+#define __HIP_PLATFORM_AMD__ 1
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "stencil3d.h"
+
+#define EXPECT(cond)                                                         \
+    do {                                                                     \
+        if (!(cond)) {                                                       \
+            fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);  \
+            return 1;                                                        \
+        }                                                                    \
+    } while (0)
+
+static int cpu_checks(void) {
+    stencil3d_desc d;
+    EXPECT(stencil3d_abi_version() == ST_ABI_VERSION);
+    EXPECT(strcmp(stencil3d_strerror(ST_OK), "ok") == 0);
+    EXPECT(stencil3d_desc_init(&d, ST_F32, 41, 23, 19, 2, ST_BC_HALO_UNTOUCHED) == ST_OK);
+    EXPECT(d.struct_size == sizeof(stencil3d_desc) && d.nx == 41 && d.nz == 19);
+    EXPECT(stencil3d_desc_validate(&d) == ST_OK);
+    d.radius = 7;
+    EXPECT(stencil3d_desc_validate(&d) == ST_ERR_RADIUS);
+    d.radius = 2;
+    /* every entry point rejects before touching a device */
+    EXPECT(stencil3d_apply(&d, NULL, NULL, NULL) == ST_ERR_NULL);
+    EXPECT(stencil3d_apply(NULL, NULL, NULL, NULL) == ST_ERR_NULL);
+    EXPECT(stencil3d_jacobi(&d, (void *)64, (void *)64, 1, NULL) == ST_ERR_ALIAS);
+    EXPECT(wave_step(&d, (void *)64, (void *)1000000, (void *)2000000,
+                     (void *)3000000, (void *)4000000, 1e-3, 0.0, NULL) == ST_ERR_ARG);
+    EXPECT(wave_add_source(&d, (void *)64, 0, 5, 5, 1.0, NULL) == ST_ERR_BAD_INDEX);
+    printf("cpu checks ok\n");
+    return 0;
+}
+
+static int gpu_run(const char *path) {
+    const int64_t nx = 41, ny = 23, nz = 19;
+    const size_t n = (size_t)(nx * ny * nz), bytes = n * sizeof(float);
+    float *h_in = (float *)malloc(bytes), *h_out = (float *)malloc(bytes);
+    void *d_in = NULL, *d_out = NULL;
+    stencil3d_desc d;
+    uint32_t s = 12345u;
+    EXPECT(h_in && h_out);
+    for (size_t i = 0; i < n; ++i) { /* an LCG in [-1, 1) */
+        s = s * 1664525u + 1013904223u;
+        h_in[i] = (float)((double)(s >> 8) / 8388608.0 - 1.0);
+    }
+    EXPECT(hipMalloc(&d_in, bytes) == hipSuccess);
+    EXPECT(hipMalloc(&d_out, bytes) == hipSuccess);
+    EXPECT(hipMemcpy(d_in, h_in, bytes, hipMemcpyHostToDevice) == hipSuccess);
+    EXPECT(hipMemset(d_out, 0, bytes) == hipSuccess);
+    EXPECT(stencil3d_desc_init(&d, ST_F32, nx, ny, nz, 2, ST_BC_HALO_UNTOUCHED) == ST_OK);
+    EXPECT(stencil3d_apply(&d, d_in, d_out, NULL) == ST_OK);
+    EXPECT(hipDeviceSynchronize() == hipSuccess);
+    EXPECT(hipMemcpy(h_out, d_out, bytes, hipMemcpyDeviceToHost) == hipSuccess);
+    FILE *f = fopen(path, "wb");
+    EXPECT(f != NULL);
+    EXPECT(fwrite(h_in, 1, bytes, f) == bytes && fwrite(h_out, 1, bytes, f) == bytes);
+    fclose(f);
+    hipFree(d_in);
+    hipFree(d_out);
+    free(h_in);
+    free(h_out);
+    printf("gpu apply ok\n");
+    return 0;
+}
+
+int main(int argc, char **argv) {
+    if (argc >= 2 && strcmp(argv[1], "cpu") == 0) return cpu_checks();
+    if (argc >= 3 && strcmp(argv[1], "gpu") == 0) return gpu_run(argv[2]);
+    fprintf(stderr, "usage: %s cpu | gpu OUT.bin\n", argv[0]);
+    return 2;
+}
