@@ -193,7 +193,11 @@ Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int c
     // kernel runs whole blocks).
     const int R = d.radius;
     const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * (g.threads >= 512 ? 1 : 512 / g.threads);
-    const int64_t maxch = bz / (4 * R) > 0 ? bz / (4 * R) : 1;
+    // more chunks than fill a few rounds of workgroups never pay; the cap
+    // keeps the search short for very tall grids
+    int64_t maxch = bz / (4 * R) > 0 ? bz / (4 * R) : 1;
+    const int64_t enough = 8 * cap / (tiles > 0 ? tiles : 1) + 1;
+    if (maxch > enough) maxch = enough;
     int64_t best_len = 0, best_nch = 1, best_cost = -1;
     for (int64_t nch = 1; nch <= maxch; ++nch) {
         int64_t len = (bz + nch - 1) / nch;

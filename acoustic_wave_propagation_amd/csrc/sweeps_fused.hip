@@ -52,7 +52,9 @@ FusedPlan plan_fused(const stencil3d_desc &d, int cus) {
     // one workgroup per compute unit (LDS and registers); minimise
     // rounds * (chunk + pipeline fill), as for the single-sweep kernel
     const int64_t cap = cus > 0 ? cus : 256;
-    const int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
+    int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
+    const int64_t enough = 8 * cap / (tiles > 0 ? tiles : 1) + 1;  // see plan_geometry
+    if (maxch > enough) maxch = enough;
     int64_t best_len = iz, best_n = 1, best_cost = -1;
     for (int64_t nch = 1; nch <= maxch; ++nch) {
         int64_t len = (iz + nch - 1) / nch;
