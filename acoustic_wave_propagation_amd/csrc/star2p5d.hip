@@ -228,18 +228,24 @@ int launch_star(const stencil3d_desc &d, const Box &box, Kind kind, const void *
 }
 
 int launch_shell_copy(const stencil3d_desc &d, const void *in, void *out, hipStream_t stream) {
-    const int64_t rows = d.ny * d.nz;
-    int64_t blocks = (rows + 3) / 4;
-    if (blocks > 8192) blocks = 8192;
+    const int64_t R = d.radius;
+    const int64_t full_rows = 2 * R * d.ny + (d.nz - 2 * R) * 2 * R;
+    int64_t full_blocks = (full_rows + 3) / 4;  // 4 waves per block, one row each
+    if (full_blocks > 4096) full_blocks = 4096;
+    const int64_t ends = (d.ny - 2 * R) * (d.nz - 2 * R);  // one thread per interior row
+    int64_t end_blocks = (ends + 255) / 256;
+    if (end_blocks > 65536) end_blocks = 65536;
+    if (end_blocks < 1) end_blocks = 1;
+    const int64_t blocks = full_blocks + end_blocks;
     const dim3 grid((unsigned)blocks), block(256);
     if (d.dtype == ST_F64)
         hipLaunchKernelGGL(shell_copy_kernel<double>, grid, block, 0, stream,
                            static_cast<const double *>(in), static_cast<double *>(out),
-                           (int)d.nx, (int)d.ny, (int)d.nz, d.radius);
+                           (int)d.nx, (int)d.ny, (int)d.nz, d.radius, (int)full_blocks);
     else
         hipLaunchKernelGGL(shell_copy_kernel<float>, grid, block, 0, stream,
                            static_cast<const float *>(in), static_cast<float *>(out),
-                           (int)d.nx, (int)d.ny, (int)d.nz, d.radius);
+                           (int)d.nx, (int)d.ny, (int)d.nz, d.radius, (int)full_blocks);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }
 

@@ -519,23 +519,47 @@ star2p5d_kernel(StarArgs<T> a) {
 }
 
 // out = in on every non-interior point; one wave per (y, z) row.
+// out = in on every non-interior point.  The non-interior points are the
+// whole rows (y, z) with z or y in the R-wide shell -- 2R ny rows in the
+// shell planes plus 2R (nz - 2R) rows of the other planes -- and the R
+// points at each end of every other row.  Blocks [0, full_blocks) copy the
+// whole rows, one wave per row; the remaining blocks copy the row ends, one
+// thread per interior row (both parts grid-stride).
 template <typename T>
 __global__ void __launch_bounds__(256)
     shell_copy_kernel(const T *__restrict__ in, T *__restrict__ out, int nx, int ny, int nz,
-                      int R) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    const int64_t rows = (int64_t)ny * nz;
-    for (int64_t row = wave; row < rows; row += nwaves) {
-        const int z = (int)(row / ny), y = (int)(row - (int64_t)z * ny);
-        const T *s = in + row * nx;
-        T *d = out + row * nx;
-        if (z < R || z >= nz - R || y < R || y >= ny - R) {
-            for (int x = lane; x < nx; x += 64) d[x] = s[x];
-        } else if (lane < 2 * R) {
-            const int x = lane < R ? lane : nx - 2 * R + lane;
-            d[x] = s[x];
+                      int R, int full_blocks) {
+    const int64_t iy = ny - 2 * R, iz = nz - 2 * R;
+    if ((int)blockIdx.x < full_blocks) {
+        const int lane = threadIdx.x & 63;
+        const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+        const int64_t nwaves = ((int64_t)full_blocks * blockDim.x) >> 6;
+        const int64_t zrows = 2 * (int64_t)R * ny;   // rows of the 2R shell planes
+        const int64_t rows = zrows + iz * 2 * R;     // plus y-shell rows of the others
+        for (int64_t r = wave; r < rows; r += nwaves) {
+            int64_t z, y;
+            if (r < zrows) {
+                const int64_t p = r / ny;
+                z = p < R ? p : nz - 2 * R + p;
+                y = r - p * ny;
+            } else {
+                const int64_t q = r - zrows, p = q / (2 * R), k = q - p * (2 * R);
+                z = R + p;
+                y = k < R ? k : ny - 2 * R + k;
+            }
+            const int64_t base = (z * ny + y) * nx;
+            for (int x = lane; x < nx; x += 64) out[base + x] = in[base + x];
+        }
+    } else {
+        const int64_t stride = ((int64_t)gridDim.x - full_blocks) * blockDim.x;
+        for (int64_t t = ((int64_t)blockIdx.x - full_blocks) * blockDim.x + threadIdx.x;
+             t < iy * iz; t += stride) {
+            const int64_t z = R + t / iy, y = R + t % iy;
+            const int64_t base = (z * ny + y) * nx;
+            for (int k = 0; k < R; ++k) {
+                out[base + k] = in[base + k];
+                out[base + nx - 1 - k] = in[base + nx - 1 - k];
+            }
         }
     }
 }
