@@ -66,6 +66,8 @@ def _load():
         lib.oracle_wave_step.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32,
                                          vp, i64, i64, i64, i32, vp, vp, vp,
                                          dp, dp]
+        lib.oracle_wave_step_pml.restype = None
+        lib.oracle_wave_step_pml.argtypes = lib.oracle_wave_step.argtypes
         _lib = lib
     return _lib
 
@@ -169,6 +171,11 @@ def wave_step(u_prev, u, vel2, eta, R, c, dt, h, out=None):
     ``u_next = (2u - (1-eta) u_prev + vel2 dt^2 star(u)/h^2) / (1+eta)``.
     Non-interior points of ``out`` are left as given (zeros by default).
     """
+    return _wave(_load().oracle_wave_step, u_prev, u, vel2, eta, R, c, dt, h,
+                 out)
+
+
+def _wave(fn, u_prev, u, vel2, eta, R, c, dt, h, out):
     arrs = [np.ascontiguousarray(a) for a in (u_prev, u, vel2, eta)]
     shape = arrs[1].shape
     if any(a.shape != shape for a in arrs) or len(shape) != 3:
@@ -177,16 +184,31 @@ def wave_step(u_prev, u, vel2, eta, R, c, dt, h, out=None):
     c = _coef(c, R)
     if out is None:
         out = np.zeros(shape, dtype=np.float64)
+    if out.dtype != np.float64 or not out.flags.c_contiguous or \
+            out.shape != shape:
+        raise ValueError("out must be a C-contiguous float64 array of the "
+                         "fields' shape")
     up, uu, v2, et = arrs
-    _load().oracle_wave_step(_ptr(up), _f64flag(up), _ptr(uu), _f64flag(uu),
-                             _ptr(v2), _f64flag(v2), _ptr(et), _f64flag(et),
-                             _ptr(out), nx, ny, nz, R, _ptr(c), _ptr(c),
-                             _ptr(c), float(dt), float(h))
+    fn(_ptr(up), _f64flag(up), _ptr(uu), _f64flag(uu), _ptr(v2), _f64flag(v2),
+       _ptr(et), _f64flag(et), _ptr(out), nx, ny, nz, R, _ptr(c), _ptr(c),
+       _ptr(c), float(dt), float(h))
     return out
 
 
+def wave_step_pml(u_prev, u, vel2, eta, R, c, dt, h, out=None):
+    """One wave step of the PML kernel on the interior; returns fp64 ``u_next``.
+
+    ``u_next = (2u - (1-eta) u_prev + vel2 dt^2 (star(u) + G)/h^2) / (1+eta)``
+    with ``G = sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) - u(p-e_a)) / 4``,
+    the eta-gradient coupling (7-point stencil on eta, halo 1).  Non-interior
+    points of ``out`` are left as given (zeros by default).
+    """
+    return _wave(_load().oracle_wave_step_pml, u_prev, u, vel2, eta, R, c,
+                 dt, h, out)
+
+
 def wave_run(u_prev, u, vel2, eta, R, c, dt, h, nsteps, src=None,
-             src_trace=None, callback=None):
+             src_trace=None, callback=None, pml=False):
     """Leapfrog time loop: ``nsteps`` wave steps with a point source.
 
     After step n's update, ``src_trace[n]`` is added to ``u_next`` at the
@@ -194,13 +216,15 @@ def wave_run(u_prev, u, vel2, eta, R, c, dt, h, nsteps, src=None,
     rotates (u_prev, u) <- (u, u_next).  Each new state starts as a copy of
     the old ``u_prev`` (the two-buffer leapfrog: only the interior is
     rewritten, the halo carries over).  ``callback(n, u_prev, u)`` sees the
-    state after each step.  Returns the final (u_prev, u), fp64.
+    state after each step.  ``pml=True`` takes the PML kernel's step
+    (``wave_step_pml``).  Returns the final (u_prev, u), fp64.
     """
+    step = wave_step_pml if pml else wave_step
     up = np.array(u_prev, dtype=np.float64)
     uc = np.array(u, dtype=np.float64)
     for n in range(nsteps):
         un = np.array(up)
-        wave_step(up, uc, vel2, eta, R, c, dt, h, out=un)
+        step(up, uc, vel2, eta, R, c, dt, h, out=un)
         if src is not None:
             ix, iy, iz = src
             un[iz, iy, ix] += float(src_trace[n])

@@ -147,3 +147,75 @@ void oracle_wave_step(const void *u_prev, int up_f64, const void *u,
         }
     }
 }
+
+/*
+ * The eta-gradient coupling at one interior point, without the 1/h^2:
+ *
+ *   G = sum over the axes a of (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) - u(p-e_a)) / 4
+ *
+ * i.e. grad(eta) . grad(u) with both gradients by second-order central
+ * differences.  "Accelerating High-Order Stencils on GPUs" (smem_eta
+ * description) states that the PML kernel reads eta through a low-order
+ * 7-point stencil, halo 1, next to the 25-point stencil on u, but prints no
+ * formula; this term -- the six face neighbours of eta paired with the
+ * same six neighbours of u, which with the centre value that the damping
+ * reads makes the 7-point stencil -- is the reading recorded in the design
+ * notes.
+ */
+static long double eta_coupling_at(const void *u, int u_f64, const void *eta,
+                                   int e_f64, int64_t nx, int64_t ny,
+                                   int64_t x, int64_t y, int64_t z)
+{
+    const int64_t c = x + nx * (y + ny * z);
+    const int64_t stride[3] = {1, nx, nx * ny};
+    long double acc = 0.0L;
+    for (int a = 0; a < 3; ++a) {
+        const int64_t s = stride[a];
+        const long double deta = rd(eta, e_f64, c + s) - rd(eta, e_f64, c - s);
+        const long double du = rd(u, u_f64, c + s) - rd(u, u_f64, c - s);
+        acc += deta * du;
+    }
+    return acc / 4.0L;
+}
+
+/*
+ * One wave step of the PML kernel: the update of oracle_wave_step with the
+ * eta-gradient coupling added to the Laplacian term,
+ *
+ *   L      = star(u) / h^2
+ *   G      = eta_coupling(u, eta) / h^2
+ *   u_next = (2 u - (1 - eta) u_prev + vel2 dt^2 (L + G)) / (1 + eta)
+ *
+ * on every interior point (non-interior points of u_next are not written).
+ * Where eta is constant over a point's six face neighbours, G = 0 and the
+ * step is that of oracle_wave_step.
+ */
+void oracle_wave_step_pml(const void *u_prev, int up_f64, const void *u,
+                          int u_f64, const void *vel2, int v_f64,
+                          const void *eta, int e_f64, double *u_next,
+                          int64_t nx, int64_t ny, int64_t nz, int R,
+                          const double *cx, const double *cy,
+                          const double *cz, double dt, double h)
+{
+    const long double dt2 = (long double)dt * (long double)dt;
+    const long double h2 = (long double)h * (long double)h;
+    int64_t z;
+#pragma omp parallel for schedule(static)
+    for (z = R; z < nz - R; ++z) {
+        for (int64_t y = R; y < ny - R; ++y) {
+            for (int64_t x = R; x < nx - R; ++x) {
+                const int64_t i = x + nx * (y + ny * z);
+                const long double L =
+                    star_at(u, u_f64, nx, ny, x, y, z, R, cx, cy, cz) / h2;
+                const long double G =
+                    eta_coupling_at(u, u_f64, eta, e_f64, nx, ny, x, y, z) / h2;
+                const long double e = rd(eta, e_f64, i);
+                const long double un = rd(u, u_f64, i);
+                const long double up = rd(u_prev, up_f64, i);
+                const long double v2 = rd(vel2, v_f64, i);
+                u_next[i] = (double)((2.0L * un - (1.0L - e) * up +
+                                      v2 * dt2 * (L + G)) / (1.0L + e));
+            }
+        }
+    }
+}

@@ -142,3 +142,112 @@ def test_wave_workload_is_stable():
     courant = e["vmax"] * e["dt"] / e["h"]
     assert courant ** 2 * float(lam_max) <= 4.0
     assert courant ** 2 * float(lam_max) > 3.9
+
+
+# ---- the PML kernel's step: eta-gradient coupling --------------------------
+# u_next = (2u - (1-eta) u_prev + vel2 dt^2 (star(u) + G)/h^2) / (1+eta),
+# G = sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) - u(p-e_a)) / 4.
+
+def _cubic(rng, scale):
+    """Random polynomial of total degree <= 3 as {(i, j, k): coef} for the
+    monomial x^i y^j z^k."""
+    return {(i, j, k): scale * rng.uniform(-1, 1)
+            for i in range(4) for j in range(4) for k in range(4)
+            if i + j + k <= 3}
+
+
+def _poly_eval(p, X, Y, Z, d=(0, 0, 0)):
+    """Value of the partial derivative d/dx^d0 d/dy^d1 d/dz^d2 of p."""
+    def fall(n, m):  # n (n-1) ... (n-m+1)
+        r = 1
+        for t in range(m):
+            r *= n - t
+        return r
+    out = np.zeros(X.shape)
+    for (i, j, k), c in p.items():
+        if i < d[0] or j < d[1] or k < d[2]:
+            continue
+        f = c * fall(i, d[0]) * fall(j, d[1]) * fall(k, d[2])
+        out += f * X ** (i - d[0]) * Y ** (j - d[1]) * Z ** (k - d[2])
+    return out
+
+
+def test_pml_constant_eta_is_the_pointwise_step(oracle_mod):
+    """Where eta is the same on a point's six face neighbours the coupling
+    vanishes exactly, so with a constant eta field the PML step is the
+    pinned pointwise step, bit for bit."""
+    shape = (13, 12, 14)
+    g = np.random.default_rng(11)
+    up, u = g.uniform(-1, 1, shape), g.uniform(-1, 1, shape)
+    vel2, _ = _fields(shape, 12)
+    eta = np.full(shape, 0.0625)
+    for R in (1, 4):
+        w = oracle_mod.laplacian_weights(R)
+        a = oracle_mod.wave_step(up, u, vel2, eta, R, w, 1e-3, 10.0)
+        b = oracle_mod.wave_step_pml(up, u, vel2, eta, R, w, 1e-3, 10.0)
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_pml_cubic_fields_closed_form(oracle_mod, R):
+    """u and eta cubic polynomials in centred grid coordinates.  The order-2R
+    rule is exact on cubics, so star(u) = lap(u); a central difference over
+    +-1 of a cubic is exact up to its third derivative: (f(p+e) - f(p-e))/2
+    = f' + f'''/6.  Hence G = sum_a (eta'_a + eta'''_a/6)(u'_a + u'''_a/6).
+    A dropped term, a wrong sign, a factor 1/2 for 1/4, a difference over
+    +-2 (weight 4/6 on the third derivative) or crossed axes each move the
+    result far past the bound."""
+    shape = (2 * R + 9, 2 * R + 8, 2 * R + 10)
+    nz, ny, nx = shape
+    g = np.random.default_rng(40 + R)
+    Z, Y, X = np.meshgrid(np.arange(nz) - (nz - 1) / 2,
+                          np.arange(ny) - (ny - 1) / 2,
+                          np.arange(nx) - (nx - 1) / 2, indexing="ij")
+    pu = _cubic(g, 1.0)
+    pe = _cubic(g, 0.004)
+    pe[(0, 0, 0)] = 0.05
+    u = _poly_eval(pu, X, Y, Z)
+    eta = _poly_eval(pe, X, Y, Z)
+    up = g.uniform(-1, 1, shape)
+    vel2, _ = _fields(shape, 41)
+    dt, h = 1e-3, 10.0
+    lap = sum(_poly_eval(pu, X, Y, Z, d) for d in ((2, 0, 0), (0, 2, 0),
+                                                   (0, 0, 2)))
+    G = 0.0
+    for a in range(3):
+        d1 = tuple(1 if b == a else 0 for b in range(3))
+        d3 = tuple(3 if b == a else 0 for b in range(3))
+        G = G + (_poly_eval(pe, X, Y, Z, d1) + _poly_eval(pe, X, Y, Z, d3) / 6) \
+            * (_poly_eval(pu, X, Y, Z, d1) + _poly_eval(pu, X, Y, Z, d3) / 6)
+    want = (2 * u - (1 - eta) * up + vel2 * dt * dt * (lap + G) / (h * h)) / \
+        (1 + eta)
+    w = oracle_mod.laplacian_weights(R)
+    got = oracle_mod.wave_step_pml(up, u, vel2, eta, R, w, dt, h)
+    I = (slice(R, -R),) * 3
+    scale = np.abs(u[I]).max() + np.abs(up[I]).max()
+    err = np.abs(got[I] - want[I]).max()
+    assert err <= 1e-11 * scale, err
+    # the coupling is well above that bound: its share of the update
+    gshare = np.abs((vel2 * dt * dt * G / (h * h) / (1 + eta))[I]).max()
+    assert gshare > 1e-5 * scale
+    # and the pointwise step misses it by about that share
+    plain = oracle_mod.wave_step(up, u, vel2, eta, R, w, dt, h)
+    assert np.abs(plain[I] - want[I]).max() > 0.5 * gshare
+
+
+def test_pml_run_matches_steps(oracle_mod):
+    """wave_run(pml=True) is the PML step in the leapfrog loop."""
+    R = 4
+    shape = (2 * R + 6,) * 3
+    g = np.random.default_rng(5)
+    up, u = g.uniform(-1, 1, shape), g.uniform(-1, 1, shape)
+    vel2, eta = _fields(shape, 6)
+    w = oracle_mod.laplacian_weights(R)
+    a, b = np.array(up), np.array(u)
+    for _ in range(3):
+        n = np.array(a)
+        oracle_mod.wave_step_pml(a, b, vel2, eta, R, w, 1e-3, 10.0, out=n)
+        a, b = b, n
+    rp, ru = oracle_mod.wave_run(up, u, vel2, eta, R, w, 1e-3, 10.0, 3,
+                                 pml=True)
+    assert np.array_equal(rp, a) and np.array_equal(ru, b)
