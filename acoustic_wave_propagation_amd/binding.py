@@ -21,7 +21,8 @@ HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
 # every entry point declared in include/stencil3d.h
 EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
            "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
-           "wave_step", "wave_add_source", "wave_run")
+           "wave_step", "wave_step_pml", "wave_add_source", "wave_run",
+           "wave_run_pml")
 
 
 class Desc(ctypes.Structure):
@@ -69,9 +70,12 @@ def lib():
             "stencil3d_apply": (i32, [D, vp, vp, vp]),
             "stencil3d_jacobi": (i32, [D, vp, vp, i32, vp]),
             "wave_step": (i32, [D, vp, vp, vp, vp, vp, dp, dp, vp]),
+            "wave_step_pml": (i32, [D, vp, vp, vp, vp, vp, dp, dp, vp]),
             "wave_add_source": (i32, [D, vp, i64, i64, i64, dp, vp]),
             "wave_run": (i32, [D, vp, vp, vp, vp, dp, dp, i32, i64, i64, i64,
                                ctypes.POINTER(ctypes.c_double), vp]),
+            "wave_run_pml": (i32, [D, vp, vp, vp, vp, dp, dp, i32, i64, i64,
+                                   i64, ctypes.POINTER(ctypes.c_double), vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -159,14 +163,24 @@ def stencil3d_jacobi(d: Desc, buf0, buf1, sweeps: int, stream=None):
     return buf0 if sweeps % 2 == 0 else buf1
 
 
+def _step(name, d: Desc, u_prev, u, u_next, vel2, eta, dt, h, stream):
+    _check(getattr(lib(), name)(
+        ctypes.byref(d), _ptr(u_prev, d, "u_prev"), _ptr(u, d, "u"),
+        _ptr(u_next, d, "u_next"), _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"),
+        float(dt), float(h), _stream(u, stream)), name)
+    return u_next
+
+
 def wave_step(d: Desc, u_prev, u, u_next, vel2, eta, dt: float, h: float,
               stream=None):
-    _check(lib().wave_step(ctypes.byref(d), _ptr(u_prev, d, "u_prev"),
-                           _ptr(u, d, "u"), _ptr(u_next, d, "u_next"),
-                           _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"),
-                           float(dt), float(h), _stream(u, stream)),
-           "wave_step")
-    return u_next
+    return _step("wave_step", d, u_prev, u, u_next, vel2, eta, dt, h, stream)
+
+
+def wave_step_pml(d: Desc, u_prev, u, u_next, vel2, eta, dt: float, h: float,
+                  stream=None):
+    """The PML kernel's step (eta-gradient coupling added)."""
+    return _step("wave_step_pml", d, u_prev, u, u_next, vel2, eta, dt, h,
+                 stream)
 
 
 def wave_add_source(d: Desc, u, ix: int, iy: int, iz: int, value: float,
@@ -178,8 +192,9 @@ def wave_add_source(d: Desc, u, ix: int, iy: int, iz: int, value: float,
 
 
 def wave_run(d: Desc, u_prev, u, vel2, eta, dt: float, h: float, nsteps: int,
-             src=(0, 0, 0), src_trace=None, stream=None):
-    """Two-buffer leapfrog; returns (older, newest) tensors."""
+             src=(0, 0, 0), src_trace=None, stream=None, pml: bool = False):
+    """Two-buffer leapfrog; returns (older, newest) tensors.  ``pml``
+    calls ``wave_run_pml`` (the PML kernel's step)."""
     n = int(nsteps)
     tr = None
     if src_trace is not None:
@@ -188,8 +203,16 @@ def wave_run(d: Desc, u_prev, u, vel2, eta, dt: float, h: float, nsteps: int,
             raise ValueError("src_trace needs %d values" % n)
         tr = (ctypes.c_double * max(n, 1))(*vals[:max(n, 1)])
     ix, iy, iz = src
-    _check(lib().wave_run(ctypes.byref(d), _ptr(u_prev, d, "u_prev"),
-                          _ptr(u, d, "u"), _ptr(vel2, d, "vel2"),
-                          _ptr(eta, d, "eta"), float(dt), float(h), n, ix, iy,
-                          iz, tr, _stream(u, stream)), "wave_run")
+    name = "wave_run_pml" if pml else "wave_run"
+    _check(getattr(lib(), name)(
+        ctypes.byref(d), _ptr(u_prev, d, "u_prev"), _ptr(u, d, "u"),
+        _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"), float(dt), float(h), n, ix,
+        iy, iz, tr, _stream(u, stream)), name)
     return (u_prev, u) if n % 2 == 0 else (u, u_prev)
+
+
+def wave_run_pml(d: Desc, u_prev, u, vel2, eta, dt: float, h: float,
+                 nsteps: int, src=(0, 0, 0), src_trace=None, stream=None):
+    """wave_run with the PML kernel's step; returns (older, newest)."""
+    return wave_run(d, u_prev, u, vel2, eta, dt, h, nsteps, src, src_trace,
+                    stream, pml=True)

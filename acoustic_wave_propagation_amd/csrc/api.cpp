@@ -81,24 +81,28 @@ const double *second_difference(int R) {
     return nullptr;
 }
 
-// The wave update on the interior.  When the descriptor states a sponge
-// width p (eta = 0 at least p points inside every interior face) and the
-// eta-free kernel exists, the interior is launched as data regions -- an
-// inner box at distance >= p from every face, which does not read eta, and
-// six slabs that do ("Accelerating High-Order Stencils on GPUs": one kernel
-// for the inner region, another for the PML region).  Every point is
-// written by exactly one launch with the same arithmetic, so the result is
-// bit-identical to one launch over the interior.
+// The wave update on the interior (pml: the PML step, with the
+// eta-gradient coupling).  When the descriptor states a sponge width p
+// (eta = 0 at least p points inside every interior face) and the eta-free
+// kernel exists, the interior is launched as data regions -- an inner box
+// that does not read eta, and six slabs that do ("Accelerating High-Order
+// Stencils on GPUs": one kernel for the inner region, another for the PML
+// region).  The inner box keeps distance p from every face, p + 1 for the
+// PML step, whose coupling reads eta one point further out; there eta and
+// its differences are zero.  Every point is written by exactly one launch
+// with the same arithmetic, so the result is bit-identical to one launch
+// over the interior (for the PML step: up to the sign of a zero result).
 int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void *u_prev,
-                const void *vel2, const void *eta, double wscale, int cus, hipStream_t s) {
+                const void *vel2, const void *eta, double wscale, int cus, hipStream_t s,
+                bool pml) {
     const st::Box in = st::interior_box(d);
-    const int64_t p = d.pml_width;
+    const st::Kind kind = pml ? st::Kind::WavePml : st::Kind::Wave;
+    const int64_t p = d.pml_width > 0 ? d.pml_width + (pml ? 1 : 0) : 0;
     auto fits = [p](int64_t lo, int64_t hi) { return p < hi - lo && 2 * p < hi - lo; };
     const bool split = p > 0 && st::kind_available(d, st::Kind::WaveNoEta) &&
                        fits(in.x0, in.x1) && fits(in.y0, in.y1) && fits(in.z0, in.z1);
     if (!split)
-        return st::launch_star(d, in, st::Kind::Wave, u, u_next, u_prev, vel2, eta, wscale, cus,
-                               s);
+        return st::launch_star(d, in, kind, u, u_next, u_prev, vel2, eta, wscale, cus, s);
     const st::Box c{in.x0 + p, in.x1 - p, in.y0 + p, in.y1 - p, in.z0 + p, in.z1 - p};
     const st::Box slabs[6] = {
         {in.x0, in.x1, in.y0, in.y1, in.z0, c.z0},  // below the inner box in z
@@ -111,8 +115,7 @@ int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void
     int st = st::launch_star(d, c, st::Kind::WaveNoEta, u, u_next, u_prev, vel2, eta, wscale,
                              cus, s);
     for (int i = 0; i < 6 && st == ST_OK; ++i)
-        st = st::launch_star(d, slabs[i], st::Kind::Wave, u, u_next, u_prev, vel2, eta, wscale,
-                             cus, s);
+        st = st::launch_star(d, slabs[i], kind, u, u_next, u_prev, vel2, eta, wscale, cus, s);
     return st;
 }
 
@@ -256,14 +259,26 @@ static int wave_validate(const stencil3d_desc *d, const void *u_prev, const void
     return ST_OK;
 }
 
-ST_EXPORT int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
-              const void *vel2, const void *eta, double dt, double h, void *stream) {
+static int step_common(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
+                       const void *vel2, const void *eta, double dt, double h, void *stream,
+                       bool pml) {
     int st = wave_validate(d, u_prev, u, u_next, vel2, eta, dt, h);
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
     return launch_wave(*d, u, u_next, u_prev, vel2, eta, (dt * dt) / (h * h), cus,
-                       static_cast<hipStream_t>(stream));
+                       static_cast<hipStream_t>(stream), pml);
+}
+
+ST_EXPORT int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
+              const void *vel2, const void *eta, double dt, double h, void *stream) {
+    return step_common(d, u_prev, u, u_next, vel2, eta, dt, h, stream, false);
+}
+
+ST_EXPORT int wave_step_pml(const stencil3d_desc *d, const void *u_prev, const void *u,
+                            void *u_next, const void *vel2, const void *eta, double dt, double h,
+                            void *stream) {
+    return step_common(d, u_prev, u, u_next, vel2, eta, dt, h, stream, true);
 }
 
 ST_EXPORT int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, int64_t iz,
@@ -277,9 +292,10 @@ ST_EXPORT int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int6
     return st::launch_add_source(*d, u, idx, value, static_cast<hipStream_t>(stream));
 }
 
-ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2, const void *eta,
-             double dt, double h, int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
-             const double *src_trace, void *stream) {
+static int run_common(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2,
+                      const void *eta, double dt, double h, int nsteps, int64_t src_x,
+                      int64_t src_y, int64_t src_z, const double *src_trace, void *stream,
+                      bool pml) {
     int st = wave_validate(d, u_prev, u, u_prev, vel2, eta, dt, h);
     if (st) return st;
     if (overlap(d, u_prev, u)) return ST_ERR_ALIAS;
@@ -296,7 +312,7 @@ ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const voi
     const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
     void *a = u_prev, *b = u;  // a: older, b: newer
     for (int n = 0; n < nsteps; ++n) {
-        st = launch_wave(*d, b, a, a, vel2, eta, wscale, cus, s);
+        st = launch_wave(*d, b, a, a, vel2, eta, wscale, cus, s, pml);
         if (st) return st;
         if (src_trace && (st = st::launch_add_source(*d, a, idx, src_trace[n], s))) return st;
         void *t = a;
@@ -304,6 +320,21 @@ ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const voi
         b = t;
     }
     return ST_OK;
+}
+
+ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2,
+                       const void *eta, double dt, double h, int nsteps, int64_t src_x,
+                       int64_t src_y, int64_t src_z, const double *src_trace, void *stream) {
+    return run_common(d, u_prev, u, vel2, eta, dt, h, nsteps, src_x, src_y, src_z, src_trace,
+                      stream, false);
+}
+
+ST_EXPORT int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2,
+                           const void *eta, double dt, double h, int nsteps, int64_t src_x,
+                           int64_t src_y, int64_t src_z, const double *src_trace,
+                           void *stream) {
+    return run_common(d, u_prev, u, vel2, eta, dt, h, nsteps, src_x, src_y, src_z, src_trace,
+                      stream, true);
 }
 
 }  // extern "C"

@@ -21,11 +21,12 @@ inline Box interior_box(const stencil3d_desc &d) {
 }
 
 // Variants of the streaming kernel.  Apply: out = star(in).  Wave: the
-// wave update of (u_prev, in = u, vel2, eta).  The planner may replace
-// Apply by ApplyWide (row-wide tiles) and Wave by WaveNarrow (32-column
-// tiles) where those fit the box better; WaveNoEta is the wave update for a
-// box where eta is zero (no eta stream).
-enum class Kind { Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta };
+// wave update of (u_prev, in = u, vel2, eta).  WavePml: the PML step (the
+// wave update plus the eta-gradient coupling).  The planner may replace
+// Apply by ApplyWide (row-wide tiles), Wave by WaveNarrow and WavePml by
+// WavePmlNarrow (32-column tiles) where those fit the box better; WaveNoEta
+// is the wave update for a box where eta is zero (no eta stream).
+enum class Kind { Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta, WavePml, WavePmlNarrow };
 
 // Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs
 // covering the output box, each streamed through a z chunk of chunk_len

@@ -67,6 +67,7 @@ struct StarArgs {
     int32_t bx0, bx1, by0, by1, bz0, bz1;
     T cc;             // centre weight, plain form
     T ccd;            // centre weight of the difference form
+    T gw;             // weight of the eta-gradient coupling (PML step)
     T cx[ST_MAX_R], cy[ST_MAX_R], cz[ST_MAX_R];  // weight of offsets +-(k+1)
 };
 
@@ -78,15 +79,18 @@ struct StarArgs {
 // alternating z direction of neighbouring chunks, chunk-major (vs
 // tile-major) order of the logical workgroup id, XCD remap, nontemporal
 // stores, nontemporal epilogue loads, minimum waves per SIMD the register
-// allocation must allow, nontemporal stencil-input loads.  The shipped
-// choices are in star2p5d.hip; the others are kept for measurement.
+// allocation must allow, nontemporal stencil-input loads, and whether a
+// step issues its epilogue loads before (EF) or after the stencil-input
+// prefetch.  The shipped choices are in star2p5d.hip; the others are kept
+// for measurement.
 template <int VX_, int VY_, int LX_, int LY_, int D_, int DE_, bool HLA_ = true, int LB_ = 2,
           bool ALT_ = false, bool CMAJ_ = true, bool XCD_ = true, bool NTS_ = false,
-          bool NTL_ = false, int MINW_ = 1, bool NTI_ = false>
+          bool NTL_ = false, int MINW_ = 1, bool NTI_ = false, bool EF_ = false>
 struct TileCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, DE = DE_, LB = LB_;
     static constexpr int MINW = MINW_;  // register budget for >= MINW waves per SIMD
     static constexpr bool NTI = NTI_;      // nontemporal stencil-input loads
+    static constexpr bool EF = EF_;        // epilogue loads first in a step
     static constexpr bool HLA = HLA_, ALT = ALT_, CMAJ = CMAJ_, XCD = XCD_, NTS = NTS_,
                           NTL = NTL_;
     static constexpr int NT = LX * LY, TX = LX * VX, TY = LY * VY;
@@ -95,6 +99,12 @@ struct TileCfg {
 constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
 constexpr int round_up(int a, int b) { return (a + b - 1) / b * b; }
+// smallest ring size >= lo that divides the unroll u (u itself if none)
+constexpr int ring_fit(int u, int lo) {
+    for (int r = lo; r < u; ++r)
+        if (u % r == 0) return r;
+    return u > lo ? u : lo;
+}
 
 // LDS row pitch: at least `need` elements, a multiple of the group width,
 // and an odd multiple of 16 bytes so that the 16-byte accesses of lanes on
@@ -223,8 +233,8 @@ __device__ __forceinline__ void lds_store_group(T *p, const T (&v)[N]) {
 }
 
 // Ring sizes of the kernel below, shared with the host so that z chunks can
-// be sized in whole unrolled blocks.
-template <int R, bool WAVE, class C>
+// be sized in whole unrolled blocks.  E7: the PML step's eta planes.
+template <int R, bool WAVE, class C, bool E7 = false>
 struct Rings {
     static constexpr int D = C::D;                     // stencil-input prefetch depth
     static constexpr int DE = WAVE ? C::DE : 0;        // epilogue prefetch depth
@@ -238,21 +248,32 @@ struct Rings {
     // of H so that the unroll stays short
     static constexpr int W = round_up(2 * R + 1 + D, H);
     static constexpr int E = DE + 1;                   // epilogue slots
-    static constexpr int U = clcm(clcm(clcm(W, H), E), C::LB);  // z-loop unroll
+    static constexpr int U0 = clcm(clcm(clcm(W, H), E), C::LB);
+    // PML step: eta planes z-1..z+1 in registers (the ring padded to divide
+    // the unroll), and the next plane's 1-wide eta halo ring (2 slots)
+    static constexpr int NE = E7 ? ring_fit(U0, 3) : 1;
+    static constexpr int HE = E7 ? 2 : 1;
+    static constexpr int U = clcm(clcm(U0, NE), HE);   // z-loop unroll
 };
 
 // WAVE: fused wave epilogue.  ETA (wave only): read eta; without it the
 // kernel evaluates the same update with eta = 0 (no eta stream, and the
 // factors 1 - eta and 1 / (1 + eta) fold away exactly), for boxes where the
-// caller guarantees eta = 0.
-template <typename T, int R, bool WAVE, class C, bool ETA = true>
+// caller guarantees eta = 0.  E7 (wave with eta): the PML step, which adds
+// the eta-gradient coupling sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) -
+// u(p-e_a)) / (4 h^2) to the Laplacian -- eta's 7-point stencil of halo 1
+// ("Accelerating High-Order Stencils on GPUs", smem_eta description).  As
+// in smem_eta, each plane of eta is staged in LDS with its 1-wide ring; its
+// z neighbours stay in a 3-plane register ring, as u's do.
+template <typename T, int R, bool WAVE, class C, bool ETA = true, bool E7 = false>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
 star2p5d_kernel(StarArgs<T> a) {
+    static_assert(!E7 || (WAVE && ETA), "the eta stencil belongs to the wave update with eta");
     constexpr int VX = C::VX, VY = C::VY, LX = C::LX;
     constexpr int NT = C::NT, TX = C::TX, TY = C::TY;
-    using RG = Rings<R, WAVE, C>;
+    using RG = Rings<R, WAVE, C, E7>;
     constexpr int D = RG::D, DE = RG::DE, HL = RG::HL, H = RG::H, W = RG::W, E = RG::E,
-                  U = RG::U;
+                  U = RG::U, NE = RG::NE, HE = RG::HE;
     // Halo ring in units of VX elements: R rows above and below the tile,
     // and XW units (XW*VX >= R columns) left and right of each tile row.
     constexpr int XW = (R + VX - 1) / VX;
@@ -273,8 +294,17 @@ star2p5d_kernel(StarArgs<T> a) {
     constexpr bool DIFF = std::is_same<T, double>::value;
     static_assert(D >= 1, "at least one plane in flight");
     static_assert(C::LB == 1 || C::LB == 2, "one or two LDS tile buffers");
+    // PML step: eta tile of rows gy0-1 .. gy0+TY with u's pitch and columns,
+    // LB buffers after u's sink, then its own sink; eta halo units are the
+    // two rows above and below (GX groups each) and the group left and right
+    // of every tile row that holds the column next to the tile.
+    constexpr int ETILE = E7 ? (TY + 2) * LP : 0;
+    constexpr int EBASE = LDUMMY + VX;
+    constexpr int EDUMMY = EBASE + C::LB * ETILE;
+    constexpr int NYE = 2 * GX, NXE = 2 * TY;
+    constexpr int KHE = E7 ? (NYE + NXE + NT - 1) / NT : 1;
 
-    __shared__ __align__(16) T lds[LDUMMY + VX];
+    __shared__ __align__(16) T lds[E7 ? EDUMMY + VX : LDUMMY + VX];
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny;
@@ -350,9 +380,36 @@ star2p5d_kernel(StarArgs<T> a) {
         }
     }
 
+    // eta halo units of this thread (PML step)
+    uint32_t eh_off[KHE];
+    int eh_l[KHE];
+#pragma unroll
+    for (int q = 0; q < KHE; ++q) {
+        const int u = E7 ? tid + q * NT : NYE + NXE;
+        if (u < NYE) {
+            const int side = u / GX, g = u - side * GX;
+            const int gy = side ? gy0 + TY : gy0 - 1;
+            eh_off[q] = ((uint32_t)gy * (uint32_t)nx + (uint32_t)(gx0 + g * VX)) * ES;
+            eh_l[q] = (side ? TY + 1 : 0) * LP + PADL + g * VX;
+        } else if (u < NYE + NXE) {
+            // the group ending at gx0-1 (it may start in the previous row,
+            // whose values land in LDS columns nothing reads) or starting
+            // at gx0+TX
+            const int xu = u - NYE, side = xu / TY, row = xu - side * TY;
+            const int gx = side ? gx0 + TX : gx0 - VX;
+            eh_off[q] = ((uint32_t)(gy0 + row) * (uint32_t)nx + (uint32_t)gx) * ES;
+            eh_l[q] = (1 + row) * LP + (side ? PADL + TX : PADL - VX);
+        } else {
+            eh_off[q] = kOOB;
+            eh_l[q] = -1;
+        }
+    }
+
     T win[W][VY][VX];
     T hs[H][KH][VX];
     T up[E][VY][VX], v2[E][VY][VX], et[E][VY][VX];
+    T ew[NE][VY][VX];    // PML step: eta plane at step offset s-1 (mod NE) in slot s
+    T ehs[HE][KHE][VX];  // PML step: eta halo ring of the plane of step k in slot k % HE
 
     // resource of the plane at step offset j from step k (empty if unneeded)
     auto rsrc_at = [&](const T *base, int k, int j, bool needed) {
@@ -380,11 +437,23 @@ star2p5d_kernel(StarArgs<T> a) {
             bload<T, VX, LAUX>(rp, ooff[jj], up[e][jj]);
             bload<T, VX, LAUX>(rv, ooff[jj], v2[e][jj]);
         }
-        if constexpr (ETA) {
+        if constexpr (ETA && !E7) {
             const rsrc_t re = rsrc_at(a.eta, k, 0, needed);
 #pragma unroll
             for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(re, ooff[jj], et[e][jj]);
         }
+    };
+    auto load_eta = [&](int k, int j, bool needed, auto slot_c) {
+        constexpr int s = decltype(slot_c)::value;
+        const rsrc_t r = rsrc_at(a.eta, k, j, needed);
+#pragma unroll
+        for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(r, ooff[jj], ew[s][jj]);
+    };
+    auto load_eta_halo = [&](int k, bool needed, auto slot_c) {
+        constexpr int h = decltype(slot_c)::value;
+        const rsrc_t r = rsrc_at(a.eta, k, 0, needed);
+#pragma unroll
+        for (int q = 0; q < KHE; ++q) bload<T, VX, LAUX>(r, eh_off[q], ehs[h][q]);
     };
 
     // prologue: window planes at step offsets -R .. R+D-1 into slots
@@ -403,6 +472,14 @@ star2p5d_kernel(StarArgs<T> a) {
             constexpr int ev = decltype(e)::value;
             load_epilogue(ev, ev < n, e);
         });
+    // PML step: eta planes of step offsets -1 and 0 (a chunk has n >= 1
+    // planes, and the planes next to it lie inside the array), and the eta
+    // halo ring of step 0
+    if constexpr (E7) {
+        load_eta(0, -1, true, std::integral_constant<int, 0>{});
+        load_eta(0, 0, true, std::integral_constant<int, 1>{});
+        load_eta_halo(0, true, std::integral_constant<int, 0>{});
+    }
 
     // Whole blocks of U steps, with no exit inside a block: the instruction
     // stream is then the same every block and the compiler's wait counts
@@ -416,13 +493,35 @@ star2p5d_kernel(StarArgs<T> a) {
             constexpr int HC = kk % H, HN = (kk + HL) % H;
             constexpr int EC = kk % E, EN = (kk + DE) % E;
             constexpr int LB0 = (kk % C::LB) * LTILE;  // LDS buffer of this step
+            // PML step: eta slots of planes k-1, k, k+1; halo slots of k, k+1
+            constexpr int EM = kk % NE, EC7 = (kk + 1) % NE, EP = (kk + 2) % NE;
+            constexpr int EHC = kk % HE, EHN = (kk + 1) % HE;
             const int k = k0 + kk;
             T *tile = lds + LB0;
+            T *etile = lds + EBASE + (kk % C::LB) * ETILE;
 
-            // 1. prefetch (always issued; empty resource past the chunk)
+            // 1. prefetch (always issued; empty resource past the chunk).
+            //    The load counter drains in issue order, so a wait for a
+            //    load also waits for every load issued before it: with EF
+            //    the epilogue loads go first (pinned there by a scheduling
+            //    barrier) and waiting for them leaves the stencil-input
+            //    prefetch in flight.
+            //    The PML step's eta loads (plane k+1 and its halo ring) go
+            //    with the epilogue's.
+            auto load_step_epilogue = [&]() {
+                load_epilogue(k + DE, k + DE < n, std::integral_constant<int, EN>{});
+                if constexpr (E7) {
+                    load_eta(k, 1, k + 1 <= n, std::integral_constant<int, EP>{});
+                    load_eta_halo(k + 1, k + 1 < n, std::integral_constant<int, EHN>{});
+                }
+            };
+            if constexpr (WAVE && C::EF) {
+                load_step_epilogue();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             load_window(k, R + D, k + D < n, std::integral_constant<int, LEAD>{});
             load_halo(k + HL, k + HL < n, std::integral_constant<int, HN>{});
-            if constexpr (WAVE) load_epilogue(k + DE, k + DE < n, std::integral_constant<int, EN>{});
+            if constexpr (WAVE && !C::EF) load_step_epilogue();
 
             // 2. stage plane k in LDS: own values from the window, halo ring
             //    from registers (inactive halo lanes write the sink).  With
@@ -436,6 +535,17 @@ star2p5d_kernel(StarArgs<T> a) {
                 T *dst = h_l[q] >= 0 ? tile + h_l[q] : lds + LDUMMY;
 #pragma unroll
                 for (int i = 0; i < VX; ++i) dst[i] = hs[HC][q][i];
+            }
+            if constexpr (E7) {
+#pragma unroll
+                for (int j = 0; j < VY; ++j)
+                    lds_store_group<T, VX>(etile + (1 + ly * VY + j) * LP + lcol, ew[EC7][j]);
+#pragma unroll
+                for (int q = 0; q < KHE; ++q) {
+                    T *dst = eh_l[q] >= 0 ? etile + eh_l[q] : lds + EDUMMY;
+#pragma unroll
+                    for (int i = 0; i < VX; ++i) dst[i] = ehs[EHC][q][i];
+                }
             }
             __syncthreads();
 
@@ -460,6 +570,20 @@ star2p5d_kernel(StarArgs<T> a) {
                     ys[r][i] = tile[(lrow0 - R + r) * LP + lcol + i];
                     ys[R + r][i] = tile[(lrow0 + VY + r) * LP + lcol + i];
                 }
+
+            // PML step: eta's in-plane neighbours outside this thread's
+            // own VX x VY block, from the eta tile
+            T eL[VY], eR[VY], eT[VX], eB[VX];
+            if constexpr (E7) {
+                const int er0 = 1 + ly * VY;
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    eL[j] = etile[(er0 + j) * LP + lcol - 1];
+                    eR[j] = etile[(er0 + j) * LP + lcol + VX];
+                }
+                lds_load_group<T, VX>(etile + (er0 - 1) * LP + lcol, eT);
+                lds_load_group<T, VX>(etile + (er0 + VY) * LP + lcol, eB);
+            }
 
             T res[VY][VX];
 #pragma unroll
@@ -486,9 +610,24 @@ star2p5d_kernel(StarArgs<T> a) {
                             acc = fma(a.cx[kz - 1], xm + xp, acc);
                         }
                     }
+                    if constexpr (E7) {
+                        // + dt^2/(4h^2) sum_a (eta(+a) - eta(-a)) (u(+a) - u(-a))
+                        const T exm = i > 0 ? ew[EC7][j][i - 1] : eL[j];
+                        const T exp1 = i + 1 < VX ? ew[EC7][j][i + 1] : eR[j];
+                        const T eym = j > 0 ? ew[EC7][j - 1][i] : eT[i];
+                        const T eyp = j + 1 < VY ? ew[EC7][j + 1][i] : eB[i];
+                        const T uym = j > 0 ? win[CS][j - 1][i] : ys[R - 1][i];
+                        const T uyp = j + 1 < VY ? win[CS][j + 1][i] : ys[R][i];
+                        T g = (exp1 - exm) * (xs[j][R + i + 1] - xs[j][R + i - 1]);
+                        g = fma(eyp - eym, uyp - uym, g);
+                        g = fma(ew[EP][j][i] - ew[EM][j][i],
+                                win[(CS + 1) % W][j][i] - win[(CS + W - 1) % W][j][i], g);
+                        acc = fma(a.gw, g, acc);
+                    }
                     if constexpr (WAVE) {
                         // the weights carry dt^2/h^2: acc = dt^2 * Lap(u)
-                        const T e = ETA ? et[EC][j][i] : T(0);
+                        // (PML step: plus dt^2 times the coupling)
+                        const T e = E7 ? ew[EC7][j][i] : ETA ? et[EC][j][i] : T(0);
                         acc = (T(2) * ctr - (T(1) - e) * up[EC][j][i] + v2[EC][j][i] * acc) /
                               (T(1) + e);
                     }
@@ -518,7 +657,6 @@ star2p5d_kernel(StarArgs<T> a) {
     }
 }
 
-// out = in on every non-interior point; one wave per (y, z) row.
 // out = in on every non-interior point.  The non-interior points are the
 // whole rows (y, z) with z or y in the R-wide shell -- 2R ny rows in the
 // shell planes plus 2R (nz - 2R) rows of the other planes -- and the R
@@ -595,6 +733,7 @@ StarArgs<T> make_args(const stencil3d_desc &d, const Box &b, const void *in, voi
     a.by1 = (int32_t)b.y1;
     a.bz0 = (int32_t)b.z0;
     a.bz1 = (int32_t)b.z1;
+    a.gw = (T)(wscale * 0.25);
     const double cc = d.cx[0] + d.cy[0] + d.cz[0];
     double ksum = 0.0;
     for (int k = 1; k <= R; ++k) ksum += d.cx[k] + d.cy[k] + d.cz[k];

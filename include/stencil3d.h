@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ST_ABI_VERSION 2
+#define ST_ABI_VERSION 3
 #define ST_MAX_R 4
 
 /* element types */
@@ -176,6 +176,30 @@ int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u,
               double h, void *stream);
 
 /*
+ * One time step of the PML kernel: the update of wave_step with the
+ * coupling of eta's and u's central-difference gradients added to the
+ * Laplacian term ("Accelerating High-Order Stencils on GPUs", smem_eta
+ * description: eta enters the PML region through a low-order 7-point
+ * stencil of halo 1 beside the 25-point stencil on u; the pages print no
+ * formula, this is the reading taken):
+ *
+ *   L      = star_d(u) / h^2
+ *   G      = sum_{a = x,y,z} (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) - u(p-e_a)) / (4 h^2)
+ *   u_next = (2 u - (1 - eta) u_prev + vel2 dt^2 (L + G)) / (1 + eta)
+ *
+ * on every interior point; non-interior points of u_next are not written.
+ * eta is read at the interior points and their face neighbours (which may
+ * lie in the halo).  Where eta is the same on a point's six face neighbours
+ * G = 0 and the result is wave_step's.  Same arrays, layout, aliasing and
+ * argument rules as wave_step.  With d->pml_width = p > 0 (R = 4) the
+ * inner box at distance >= p+1 from every interior face, where G = 0, runs
+ * the eta-free kernel (same bits, up to the sign of a zero result).
+ */
+int wave_step_pml(const stencil3d_desc *d, const void *u_prev,
+                  const void *u, void *u_next, const void *vel2,
+                  const void *eta, double dt, double h, void *stream);
+
+/*
  * Point source: u[ix, iy, iz] += value (rounded to d's element type), one
  * device thread.  (ix, iy, iz) are allocated coordinates and must be
  * interior (ST_ERR_BAD_INDEX).
@@ -196,6 +220,15 @@ int wave_run(const stencil3d_desc *d, void *u_prev, void *u,
              const void *vel2, const void *eta, double dt, double h,
              int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
              const double *src_trace, void *stream);
+
+/*
+ * wave_run with the PML kernel's step (wave_step_pml) in place of
+ * wave_step; same arguments, buffers and result placement.
+ */
+int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
+                 const void *vel2, const void *eta, double dt, double h,
+                 int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
+                 const double *src_trace, void *stream);
 
 #ifdef __cplusplus
 }

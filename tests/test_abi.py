@@ -65,7 +65,7 @@ def test_exports_nothing_else(L):
 
 def test_struct_layout_and_version(L):
     assert ctypes.sizeof(B.Desc) == 168
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
     d = B.desc_init("f32", (10, 11, 12), 4)
     assert d.struct_size == 168 and d.nx == 12 and d.ny == 11 and d.nz == 10
     assert d.pml_width == 0
@@ -163,6 +163,17 @@ def test_entry_points_reject_before_enqueue(L):
         c["ST_ERR_ALIAS"]
     assert ws(by, U[0], None, U[2], U[3], U[4], 1e-3, 10.0, None) == \
         c["ST_ERR_NULL"]
+    for ws in (L.wave_step, L.wave_step_pml):
+        assert ws(by, U[0], U[1], U[2], U[3], U[4], math.inf, 10.0, None) == \
+            c["ST_ERR_ARG"]
+        assert ws(by, U[0], U[1], U[1], U[3], U[4], 1e-3, 10.0, None) == \
+            c["ST_ERR_ALIAS"]
+        assert ws(by, U[0], U[1], U[2], U[3], U[2], 1e-3, 10.0, None) == \
+            c["ST_ERR_ALIAS"]
+        assert ws(by, U[0], U[1], U[2], U[3], U[4] + 2, 1e-3, 10.0, None) == \
+            c["ST_ERR_ALIGN"]
+        assert ws(by, U[0], U[1], U[2], U[3], None, 1e-3, 10.0, None) == \
+            c["ST_ERR_NULL"]
     src = L.wave_add_source
     assert src(by, U[0], 3, 10, 10, 1.0, None) == c["ST_ERR_BAD_INDEX"]
     assert src(by, U[0], 10, 10, 16, 1.0, None) == c["ST_ERR_BAD_INDEX"]
@@ -177,6 +188,13 @@ def test_entry_points_reject_before_enqueue(L):
                None) == c["ST_ERR_BAD_INDEX"]
     assert run(by, U[0], U[0] + 8, U[3], U[4], 1e-3, 10.0, 3, 10, 10, 10,
                None, None) == c["ST_ERR_ALIAS"]
+    for run in (L.wave_run, L.wave_run_pml):
+        assert run(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, -1, 10, 10, 10,
+                   None, None) == c["ST_ERR_ARG"]
+        assert run(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, 3, 2, 10, 10, tr,
+                   None) == c["ST_ERR_BAD_INDEX"]
+        assert run(by, U[0], U[1], U[0], U[4], 1e-3, 10.0, 3, 10, 10, 10,
+                   None, None) == c["ST_ERR_ALIAS"]
 
 
 def test_binding_checks_tensors(L):

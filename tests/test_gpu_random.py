@@ -183,3 +183,29 @@ def test_random_wave_data_regions(oracle_mod, torch_dev, seed):
     check_close(interior(outs[1], R), interior(ref, R), _tol(dtype),
                 "data regions case %d" % seed)
 
+
+
+@pytest.mark.parametrize("case", _draw_cases(12, 5151),
+                         ids=lambda c: "case%d" % c[0])
+def test_random_pml_step(oracle_mod, torch_dev, case):
+    """The PML step (eta-gradient coupling) on random shapes, radii and
+    types, with eta drawn per point."""
+    i, R, dtype, shape, _, _, wseed = case
+    log("case %d: pml step R=%d %s shape %s" %
+        (i, R, np.dtype(dtype).name, shape))
+    g = np.random.default_rng(wseed)
+    up = g.uniform(-1, 1, shape).astype(dtype)
+    uu = g.uniform(-1, 1, shape).astype(dtype)
+    v2 = g.uniform(1.5e3 ** 2, 4.5e3 ** 2, shape).astype(dtype)
+    et = g.uniform(0.0, 0.1, shape).astype(dtype)
+    dt_, h = 1e-3, 10.0
+    d = B.desc_init("f32" if dtype == np.float32 else "f64", shape, R)
+    nxt = sentinel_like(shape, dtype)
+    B.wave_step_pml(d, upload(up), upload(uu), nxt, upload(v2), upload(et),
+                    dt_, h)
+    got = nxt.cpu().numpy()
+    ref = oracle_mod.wave_step_pml(up, uu, v2, et, R, list(d.cx[:R + 1]),
+                                   dt_, h)
+    check_close(interior(got, R), interior(ref, R), _tol(dtype),
+                "random pml case %d" % i)
+    check_halo_untouched(got, R, "random pml case %d" % i)
