@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the 25-point (R = 4) star stencil on a 512^3 fp32 interior
 (520^3 allocated with a 4-point halo) on one MI355X, plus the acoustic wave
-step on a 1024^3 interior, the R = 1 Jacobi sweeps on 512^3 and the fp64
-ragged grid as secondary figures.
+step on a 1024^3 interior (and the PML kernel's step on the same fields),
+the R = 1 Jacobi sweeps on 512^3 and the fp64 ragged grid as secondary
+figures.
 
     python bench.py [--steps K] [--warmup W] [--no-wave] [--no-others]
                     [--no-cpu]
@@ -196,11 +197,28 @@ def bench_wave(torch, B, wl, args):
     # vel2, eta read, u_next written
     nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
     achieved = nbytes / per_step / 1e9
+    # the PML kernel's step (eta-gradient coupling, eta's 7-point stencil)
+    # on the same fields: the same bytes, eta's neighbours come from LDS and
+    # registers
+    fn_pml = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
+                                w.sweeps, src, trace, pml=True)
+    wall_p, durs_p = timed_launches(torch, fn_pml, runs, 1)
+    per_p = float(durs_p.mean()) / w.sweeps
+    ach_p = nbytes / per_p / 1e9
     del vel2, eta, u_prev, u
     torch.cuda.empty_cache()
     cpu = None if args.no_cpu else cpu_wave_slab(wl, w, args.cpu_budget / 4)
+    cpu_p = None if args.no_cpu else cpu_wave_slab(wl, w, args.cpu_budget / 4,
+                                                   pml=True)
+    pml = dict(value=round(pts * runs / wall_p / 1e9, 2), unit="GPoints/s",
+               ms_per_step=round(per_p * 1e3, 5), steps_per_run=w.sweeps,
+               runs=runs, cpu_baseline=cpu_p,
+               roofline=dict(bound="hbm", achieved=round(ach_p, 1),
+                             peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(ach_p / PEAK_HBM_GBS, 4),
+                             algorithmic_bytes_per_step=nbytes))
     return dict(workload=w.name, value=pts * runs / wall / 1e9,
-                cpu_baseline=cpu,
+                cpu_baseline=cpu, pml_step=pml,
                 unit="GPoints/s", ms_per_step=per_step * 1e3,
                 steps_per_run=w.sweeps, runs=runs,
                 roofline=dict(bound="hbm", achieved=round(achieved, 1),
@@ -213,11 +231,11 @@ def bench_wave(torch, B, wl, args):
                                    "B/point)"))
 
 
-def cpu_wave_slab(wl, w, budget_s, planes=64):
-    """The oracle's wave step on a slab of the 1032^3 workload: `planes`
-    interior z planes (plus the R halo planes on each side) of the real
-    fields, mid-simulation values for u and u_prev (seeded uniform), the
-    real vel2 and eta."""
+def cpu_wave_slab(wl, w, budget_s, planes=64, pml=False):
+    """The oracle's wave step (pml: the PML step) on a slab of the 1032^3
+    workload: `planes` interior z planes (plus the R halo planes on each
+    side) of the real fields, mid-simulation values for u and u_prev (seeded
+    uniform), the real vel2 and eta."""
     import oracle
     e = w.extra
     R = w.radius
@@ -231,14 +249,15 @@ def cpu_wave_slab(wl, w, budget_s, planes=64):
     c = oracle.laplacian_weights(R)
     out = np.zeros(shp, np.float64)
     npts = planes * (w.shape[1] - 2 * R) * (w.shape[2] - 2 * R)
+    step = oracle.wave_step_pml if pml else oracle.wave_step
     rate, nrun, med = cpu_rate(
-        lambda: oracle.wave_step(up, u, v2, et, R, c, e["dt"], e["h"], out=out),
+        lambda: step(up, u, v2, et, R, c, e["dt"], e["h"], out=out),
         npts, budget_s)
     return dict(value=round(rate, 4), unit="GPoints/s",
                 cores=oracle.num_threads(), kind="oracle",
-                sample="%d wave steps on a %d-plane z slab of the 1032^3 "
+                sample="%d %s steps on a %d-plane z slab of the 1032^3 "
                        "grid (fp64 oracle), median %.2f s each"
-                       % (nrun, planes, med))
+                       % (nrun, "PML" if pml else "wave", planes, med))
 
 
 def bench_others(torch, B, wl, args):
@@ -399,6 +418,9 @@ def main():
         log("wave: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % (wave["value"], wave["ms_per_step"],
                wave["roofline"]["achieved"]))
+        log("wave, PML step: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
+            % (wave["pml_step"]["value"], wave["pml_step"]["ms_per_step"],
+               wave["pml_step"]["roofline"]["achieved"]))
     others = None if args.no_others else bench_others(torch, B, wl, args)
     if others:
         for k, v in others.items():
