@@ -32,8 +32,16 @@ CMDS = {
     + BENCH + "--only-headline --steps 5 --warmup 2",
     "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $REPO/gpurun_out/pmc_tcc -o tcc"
     + BENCH + "--only-headline --steps 5 --warmup 2",
+    "wave_trace": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_wave -o wave"
+    + BENCH + "--only-wave both --no-cpu --steps 2",
 }
+for _v in ("wave", "pml"):
+    for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        CMDS["%s_%s" % (_v, _n)] = (
+            PRE + "--pmc %s -T -d $REPO/gpurun_out/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
+            + BENCH + "--only-wave %s --calib --no-cpu --steps 1" % _v)
 HEADLINE_BYTES = 1098907648  # algorithmic bytes of one 512^3 R=4 fp32 apply
+WAVE_BYTES = 21575499776     # one 1024^3 R=4 fp32 wave (or PML) step
 
 
 def main(argv=None):
@@ -53,7 +61,14 @@ def main(argv=None):
         "star2p5d_r4_512cube_counters.md":
             P.counters_md([db("pmc_sq", "sq"), db("pmc_tcc", "tcc")],
                           "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
+        "wave_and_pml_r4_1024cube_trace.md":
+            P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"]),
     }
+    for v in ("wave", "pml"):
+        out["%s_r4_1024cube_traffic.md" % v] = P.traffic_md(
+            db("pmc_%s_fetch" % v, "fetch"), db("pmc_%s_write" % v, "write"),
+            "star2p5d_kernel", "%s_r4_f32" % v, 1 << 30,
+            CMDS["%s_fetch" % v], CMDS["%s_write" % v], WAVE_BYTES)
     for name, text in out.items():
         with open(os.path.join(prof, name), "w") as f:
             f.write(text)

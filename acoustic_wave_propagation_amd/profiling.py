@@ -53,7 +53,9 @@ def _db(path):
 def kernel_stats(path):
     """[(name, calls, total_us, avg_us, min_us, max_us)] by total time.
     Instantiations that share a (truncated) name are told apart by their
-    kernel id and labelled with workgroups x threads, LDS bytes and VGPRs."""
+    kernel id and labelled with workgroups x threads, LDS bytes and the
+    trace's vgpr_count field (for these wave64 kernels half the compiler's
+    VGPR figure, rounded up to 8 VGPRs first: 96 for 192, 116 for 229)."""
     db = _db(path)
     rows = db.execute(
         "select name, count(*), sum(duration), avg(duration), min(duration), "
@@ -67,7 +69,7 @@ def kernel_stats(path):
     out = []
     # durations are in ns
     for n, c, t, a, mn, mx, wgs, thr, lds, vg, _ in rows:
-        label = n if names[n] == 1 else "%s [%d x %d, LDS %d, %d VGPRs]" % (
+        label = n if names[n] == 1 else "%s [%d x %d, LDS %d, vgpr_count %d]" % (
             n, wgs, thr, lds, vg)
         out.append((label, c, t / 1e3, a / 1e3, mn / 1e3, mx / 1e3))
     return out
@@ -109,7 +111,7 @@ def traffic_md(fetch, write, kernel, name, calib_bytes, cmd_fetch,
         raise RuntimeError("kernel %s not found in the runs" % kernel)
     rd = kf[0][1] * 1024.0 * ff
     wr = kw[0][1] * 1024.0 * fw
-    out = ["# HBM traffic of %s" % kernel, "",
+    out = ["# HBM traffic of %s (%s)" % (kernel, name), "",
            "FETCH_SIZE run:", "", "    " + cmd_fetch, "",
            "WRITE_SIZE run:", "", "    " + cmd_write, "",
            "| counter | copy calibration (KiB/dispatch) | scale | %s "

@@ -18,7 +18,8 @@ bounded number of whole-grid applications.
 --calib adds a plain device copy of known size (for the counter runs that
 turn FETCH_SIZE / WRITE_SIZE into bytes); --only-headline skips everything
 but the timed stencil launches, --only-others runs only the Jacobi and fp64
-workloads (both for profiler runs).
+workloads, --only-wave {wave,pml,both} only the 1032^3 leapfrog with those
+step kinds (all for profiler runs).
 """
 from __future__ import annotations
 
@@ -38,18 +39,20 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
           "R=4 25-pt stencil at 512³ fp32")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "star2p5d_r4_512cube_traffic.md")
+WAVE_TRAFFIC = {v: os.path.join(ROOT, "profiles", "%s_r4_1024cube_traffic.md" % v)
+                for v in ("wave", "pml")}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def recorded_traffic(kernel: str):
+def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE):
     """Bytes per launch measured by the committed counter runs, if they were
     taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
     t = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
                   re.escape(kernel), text)
@@ -163,8 +166,9 @@ def bench_headline(torch, B, wl, args):
     return res, host
 
 
-def bench_wave(torch, B, wl, args):
-    """20-step leapfrog on 1032^3 (1024^3 interior), native time loop."""
+def bench_wave(torch, B, wl, args, variants=("wave", "pml")):
+    """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
+    the pointwise step ("wave") and the PML kernel's step ("pml")."""
     w = wl.WAVE_1024
     e = w.extra
     dev = torch.device("cuda:0")
@@ -187,48 +191,47 @@ def bench_wave(torch, B, wl, args):
     # grid than the data-region launches (thin x slabs of the sponge)
     src = wl.source_point(w)
     trace = wl.source_trace(w)
-    fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
-                            w.sweeps, src, trace)
     runs = max(1, min(args.steps, 5))
-    wall, durs = timed_launches(torch, fn, runs, 1)
     pts = w.interior_points * w.sweeps
-    per_step = float(durs.mean()) / w.sweeps
     # one read and one write per field: u (with its face slabs), u_prev,
-    # vel2, eta read, u_next written
+    # vel2, eta read, u_next written.  The PML kernel's step (eta-gradient
+    # coupling, eta's 7-point stencil) moves the same bytes: eta's
+    # neighbours come from LDS and registers.
     nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
-    achieved = nbytes / per_step / 1e9
-    # the PML kernel's step (eta-gradient coupling, eta's 7-point stencil)
-    # on the same fields: the same bytes, eta's neighbours come from LDS and
-    # registers
-    fn_pml = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
-                                w.sweeps, src, trace, pml=True)
-    wall_p, durs_p = timed_launches(torch, fn_pml, runs, 1)
-    per_p = float(durs_p.mean()) / w.sweeps
-    ach_p = nbytes / per_p / 1e9
+    res = {}
+    for v in variants:
+        fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
+                                w.sweeps, src, trace, pml=(v == "pml"))
+        wall, durs = timed_launches(torch, fn, runs, 1)
+        per = float(durs.mean()) / w.sweeps
+        ach = nbytes / per / 1e9
+        res[v] = dict(value=pts * runs / wall / 1e9, unit="GPoints/s",
+                      ms_per_step=per * 1e3, steps_per_run=w.sweeps,
+                      runs=runs,
+                      roofline=dict(bound="hbm", achieved=round(ach, 1),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(ach / PEAK_HBM_GBS, 4),
+                                    traffic=recorded_traffic(
+                                        "%s_r4_f32" % v, WAVE_TRAFFIC[v]),
+                                    algorithmic_bytes_per_step=nbytes))
+        log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
+            % ("wave" if v == "wave" else "wave, PML step", res[v]["value"],
+               res[v]["ms_per_step"], ach))
     del vel2, eta, u_prev, u
     torch.cuda.empty_cache()
-    cpu = None if args.no_cpu else cpu_wave_slab(wl, w, args.cpu_budget / 4)
-    cpu_p = None if args.no_cpu else cpu_wave_slab(wl, w, args.cpu_budget / 4,
-                                                   pml=True)
-    pml = dict(value=round(pts * runs / wall_p / 1e9, 2), unit="GPoints/s",
-               ms_per_step=round(per_p * 1e3, 5), steps_per_run=w.sweeps,
-               runs=runs, cpu_baseline=cpu_p,
-               roofline=dict(bound="hbm", achieved=round(ach_p, 1),
-                             peak=PEAK_HBM_GBS, unit="GB/s",
-                             frac=round(ach_p / PEAK_HBM_GBS, 4),
-                             algorithmic_bytes_per_step=nbytes))
-    return dict(workload=w.name, value=pts * runs / wall / 1e9,
-                cpu_baseline=cpu, pml_step=pml,
-                unit="GPoints/s", ms_per_step=per_step * 1e3,
-                steps_per_run=w.sweeps, runs=runs,
-                roofline=dict(bound="hbm", achieved=round(achieved, 1),
-                              peak=PEAK_HBM_GBS, unit="GB/s",
-                              frac=round(achieved / PEAK_HBM_GBS, 4),
-                              algorithmic_bytes_per_step=nbytes,
-                              note="per-step mean incl. the 1-thread source "
-                                   "kernel; bytes in the one-read-one-write "
-                                   "convention for all five fields (20.09 "
-                                   "B/point)"))
+    for v in variants:
+        res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
+            wl, w, args.cpu_budget / 4, pml=(v == "pml"))
+    if "wave" not in res:
+        return res
+    out = dict(workload=w.name, **res["wave"])
+    out["roofline"]["note"] = ("per-step mean incl. the 1-thread source "
+                               "kernel; bytes in the one-read-one-write "
+                               "convention for all five fields (20.09 "
+                               "B/point)")
+    if "pml" in res:
+        out["pml_step"] = res["pml"]
+    return out
 
 
 def cpu_wave_slab(wl, w, budget_s, planes=64, pml=False):
@@ -385,6 +388,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-others", action="store_true",
                     help="run only the Jacobi and fp64 workloads (profiling)")
+    ap.add_argument("--only-wave", choices=("wave", "pml", "both"),
+                    help="run only the 1032^3 leapfrog with that step "
+                         "(profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -400,6 +406,13 @@ def main():
         sys.exit(1)
     B.lib()  # fail loudly if the library is missing
 
+    if args.only_wave:
+        bench_wave(torch, B, wl, args,
+                   variants=("wave", "pml") if args.only_wave == "both"
+                   else (args.only_wave,))
+        if args.calib:
+            calib_copy(torch)
+        return
     if args.only_others:
         for k, v in bench_others(torch, B, wl, args).items():
             log("%s: %.1f GPoints/s, %.1f GB/s"
@@ -414,13 +427,6 @@ def main():
     if args.only_headline:
         return
     wave = None if args.no_wave else bench_wave(torch, B, wl, args)
-    if wave:
-        log("wave: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
-            % (wave["value"], wave["ms_per_step"],
-               wave["roofline"]["achieved"]))
-        log("wave, PML step: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
-            % (wave["pml_step"]["value"], wave["pml_step"]["ms_per_step"],
-               wave["pml_step"]["roofline"]["achieved"]))
     others = None if args.no_others else bench_others(torch, B, wl, args)
     if others:
         for k, v in others.items():
