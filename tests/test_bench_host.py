@@ -1,0 +1,97 @@
+"""Host logic of the measurement (CPU only): the one-GPU guard of bench.py,
+the algorithmic-byte formulas the roofline divides by, the staleness check of
+recorded HBM traffic, and the counter-to-bytes scaling of the profile
+summaries (on a synthetic rocpd database)."""
+import importlib.util
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(ROOT, "bench.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_algorithmic_bytes():
+    b = _bench()
+    # 512^3 interior, R = 4, fp32: interior + 8-deep face slabs read once,
+    # interior written once
+    n = 512 ** 3
+    faces = 2 * 4 * 3 * 512 * 512
+    assert b.star_bytes((512, 512, 512), 4, 4) == 4 * (2 * n + faces) \
+        == 1098907648
+    # the wave step adds u_prev, vel2, eta reads on the 1024^3 interior
+    m = 1024 ** 3
+    wave = b.star_bytes((1024,) * 3, 4, 4) + 3 * 4 * m
+    assert wave == 21575499776
+    # non-cubic: faces are per pair of axes
+    assert b.star_bytes((3, 5, 7), 1, 8) == 8 * (2 * 105 + 2 * (35 + 21 + 15))
+
+
+def test_recorded_traffic_tracks_the_kernel_source(tmp_path):
+    b = _bench()
+    from acoustic_wave_propagation_amd.profiling import kernel_hash
+    good = tmp_path / "t.md"
+    good.write_text("traffic_bytes_per_launch[k_r4]: 1234567\n"
+                    "kernel_source_sha256_16: %s\n" % kernel_hash())
+    assert b.recorded_traffic("k_r4", str(good)) == 1234567.0
+    assert b.recorded_traffic("other", str(good)) is None
+    stale = tmp_path / "s.md"
+    stale.write_text("traffic_bytes_per_launch[k_r4]: 1234567\n"
+                     "kernel_source_sha256_16: 0000000000000000\n")
+    assert b.recorded_traffic("k_r4", str(stale)) is None
+    assert b.recorded_traffic("k_r4", str(tmp_path / "missing.md")) is None
+
+
+def _pmc_db(path, counter, rows):
+    db = sqlite3.connect(path)
+    db.execute("create table pmc_events (dispatch_id integer, name text, "
+               "counter_name text, counter_value real)")
+    db.executemany("insert into pmc_events values (?, ?, ?, ?)",
+                   [(i, n, counter, v) for i, (n, v) in enumerate(rows)])
+    db.commit()
+    db.close()
+
+
+def test_traffic_scaling(tmp_path):
+    """FETCH_SIZE reads half the bytes of the 1 GiB calibration copy, so the
+    kernel's fetch counter is scaled by 2; WRITE_SIZE reads them all."""
+    from acoustic_wave_propagation_amd import profiling as P
+    gib = 1 << 30
+    f, w = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _pmc_db(f, "FETCH_SIZE", [(P.COPY_KERNEL, gib / 2 / 1024),
+                              ("star2p5d_kernel", 1000.0),
+                              ("star2p5d_kernel", 1200.0)])
+    _pmc_db(w, "WRITE_SIZE", [(P.COPY_KERNEL, gib / 1024),
+                              ("star2p5d_kernel", 500.0)])
+    text = P.traffic_md(f, w, "star2p5d_kernel", "k_r4", gib, "cmd f",
+                        "cmd w", algorithmic=4000 * 1024)
+    lines = dict(l.split(": ", 1) for l in text.splitlines()
+                 if l.startswith(("read_", "write_", "traffic_")))
+    assert float(lines["read_bytes_per_launch[k_r4]"]) == 2 * 1100 * 1024
+    assert float(lines["write_bytes_per_launch[k_r4]"]) == 500 * 1024
+    assert float(lines["traffic_bytes_per_launch[k_r4]"]) == 2700 * 1024
+    assert "traffic / algorithmic = 0.675" in text
+    with pytest.raises(RuntimeError):
+        _pmc_db(str(tmp_path / "n.db"), "FETCH_SIZE",
+                [("star2p5d_kernel", 1.0)])
+        P.traffic_md(str(tmp_path / "n.db"), w, "star2p5d_kernel", "k", gib,
+                     "", "")
