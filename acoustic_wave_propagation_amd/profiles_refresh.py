@@ -1,11 +1,11 @@
 """Rewrite the rocprofv3 summaries under profiles/ from the raw output of
-one profiling session (the databases the commands below leave under
-gpurun_out/, relative to the repository root).
+one profiling session: the databases the commands below write under $RAW.
 
-    python -m acoustic_wave_propagation_amd.profiles_refresh [RAW_DIR]
+    python -m acoustic_wave_propagation_amd.profiles_refresh RAW_DIR
 
 Each summary records the exact command that produced its database; the
-commands are run from /tmp with TMPDIR=/tmp and the repository at $REPO.
+commands are run from /tmp with TMPDIR=/tmp, the repository at $REPO and the
+raw output directory at $RAW.
 """
 from __future__ import annotations
 
@@ -20,25 +20,25 @@ BENCH = " -- python3 $REPO/bench.py "
 SQ = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
       "SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES SQ_WAIT_INST_LDS")
 CMDS = {
-    "trace": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_trace -o trace"
+    "trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_trace -o trace"
     + BENCH + "--only-headline --steps 50 --warmup 10",
-    "fetch": PRE + "--pmc FETCH_SIZE -T -d $REPO/gpurun_out/pmc_fetch -o fetch"
+    "fetch": PRE + "--pmc FETCH_SIZE -T -d $RAW/pmc_fetch -o fetch"
     + BENCH + "--only-headline --calib --steps 5 --warmup 2",
-    "write": PRE + "--pmc WRITE_SIZE -T -d $REPO/gpurun_out/pmc_write -o write"
+    "write": PRE + "--pmc WRITE_SIZE -T -d $RAW/pmc_write -o write"
     + BENCH + "--only-headline --calib --steps 5 --warmup 2",
-    "others": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_others -o others"
+    "others": PRE + "--kernel-trace --stats -T -d $RAW/prof_others -o others"
     + BENCH + "--only-others --no-cpu --steps 20 --warmup 5",
-    "sq": PRE + "--pmc " + SQ + " -T -d $REPO/gpurun_out/pmc_sq -o sq"
+    "sq": PRE + "--pmc " + SQ + " -T -d $RAW/pmc_sq -o sq"
     + BENCH + "--only-headline --steps 5 --warmup 2",
-    "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $REPO/gpurun_out/pmc_tcc -o tcc"
+    "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_tcc -o tcc"
     + BENCH + "--only-headline --steps 5 --warmup 2",
-    "wave_trace": PRE + "--kernel-trace --stats -T -d $REPO/gpurun_out/prof_wave -o wave"
+    "wave_trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_wave -o wave"
     + BENCH + "--only-wave both --no-cpu --steps 2",
 }
 for _v in ("wave", "pml"):
     for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         CMDS["%s_%s" % (_v, _n)] = (
-            PRE + "--pmc %s -T -d $REPO/gpurun_out/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
+            PRE + "--pmc %s -T -d $RAW/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
             + BENCH + "--only-wave %s --calib --no-cpu --steps 1" % _v)
 HEADLINE_BYTES = 1098907648  # algorithmic bytes of one 512^3 R=4 fp32 apply
 WAVE_BYTES = 21575499776     # one 1024^3 R=4 fp32 wave (or PML) step
@@ -46,7 +46,10 @@ WAVE_BYTES = 21575499776     # one 1024^3 R=4 fp32 wave (or PML) step
 
 def main(argv=None):
     argv = sys.argv[1:] if argv is None else argv
-    raw = argv[0] if argv else os.path.join(ROOT, "gpurun_out")
+    if len(argv) != 1:
+        print(__doc__, file=sys.stderr)
+        return 2
+    raw = argv[0]
     prof = os.path.join(ROOT, "profiles")
     db = lambda d, n: os.path.join(raw, d, n + "_results.db")
     out = {

@@ -86,7 +86,7 @@ def counter_means(path, counter):
 
 def trace_md(path, cmd) -> str:
     out = ["# Kernel trace summary", "",
-           "Command (run from /tmp, repository at $REPO):", "",
+           "Command (run from /tmp, repository at $REPO, raw output under $RAW):", "",
            "    " + cmd, "",
            "| kernel | calls | total (us) | mean (us) | min (us) | max (us) |",
            "|---|---|---|---|---|---|"]
