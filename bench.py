@@ -62,23 +62,43 @@ def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE):
     return float(t.group(1))
 
 
+WARM_S = 0.25  # least device time of untimed calls before a timed region
+
+
 def timed_launches(torch, fn, steps, warmup):
-    """W untimed calls, then K timed ones: wall time of the K (synchronised
-    on both sides) and per-launch HIP-event durations on the launch
-    stream."""
+    """Untimed calls, at least W + 1 of them and at least WARM_S seconds of them
+    (the GPU's clocks ramp up under load: after 10 launches of the 520^3
+    apply a step takes ~0.223 ms, after 200 ~0.210 ms, and half a second idle
+    undoes it), then K timed ones back to back: their wall time (synchronised
+    on both sides).  Then K more calls, each bracketed by HIP events on the
+    launch stream, for per-launch durations; the events stay out of the
+    wall-timed region, where they would add a stream packet and a gap between
+    consecutive kernels."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    fn()  # the first call also loads code objects: not a timing sample
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    for _ in range(max(warmup, 1)):
         fn()
     torch.cuda.synchronize()
+    spent = time.perf_counter() - t_warm
+    # the rest of the warm-up time in one back-to-back batch
+    per_call = spent / max(warmup, 1)
+    for _ in range(int(np.ceil(max(WARM_S - spent, 0.0) / per_call))):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ev = [(torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in ev:
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # s
     return wall, durs
 
@@ -378,7 +398,7 @@ def calib_copy(torch, nbytes=1 << 30):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-wave", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
