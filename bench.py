@@ -186,9 +186,11 @@ def bench_headline(torch, B, wl, args):
     return res, host
 
 
-def bench_wave(torch, B, wl, args, variants=("wave", "pml")):
+def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
     """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
-    the pointwise step ("wave") and the PML kernel's step ("pml")."""
+    the pointwise step ("wave"), the PML kernel's step ("pml") and the
+    pointwise step launched as data regions ("regions": pml_width = the
+    sponge width, so the inner box runs without the eta stream)."""
     w = wl.WAVE_1024
     e = w.extra
     dev = torch.device("cuda:0")
@@ -218,9 +220,17 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml")):
     # coupling, eta's 7-point stencil) moves the same bytes: eta's
     # neighbours come from LDS and registers.
     nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
+    # data regions: eta is zero from depth `sponge` on, so the inner box at
+    # that depth skips the eta stream; its true bytes lack those eta reads
+    dr = B.desc_init("f32", shp, w.radius)
+    dr.pml_width = e["sponge"]
+    inner = 1
+    for n in w.interior:
+        inner *= n - 2 * e["sponge"]
     res = {}
     for v in variants:
-        fn = lambda: B.wave_run(d, u_prev, u, vel2, eta, e["dt"], e["h"],
+        dv = dr if v == "regions" else d
+        fn = lambda: B.wave_run(dv, u_prev, u, vel2, eta, e["dt"], e["h"],
                                 w.sweeps, src, trace, pml=(v == "pml"))
         wall, durs = timed_launches(torch, fn, runs, 1)
         per = float(durs.mean()) / w.sweeps
@@ -232,16 +242,29 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml")):
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(ach / PEAK_HBM_GBS, 4),
                                     traffic=recorded_traffic(
-                                        "%s_r4_f32" % v, WAVE_TRAFFIC[v]),
+                                        "%s_r4_f32" % v, WAVE_TRAFFIC[v])
+                                    if v in WAVE_TRAFFIC else None,
                                     algorithmic_bytes_per_step=nbytes))
+        if v == "regions":
+            true_b = nbytes - 4 * inner
+            res[v]["roofline"]["true_bytes_per_step"] = true_b
+            res[v]["roofline"]["achieved_true_bytes"] = round(
+                true_b / per / 1e9, 1)
+            res[v]["pml_width"] = e["sponge"]
         log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
-            % ("wave" if v == "wave" else "wave, PML step", res[v]["value"],
+            % ({"wave": "wave", "pml": "wave, PML step",
+                "regions": "wave, data regions"}[v], res[v]["value"],
                res[v]["ms_per_step"], ach))
     del vel2, eta, u_prev, u
     torch.cuda.empty_cache()
     for v in variants:
+        if v == "regions":  # the same update as "wave": the same oracle
+            continue
         res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
             wl, w, args.cpu_budget / 4, pml=(v == "pml"))
+    if "regions" in res:
+        res["regions"]["cpu_baseline"] = res.get("wave", {}).get(
+            "cpu_baseline")
     if "wave" not in res:
         return res
     out = dict(workload=w.name, **res["wave"])
@@ -251,6 +274,8 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml")):
                                "B/point)")
     if "pml" in res:
         out["pml_step"] = res["pml"]
+    if "regions" in res:
+        out["data_regions"] = res["regions"]
     return out
 
 
@@ -408,7 +433,7 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-others", action="store_true",
                     help="run only the Jacobi and fp64 workloads (profiling)")
-    ap.add_argument("--only-wave", choices=("wave", "pml", "both"),
+    ap.add_argument("--only-wave", choices=("wave", "pml", "regions", "both"),
                     help="run only the 1032^3 leapfrog with that step "
                          "(profiling)")
     args = ap.parse_args()
