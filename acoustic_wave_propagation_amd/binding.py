@@ -128,6 +128,10 @@ def _ptr(t, d: Desc, name: str) -> int:
         raise TypeError("%s must be a torch tensor" % name)
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device
+        raise ValueError("%s is on %s, the current device is cuda:%d"
+                         % (name, t.device, torch.cuda.current_device()))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if _dtype_code(t.dtype) != d.dtype:

@@ -97,7 +97,10 @@ int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void
                 bool pml) {
     const st::Box in = st::interior_box(d);
     const st::Kind kind = pml ? st::Kind::WavePml : st::Kind::Wave;
-    const int64_t p = d.pml_width > 0 ? d.pml_width + (pml ? 1 : 0) : 0;
+    // (extents are below 2^31: a width from 2^30 up never fits, and clamping
+    // it keeps p + 1 and 2 p from overflowing)
+    const int64_t pw = d.pml_width < ((int64_t)1 << 30) ? d.pml_width : (int64_t)1 << 30;
+    const int64_t p = pw > 0 ? pw + (pml ? 1 : 0) : 0;
     auto fits = [p](int64_t lo, int64_t hi) { return p < hi - lo && 2 * p < hi - lo; };
     const bool split = p > 0 && st::kind_available(d, st::Kind::WaveNoEta) &&
                        fits(in.x0, in.x1) && fits(in.y0, in.y1) && fits(in.z0, in.z1);

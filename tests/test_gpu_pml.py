@@ -221,3 +221,22 @@ def test_pml_run_source_and_roles(oracle_mod, torch_dev):
                                      src=src, src_trace=trace, pml=True)
         check_close(newest.cpu().numpy(), rn, 1e-11, "pml run n=%d" % n)
         check_close(older.cpu().numpy(), ro, 1e-11, "pml run older n=%d" % n)
+
+
+def test_huge_pml_width_is_one_launch(oracle_mod, torch_dev):
+    """A sponge width beyond every extent (up to INT64_MAX) cannot split the
+    interior: the single launch, same bits as pml_width = 0, both steps."""
+    R, dtype = 4, np.float32
+    shape = (30, 31, 70)
+    up, uc, v2, et = _fields(shape, 760, dtype)
+    t = [upload(a) for a in (up, uc, v2, et)]
+    for step in (B.wave_step, B.wave_step_pml):
+        outs = []
+        for pw in (0, 1 << 30, 1 << 62, (1 << 63) - 1):
+            d = B.desc_init("f32", shape, R)
+            d.pml_width = pw
+            out = sentinel_like(shape, dtype)
+            step(d, t[0], t[1], out, t[2], t[3], DT, H)
+            outs.append(out.cpu().numpy())
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
