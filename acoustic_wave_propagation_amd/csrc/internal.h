@@ -29,13 +29,16 @@ inline Box interior_box(const stencil3d_desc &d) {
 enum class Kind { Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta, WavePml, WavePmlNarrow };
 
 // Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs
-// covering the output box, each streamed through a z chunk of chunk_len
-// planes.
+// covering the output box, each streamed through z in chunks.  The first
+// a_nwg workgroups (group A, possibly none) stream tiles [0, a_tiles) in
+// chunks of a_len planes; the others stream the remaining tiles in
+// nchunks chunks of chunk_len planes.  nwg counts both groups.
 struct Geometry {
     Kind kind;
     Box box;
     int tile_x, tile_y, threads;
     int tiles_x, tiles_y, nchunks, chunk_len, nwg;
+    int a_nwg, a_tiles, a_len;
 };
 
 // Whether the kernel variant is instantiated for d's type and radius.

@@ -62,6 +62,10 @@ struct StarArgs {
     int64_t pz;       // plane pitch in elements (nx * ny)
     int32_t nx, ny, nz;
     int32_t tiles_x, tiles_y, chunk_len, nwg;
+    // Two workgroup groups: the first ga_nwg workgroups (group A) stream
+    // tiles [0, ga_tiles) in z chunks of ga_len planes; the rest stream the
+    // other tiles in chunks of chunk_len.  Uniform chunking: ga_nwg = 0.
+    int32_t ga_nwg, ga_tiles, ga_len;
     // output box [bx0,bx1) x [by0,by1) x [bz0,bz1): inside the interior; the
     // tiles and z chunks cover it, and only its points are written
     int32_t bx0, bx1, by0, by1, bz0, bz1;
@@ -308,23 +312,33 @@ star2p5d_kernel(StarArgs<T> a) {
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny;
-    const int wg = C::XCD ? xcd_remap(blockIdx.x, a.nwg) : (int)blockIdx.x;
+    // workgroup group (A: ids below ga_nwg), remapped within the group so
+    // that each XCD sweeps a contiguous band of the group's tiles
+    const bool ga = (int)blockIdx.x < a.ga_nwg;
     const int ntile = a.tiles_x * a.tiles_y;
-    const int nchunks = a.nwg / ntile;
+    const int gfirst = ga ? 0 : a.ga_nwg;            // first workgroup id of the group
+    const int gnwg = ga ? a.ga_nwg : a.nwg - a.ga_nwg;
+    const int gt0 = ga ? 0 : a.ga_tiles;             // first tile of the group
+    const int gtiles = ga ? a.ga_tiles : ntile - a.ga_tiles;
+    const int glen = ga ? a.ga_len : a.chunk_len;
+    const int gid = (int)blockIdx.x - gfirst;
+    const int wg = C::XCD ? xcd_remap(gid, gnwg) : gid;
+    const int nchunks = gnwg / gtiles;
     int chunk, trem;
     if (C::CMAJ) {
-        chunk = wg / ntile;
-        trem = wg - chunk * ntile;
+        chunk = wg / gtiles;
+        trem = wg - chunk * gtiles;
     } else {
         trem = wg / nchunks;
         chunk = wg - trem * nchunks;
     }
+    trem += gt0;
     const int tyi = trem / a.tiles_x;
     const int txi = trem - tyi * a.tiles_x;
     const int gx0 = a.bx0 + txi * TX;
     const int gy0 = a.by0 + tyi * TY;
-    const int zs = a.bz0 + chunk * a.chunk_len;
-    const int ze = min(zs + a.chunk_len, a.bz1);
+    const int zs = a.bz0 + chunk * glen;
+    const int ze = min(zs + glen, a.bz1);
     const int n = ze - zs;                      // planes of this chunk
     // Odd chunks stream downwards, so two neighbouring chunks reach their
     // shared boundary planes at the same time (both at their start, or both
@@ -727,6 +741,9 @@ StarArgs<T> make_args(const stencil3d_desc &d, const Box &b, const void *in, voi
     a.tiles_y = tiles_y;
     a.chunk_len = chunk_len;
     a.nwg = nwg;
+    a.ga_nwg = 0;
+    a.ga_tiles = 0;
+    a.ga_len = 0;
     a.bx0 = (int32_t)b.x0;
     a.bx1 = (int32_t)b.x1;
     a.by0 = (int32_t)b.y0;

@@ -565,3 +565,41 @@ def test_wave_data_regions_ragged(oracle_mod, torch_dev, dtype):
     check_close(interior(runs[12], R), interior(ref, R), tol,
                 "3 free steps, data regions")
 
+
+
+@pytest.mark.parametrize("what", ["apply f32", "wave f32", "apply f64"])
+def test_mixed_chunking(oracle_mod, torch_dev, what):
+    """Grids with a few more tiles than one round of workgroups: the planner
+    streams whole rounds of tiles through all of z and splits only the rest
+    into chunks (two workgroup groups in one launch).  Every output point
+    is still computed once, as the oracle's."""
+    torch, _ = torch_dev
+    # 80 interior planes: 256 tiles stream them whole, the other 8 in 4
+    # chunks of 24 (on 256 compute units)
+    if what == "apply f32":      # 3 x 88 = 264 tiles of 256 x 16
+        R, dtype, shape = 4, np.float32, (88, 1408 + 8, 600 + 8)
+    elif what == "wave f32":     # 8 x 33 = 264 tiles of 128 x 32
+        R, dtype, shape = 4, np.float32, (88, 1056 + 8, 1024 + 8)
+    else:                        # 8 x 33 = 264 tiles of 128 x 16
+        R, dtype, shape = 4, np.float64, (88, 528 + 8, 1000 + 8)
+    log("case mixed chunking %s %s" % (what, shape))
+    if what.startswith("apply"):
+        u = wl.uniform_planes(shape, 810, -1, 1, dtype=dtype)
+        _apply_case(oracle_mod, torch, u, R, what="mixed chunking " + what)
+        return
+    up = wl.uniform_planes(shape, 811, -1, 1, dtype=dtype)
+    uc = wl.uniform_planes(shape, 812, -1, 1, dtype=dtype)
+    v2 = wl.uniform_planes(shape, 813, 1.5e3 ** 2, 4.5e3 ** 2, dtype=dtype)
+    et = wl.uniform_planes(shape, 814, 0.0, 0.1, dtype=dtype)
+    d = B.desc_init("f32", shape, R)
+    c = list(d.cx[:R + 1])
+    t = [upload(a) for a in (up, uc, v2, et)]
+    for step, ref_fn in ((B.wave_step, oracle_mod.wave_step),
+                         (B.wave_step_pml, oracle_mod.wave_step_pml)):
+        out = sentinel_like(shape, dtype)
+        step(d, t[0], t[1], out, t[2], t[3], 1e-3, 10.0)
+        got = out.cpu().numpy()
+        ref = ref_fn(up, uc, v2, et, R, c, 1e-3, 10.0)
+        check_close(interior(got, R), interior(ref, R), F32_TOL,
+                    "mixed chunking %s" % step.__name__)
+        check_halo_untouched(got, R, "mixed chunking")
