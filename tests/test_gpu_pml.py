@@ -17,9 +17,9 @@ import pytest
 from acoustic_wave_propagation_amd import binding as B
 from acoustic_wave_propagation_amd import workloads as wl
 
-from gpu_common import (F32_TOL, F64_TOL, check_close, check_halo_untouched,
-                        device, interior, log, rel_err, sentinel_like, upload,
-                        upload_planes)
+from gpu_common import (F32_TOL, F64_TOL, SENTINEL, check_close,
+                        check_halo_untouched, device, interior, log, rel_err,
+                        sentinel_like, upload, upload_planes)
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +240,42 @@ def test_huge_pml_width_is_one_launch(oracle_mod, torch_dev):
             outs.append(out.cpu().numpy())
         for o in outs[1:]:
             assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
+
+
+def test_pml_1024_sampled_slabs(oracle_mod, torch_dev):
+    """One PML step on the full 1032^3 fields in the launch configuration the
+    benchmark times (random u_prev, u; the workload's vel2 and 32-point
+    sponge), checked against the oracle on three 12-plane slabs: the bottom
+    of the sponge, the middle and the top."""
+    torch, _ = torch_dev
+    w = wl.WAVE_1024
+    e, R = w.extra, w.radius
+    nz = w.shape[0]
+    log("case pml 1024 slabs %s" % (w.shape,))
+    vel2 = upload_planes(lambda a, b: wl.vel2_planes(w, a, b), w.shape,
+                         w.np_dtype)
+    eta = upload_planes(lambda a, b: wl.eta_planes(w, a, b), w.shape,
+                        w.np_dtype)
+    up = upload_planes(lambda a, b: wl.uniform_planes(w.shape, 771, -1, 1, a, b),
+                       w.shape, w.np_dtype)
+    uc = upload_planes(lambda a, b: wl.uniform_planes(w.shape, 772, -1, 1, a, b),
+                       w.shape, w.np_dtype)
+    out = sentinel_like(w.shape, w.np_dtype)
+    d = B.desc_init("f32", w.shape, R)
+    c = list(d.cx[:R + 1])
+    B.wave_step_pml(d, up, uc, out, vel2, eta, e["dt"], e["h"])
+    torch.cuda.synchronize()
+    for z0 in (R, nz // 2 - 6, nz - R - 12):
+        z1 = z0 + 12
+        sl = slice(z0 - R, z1 + R)
+        sub = [t[sl].cpu().numpy() for t in (up, uc, vel2, eta)]
+        ref = oracle_mod.wave_step_pml(*sub, R, c, e["dt"], e["h"])
+        got = out[z0:z1].cpu().numpy()
+        check_close(got[:, R:-R, R:-R], ref[R:-R, R:-R, R:-R], F32_TOL,
+                    "pml 1024 slab z %d..%d" % (z0, z1))
+        s = np.float32(SENTINEL)
+        assert (np.all(got[:, :R] == s) and np.all(got[:, -R:] == s) and
+                np.all(got[:, :, :R] == s) and np.all(got[:, :, -R:] == s)), \
+            "pml 1024 slab: y or x halo written"
+    del vel2, eta, up, uc, out
+    torch.cuda.empty_cache()
