@@ -143,13 +143,11 @@ def cpu_rate(fn, points, budget_s):
     return points / med / 1e9, len(times), med
 
 
-def star_bytes(interior, R, elem):
-    """One read of the interior plus its 2R-deep face slabs, one write of
-    the interior (edges and corners of the halo are never read)."""
-    nz, ny, nx = interior
-    n = nx * ny * nz
-    faces = 2 * R * (ny * nz + nx * nz + nx * ny)
-    return elem * (n + faces) + elem * n
+# algorithmic bytes: one read of the interior plus its 2R-deep face slabs,
+# one write of the interior (edges and corners of the halo are never read);
+# the wave step adds u_prev, vel2 and eta
+from acoustic_wave_propagation_amd.traffic import apply_bytes as star_bytes  # noqa: E402
+from acoustic_wave_propagation_amd.traffic import wave_bytes  # noqa: E402
 
 
 def bench_headline(torch, B, wl, args):
@@ -219,7 +217,7 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
     # vel2, eta read, u_next written.  The PML kernel's step (eta-gradient
     # coupling, eta's 7-point stencil) moves the same bytes: eta's
     # neighbours come from LDS and registers.
-    nbytes = star_bytes(w.interior, w.radius, 4) + 3 * 4 * w.interior_points
+    nbytes = wave_bytes(w.interior, w.radius, 4)
     # data regions: eta is zero from depth `sponge` on, so the inner box at
     # that depth skips the eta stream; its true bytes lack those eta reads
     dr = B.desc_init("f32", shp, w.radius)
