@@ -306,14 +306,24 @@ def test_smooth_fp64_cancellation(oracle_mod, torch_dev):
 
 
 def test_deterministic_and_side_stream(oracle_mod, torch_dev):
-    """No atomics: repeated launches are bitwise identical, also on a
-    non-default stream."""
+    """No atomics: five repeated launches are bitwise identical, also on a
+    non-default stream; likewise the wave and PML steps."""
     torch, dev = torch_dev
     shape = (50, 66, 140)
     u = upload(wl.uniform_planes(shape, 3, -1, 1))
     d = B.desc_init("f32", shape, 4)
+    fields = [upload(wl.uniform_planes(shape, 30 + i, lo, hi)) for i, (lo, hi)
+              in enumerate(((-1, 1), (2.25e6, 2.0e7), (0, 0.1)))]
+    for step in (B.wave_step, B.wave_step_pml):
+        runs = []
+        for _ in range(5):
+            o = sentinel_like(shape, np.float32)
+            step(d, fields[0], u, o, fields[1], fields[2], 1e-3, 10.0)
+            runs.append(o.cpu().numpy())
+        for r in runs[1:]:
+            assert np.array_equal(r.view(np.uint8), runs[0].view(np.uint8))
     outs = []
-    for _ in range(3):
+    for _ in range(5):
         o = sentinel_like(shape, np.float32)
         B.stencil3d_apply(d, u, o)
         outs.append(o)
