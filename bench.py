@@ -47,19 +47,42 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE):
-    """Bytes per launch measured by the committed counter runs, if they were
-    taken on the current kernel source; else None."""
+def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE, what="traffic"):
+    """Bytes per launch measured by the committed counter runs (what:
+    "traffic", "read" or "write"), if they were taken on the current kernel
+    source; else None."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
-    t = re.search(r"traffic_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
-                  re.escape(kernel), text)
+    t = re.search(r"%s_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
+                  (what, re.escape(kernel)), text)
     from acoustic_wave_propagation_amd.profiling import kernel_hash
     if not m or not t or m.group(1) != kernel_hash():
         return None
     return float(t.group(1))
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def reported_hbm_peak(torch):
+    """Peak HBM GB/s from the device's reported memory clock and bus width
+    (double data rate), where the runtime reports them; else None."""
+    p = torch.cuda.get_device_properties(0)
+    clk = getattr(p, "memory_clock_rate", None)   # kHz
+    bus = getattr(p, "memory_bus_width", None)    # bits
+    if not clk or not bus:
+        return None
+    return round(2.0 * clk * 1e3 * bus / 8 / 1e9, 1)
 
 
 WARM_S = 0.25  # least device time of untimed calls before a timed region
@@ -178,6 +201,12 @@ def bench_headline(torch, B, wl, args):
                       frac=round(achieved / PEAK_HBM_GBS, 4),
                       traffic=recorded_traffic("star2p5d_r4_f32"),
                       algorithmic_bytes=nbytes,
+                      # counter reads and writes against their floors
+                      traffic_read=recorded_traffic("star2p5d_r4_f32",
+                                                    what="read"),
+                      traffic_write=recorded_traffic("star2p5d_r4_f32",
+                                                     what="write"),
+                      read_floor=nbytes - 4 * pts, write_floor=4 * pts,
                       kernel="star2p5d_kernel<float,4,false>"),
         gbs_wall=round(nbytes * args.steps / wall / 1e9, 1),
     )
@@ -400,8 +429,17 @@ def cpu_baseline(wl, host, budget_s):
         if time.perf_counter() - t_start > budget_s:
             break
     med = float(np.median(times))
+    # context: the same application on one thread (one run)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    oracle.star_apply(host, w.radius, c, out=out)
+    single = time.perf_counter() - t0
+    oracle.set_num_threads(threads)
     return dict(value=round(w.interior_points / med / 1e9, 4),
-                unit="GPoints/s", cores=oracle.num_threads(), kind="oracle",
+                unit="GPoints/s", cores=threads, kind="oracle",
+                host=host_cpu_model(),
+                single_thread_value=round(w.interior_points / single / 1e9, 4),
                 sample="%d whole-grid applications of the 520^3 R=4 fp32 "
                        "workload (fp64 oracle, long-double accumulation); "
                        "median %.2f s each" % (len(times), med))
@@ -494,7 +532,8 @@ def main():
         "config": {"workload": w.name, "grid": list(w.shape[::-1]),
                    "interior": list(w.interior[::-1]), "radius": w.radius,
                    "boundary": "halo_untouched",
-                   "device": torch.cuda.get_device_name(0)},
+                   "device": torch.cuda.get_device_name(0),
+                   "hbm_peak_reported_gbs": reported_hbm_peak(torch)},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "kernel_ms": head["kernel_ms"],

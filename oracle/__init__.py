@@ -59,6 +59,8 @@ def _load():
                             ctypes.c_double)
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [i32]
         lib.oracle_star_apply.restype = None
         lib.oracle_star_apply.argtypes = [vp, i32, vp, i64, i64, i64, i32,
                                           vp, vp, vp, i32]
@@ -75,6 +77,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle's loops run on (OMP_NUM_THREADS or cores)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Run the oracle's loops on n threads from now on."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------------------

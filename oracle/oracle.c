@@ -33,6 +33,13 @@ static inline long double rd(const void *p, int is_f64, int64_t i)
 
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads the loops below use from now on (n >= 1). */
+void oracle_set_num_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
 /*
  * The star stencil of radius R at one interior point.
  *

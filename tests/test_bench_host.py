@@ -51,8 +51,12 @@ def test_recorded_traffic_tracks_the_kernel_source(tmp_path):
     from acoustic_wave_propagation_amd.profiling import kernel_hash
     good = tmp_path / "t.md"
     good.write_text("traffic_bytes_per_launch[k_r4]: 1234567\n"
+                    "read_bytes_per_launch[k_r4]: 1000000\n"
+                    "write_bytes_per_launch[k_r4]: 234567\n"
                     "kernel_source_sha256_16: %s\n" % kernel_hash())
     assert b.recorded_traffic("k_r4", str(good)) == 1234567.0
+    assert b.recorded_traffic("k_r4", str(good), what="read") == 1000000.0
+    assert b.recorded_traffic("k_r4", str(good), what="write") == 234567.0
     assert b.recorded_traffic("other", str(good)) is None
     stale = tmp_path / "s.md"
     stale.write_text("traffic_bytes_per_launch[k_r4]: 1234567\n"
