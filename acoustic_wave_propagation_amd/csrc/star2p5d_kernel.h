@@ -544,22 +544,19 @@ star2p5d_kernel(StarArgs<T> a) {
             if constexpr (C::LB == 1) __syncthreads();
 #pragma unroll
             for (int j = 0; j < VY; ++j) lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, win[CS][j]);
+            // (ring units and the sink are whole 16-byte groups: one
+            // ds_write_b128 each)
 #pragma unroll
-            for (int q = 0; q < KH; ++q) {
-                T *dst = h_l[q] >= 0 ? tile + h_l[q] : lds + LDUMMY;
-#pragma unroll
-                for (int i = 0; i < VX; ++i) dst[i] = hs[HC][q][i];
-            }
+            for (int q = 0; q < KH; ++q)
+                lds_store_group<T, VX>(h_l[q] >= 0 ? tile + h_l[q] : lds + LDUMMY, hs[HC][q]);
             if constexpr (E7) {
 #pragma unroll
                 for (int j = 0; j < VY; ++j)
                     lds_store_group<T, VX>(etile + (1 + ly * VY + j) * LP + lcol, ew[EC7][j]);
 #pragma unroll
-                for (int q = 0; q < KHE; ++q) {
-                    T *dst = eh_l[q] >= 0 ? etile + eh_l[q] : lds + EDUMMY;
-#pragma unroll
-                    for (int i = 0; i < VX; ++i) dst[i] = ehs[EHC][q][i];
-                }
+                for (int q = 0; q < KHE; ++q)
+                    lds_store_group<T, VX>(eh_l[q] >= 0 ? etile + eh_l[q] : lds + EDUMMY,
+                                           ehs[EHC][q]);
             }
             __syncthreads();
 
