@@ -207,3 +207,16 @@ def test_binding_checks_tensors(L):
         B.stencil3d_apply(d, np.zeros(729, np.float32), cpu)
     with pytest.raises(ValueError, match="unsupported dtype"):
         B.desc_init("f16", (9, 9, 9), 1)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With the shared library absent the binding raises (no fallback of any
+    kind): the first call that needs it names the build command."""
+    import importlib
+    mod = importlib.import_module("acoustic_wave_propagation_amd.binding")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "libstencil3d.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mod.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        mod.desc_init("f32", (9, 9, 9), 1)
