@@ -21,6 +21,10 @@
  *    reports a HIP error seen right after the launch.
  *  - Thread safety: calls may come from any host thread; the library holds
  *    no mutable state besides a per-device cache of the compute-unit count.
+ *  - Graph capture: a call only enqueues kernel launches on stream (no
+ *    allocation, synchronisation, memset or copy), so it may be captured
+ *    into a HIP graph and replayed.  Host arguments are read when the call
+ *    is made: a captured wave_run replays the source values it was given.
  */
 #ifndef STENCIL3D_H
 #define STENCIL3D_H
