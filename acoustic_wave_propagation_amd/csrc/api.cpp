@@ -1,20 +1,19 @@
 // api.cpp -- the extern "C" surface of libstencil3d.so (include/stencil3d.h).
 //
-// Everything here runs on the host: argument validation (complete before
-// anything is enqueued), the Laplacian weight table, geometry planning via
-// the kernel layer, and the native Jacobi and leapfrog loops.  No exception
-// leaves this file; every entry point returns an ST_* status.
+// Everything here runs on the host: argument validation (validate.cpp,
+// complete before anything is enqueued), geometry planning via the kernel
+// layer, and the native Jacobi and leapfrog loops.  No exception leaves
+// this file; every entry point returns an ST_* status.
 
 #include <hip/hip_runtime.h>
-#include <math.h>
 #include <stdint.h>
-#include <string.h>
 
 #include <atomic>
 
 #include "internal.h"
 #include "pass_plan.h"
 #include "stencil3d.h"
+#include "validate.h"
 
 namespace {
 
@@ -40,45 +39,6 @@ int current_cus(int *status) {
     }
     if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
     return cus;
-}
-
-size_t elem_size(const stencil3d_desc *d) { return d->dtype == ST_F64 ? 8 : 4; }
-
-size_t field_bytes(const stencil3d_desc *d) {
-    return (size_t)d->nx * (size_t)d->ny * (size_t)d->nz * elem_size(d);
-}
-
-int check_ptr(const stencil3d_desc *d, const void *p) {
-    if (!p) return ST_ERR_NULL;
-    if ((uintptr_t)p % elem_size(d)) return ST_ERR_ALIGN;
-    return ST_OK;
-}
-
-bool overlap(const stencil3d_desc *d, const void *a, const void *b) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b, n = field_bytes(d);
-    return x < y + n && y < x + n;
-}
-
-bool interior_index(const stencil3d_desc *d, int64_t ix, int64_t iy, int64_t iz) {
-    const int64_t R = d->radius;
-    return ix >= R && ix < d->nx - R && iy >= R && iy < d->ny - R && iz >= R && iz < d->nz - R;
-}
-
-// Order-2R central second-difference weights per axis (unit spacing):
-// index 0 the centre, index k the weight of offsets +-k.
-const double *second_difference(int R) {
-    static const double w1[] = {-2.0, 1.0};
-    static const double w2[] = {-5.0 / 2.0, 4.0 / 3.0, -1.0 / 12.0};
-    static const double w3[] = {-49.0 / 18.0, 3.0 / 2.0, -3.0 / 20.0, 1.0 / 90.0};
-    static const double w4[] = {-205.0 / 72.0, 8.0 / 5.0, -1.0 / 5.0, 8.0 / 315.0,
-                                -1.0 / 560.0};
-    switch (R) {
-    case 1: return w1;
-    case 2: return w2;
-    case 3: return w3;
-    case 4: return w4;
-    }
-    return nullptr;
 }
 
 // The wave update on the interior (pml: the PML step, with the
@@ -122,12 +82,6 @@ int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void
     return st;
 }
 
-int wave_checks(const stencil3d_desc *d, double dt, double h) {
-    if (!isfinite(dt) || !isfinite(h) || !(h > 0.0)) return ST_ERR_ARG;
-    (void)d;
-    return ST_OK;
-}
-
 }  // namespace
 
 // The library is built with hidden symbols; only the functions of
@@ -138,68 +92,18 @@ extern "C" {
 
 ST_EXPORT int stencil3d_abi_version(void) { return ST_ABI_VERSION; }
 
-ST_EXPORT const char *stencil3d_strerror(int code) {
-    switch (code) {
-    case ST_OK: return "ok";
-    case ST_ERR_NULL: return "required pointer is NULL";
-    case ST_ERR_STRUCT_SIZE: return "descriptor struct_size does not match this library";
-    case ST_ERR_DTYPE: return "unknown element type";
-    case ST_ERR_RADIUS: return "radius outside 1..ST_MAX_R";
-    case ST_ERR_DIMS: return "grid extents too small (< 2R+1) or plane too large";
-    case ST_ERR_BOUNDARY: return "unknown boundary mode";
-    case ST_ERR_ALIAS: return "buffers overlap where they must not";
-    case ST_ERR_BAD_INDEX: return "source point outside the interior";
-    case ST_ERR_COEFF: return "non-finite stencil weight";
-    case ST_ERR_ARG: return "bad scalar argument";
-    case ST_ERR_ALIGN: return "pointer not aligned to the element size";
-    case ST_ERR_LAUNCH: return "HIP kernel launch failed";
-    case ST_ERR_DEVICE: return "no usable HIP device";
-    }
-    return "unknown status code";
-}
+ST_EXPORT const char *stencil3d_strerror(int code) { return st::check::message(code); }
 
-ST_EXPORT int stencil3d_desc_validate(const stencil3d_desc *d) {
-    if (!d) return ST_ERR_NULL;
-    if (d->struct_size != sizeof(stencil3d_desc)) return ST_ERR_STRUCT_SIZE;
-    if (d->dtype != ST_F32 && d->dtype != ST_F64) return ST_ERR_DTYPE;
-    if (d->radius < 1 || d->radius > ST_MAX_R) return ST_ERR_RADIUS;
-    if (d->boundary != ST_BC_HALO_UNTOUCHED && d->boundary != ST_BC_DIRICHLET_COPY)
-        return ST_ERR_BOUNDARY;
-    const int64_t m = 2 * (int64_t)d->radius + 1;
-    if (d->nx < m || d->ny < m || d->nz < m) return ST_ERR_DIMS;
-    const int64_t lim = (int64_t)1 << 31;
-    if (d->nx >= lim || d->ny >= lim || d->nz >= lim) return ST_ERR_DIMS;
-    if (d->nx * d->ny * (int64_t)elem_size(d) >= lim) return ST_ERR_DIMS;
-    for (int k = 0; k <= d->radius; ++k)
-        if (!isfinite(d->cx[k]) || !isfinite(d->cy[k]) || !isfinite(d->cz[k]))
-            return ST_ERR_COEFF;
-    if (d->pml_width < 0) return ST_ERR_ARG;
-    return ST_OK;
-}
+ST_EXPORT int stencil3d_desc_validate(const stencil3d_desc *d) { return st::check::desc(d); }
 
 ST_EXPORT int stencil3d_desc_init(stencil3d_desc *d, int dtype, int64_t nx, int64_t ny, int64_t nz,
-                        int radius, int boundary) {
-    if (!d) return ST_ERR_NULL;
-    memset(d, 0, sizeof(*d));
-    d->struct_size = sizeof(stencil3d_desc);
-    d->dtype = dtype;
-    d->nx = nx;
-    d->ny = ny;
-    d->nz = nz;
-    d->radius = radius;
-    d->boundary = boundary;
-    const double *w = second_difference(radius);
-    if (!w) return ST_ERR_RADIUS;
-    for (int k = 0; k <= radius; ++k) d->cx[k] = d->cy[k] = d->cz[k] = w[k];
-    return stencil3d_desc_validate(d);
+                                  int radius, int boundary) {
+    return st::check::init(d, dtype, nx, ny, nz, radius, boundary);
 }
 
 ST_EXPORT int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out, void *stream) {
-    int st = stencil3d_desc_validate(d);
+    int st = st::check::apply_args(d, in, out);
     if (st) return st;
-    if ((st = check_ptr(d, in)) || (st = check_ptr(d, out))) return st;
-    if (overlap(d, in, out)) return ST_ERR_ALIAS;
-    st = ST_OK;
     const int cus = current_cus(&st);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -212,12 +116,8 @@ ST_EXPORT int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out
 
 ST_EXPORT int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, int sweeps,
                      void *stream) {
-    int st = stencil3d_desc_validate(d);
+    int st = st::check::jacobi_args(d, buf0, buf1, sweeps);
     if (st) return st;
-    if ((st = check_ptr(d, buf0)) || (st = check_ptr(d, buf1))) return st;
-    if (sweeps < 0) return ST_ERR_ARG;
-    if (overlap(d, buf0, buf1)) return ST_ERR_ALIAS;
-    st = ST_OK;
     const int cus = current_cus(&st);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,27 +145,10 @@ ST_EXPORT int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, 
     return ST_OK;
 }
 
-static int wave_validate(const stencil3d_desc *d, const void *u_prev, const void *u,
-                         const void *u_next, const void *vel2, const void *eta, double dt,
-                         double h) {
-    int st = stencil3d_desc_validate(d);
-    if (st) return st;
-    if ((st = check_ptr(d, u_prev)) || (st = check_ptr(d, u)) || (st = check_ptr(d, u_next)) ||
-        (st = check_ptr(d, vel2)) || (st = check_ptr(d, eta)))
-        return st;
-    if ((st = wave_checks(d, dt, h))) return st;
-    // u_next may be u_prev exactly (in-place leapfrog) but not a shifted
-    // overlap of it, and must not overlap any other input.
-    if (overlap(d, u_next, u) || overlap(d, u_next, vel2) || overlap(d, u_next, eta))
-        return ST_ERR_ALIAS;
-    if (u_next != u_prev && overlap(d, u_next, u_prev)) return ST_ERR_ALIAS;
-    return ST_OK;
-}
-
 static int step_common(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
                        const void *vel2, const void *eta, double dt, double h, void *stream,
                        bool pml) {
-    int st = wave_validate(d, u_prev, u, u_next, vel2, eta, dt, h);
+    int st = st::check::wave_args(d, u_prev, u, u_next, vel2, eta, dt, h);
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
@@ -286,11 +169,8 @@ ST_EXPORT int wave_step_pml(const stencil3d_desc *d, const void *u_prev, const v
 
 ST_EXPORT int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int64_t iy, int64_t iz,
                     double value, void *stream) {
-    int st = stencil3d_desc_validate(d);
+    const int st = st::check::source_args(d, u, ix, iy, iz, value);
     if (st) return st;
-    if ((st = check_ptr(d, u))) return st;
-    if (!interior_index(d, ix, iy, iz)) return ST_ERR_BAD_INDEX;
-    if (!isfinite(value)) return ST_ERR_ARG;
     const int64_t idx = ix + d->nx * (iy + d->ny * iz);
     return st::launch_add_source(*d, u, idx, value, static_cast<hipStream_t>(stream));
 }
@@ -299,15 +179,9 @@ static int run_common(const stencil3d_desc *d, void *u_prev, void *u, const void
                       const void *eta, double dt, double h, int nsteps, int64_t src_x,
                       int64_t src_y, int64_t src_z, const double *src_trace, void *stream,
                       bool pml) {
-    int st = wave_validate(d, u_prev, u, u_prev, vel2, eta, dt, h);
+    int st = st::check::run_args(d, u_prev, u, vel2, eta, dt, h, nsteps, src_x, src_y, src_z,
+                                 src_trace);
     if (st) return st;
-    if (overlap(d, u_prev, u)) return ST_ERR_ALIAS;
-    if (nsteps < 0) return ST_ERR_ARG;
-    if (src_trace) {
-        if (!interior_index(d, src_x, src_y, src_z)) return ST_ERR_BAD_INDEX;
-        for (int n = 0; n < nsteps; ++n)
-            if (!isfinite(src_trace[n])) return ST_ERR_ARG;
-    }
     const int cus = current_cus(&st);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
