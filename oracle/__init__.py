@@ -172,23 +172,26 @@ def jacobi(inp: np.ndarray, sweeps: int, R: int, cx, cy=None, cz=None):
     return a
 
 
-def wave_step(u_prev, u, vel2, eta, R, c, dt, h, out=None):
+def wave_step(u_prev, u, vel2, eta, R, c, dt, h, out=None, cy=None, cz=None):
     """One wave step on the interior; returns fp64 ``u_next``.
 
-    ``u_next = (2u - (1-eta) u_prev + vel2 dt^2 star(u)/h^2) / (1+eta)``.
+    ``u_next = (2u - (1-eta) u_prev + vel2 dt^2 star(u)/h^2) / (1+eta)``,
+    star with per-axis weights ``c`` (x), ``cy``, ``cz`` (default: ``c``).
     Non-interior points of ``out`` are left as given (zeros by default).
     """
     return _wave(_load().oracle_wave_step, u_prev, u, vel2, eta, R, c, dt, h,
-                 out)
+                 out, cy, cz)
 
 
-def _wave(fn, u_prev, u, vel2, eta, R, c, dt, h, out):
+def _wave(fn, u_prev, u, vel2, eta, R, c, dt, h, out, cy=None, cz=None):
     arrs = [np.ascontiguousarray(a) for a in (u_prev, u, vel2, eta)]
     shape = arrs[1].shape
     if any(a.shape != shape for a in arrs) or len(shape) != 3:
         raise ValueError("all fields must share one 3D shape")
     nz, ny, nx = shape
     c = _coef(c, R)
+    cy = c if cy is None else _coef(cy, R)
+    cz = c if cz is None else _coef(cz, R)
     if out is None:
         out = np.zeros(shape, dtype=np.float64)
     if out.dtype != np.float64 or not out.flags.c_contiguous or \
@@ -197,12 +200,13 @@ def _wave(fn, u_prev, u, vel2, eta, R, c, dt, h, out):
                          "fields' shape")
     up, uu, v2, et = arrs
     fn(_ptr(up), _f64flag(up), _ptr(uu), _f64flag(uu), _ptr(v2), _f64flag(v2),
-       _ptr(et), _f64flag(et), _ptr(out), nx, ny, nz, R, _ptr(c), _ptr(c),
-       _ptr(c), float(dt), float(h))
+       _ptr(et), _f64flag(et), _ptr(out), nx, ny, nz, R, _ptr(c), _ptr(cy),
+       _ptr(cz), float(dt), float(h))
     return out
 
 
-def wave_step_pml(u_prev, u, vel2, eta, R, c, dt, h, out=None):
+def wave_step_pml(u_prev, u, vel2, eta, R, c, dt, h, out=None, cy=None,
+                  cz=None):
     """One wave step of the PML kernel on the interior; returns fp64 ``u_next``.
 
     ``u_next = (2u - (1-eta) u_prev + vel2 dt^2 (star(u) + G)/h^2) / (1+eta)``
@@ -211,7 +215,7 @@ def wave_step_pml(u_prev, u, vel2, eta, R, c, dt, h, out=None):
     points of ``out`` are left as given (zeros by default).
     """
     return _wave(_load().oracle_wave_step_pml, u_prev, u, vel2, eta, R, c,
-                 dt, h, out)
+                 dt, h, out, cy, cz)
 
 
 def wave_run(u_prev, u, vel2, eta, R, c, dt, h, nsteps, src=None,

@@ -279,3 +279,27 @@ def test_pml_1024_sampled_slabs(oracle_mod, torch_dev):
             "pml 1024 slab: y or x halo written"
     del vel2, eta, up, uc, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_anisotropic_weights_wave_and_pml(oracle_mod, torch_dev, dtype):
+    """Per-axis weights from the descriptor in the wave and PML steps (each
+    axis scaled by dt^2/h^2 on its own), against the oracle's anisotropic
+    stencil."""
+    R = 4
+    shape = (30, 41, 77)
+    up, uc, v2, et = _fields(shape, 780, dtype)
+    d = B.desc_init(_name(dtype), shape, R)
+    w = np.random.default_rng(781).uniform(-1, 1, (3, R + 1))
+    for k in range(R + 1):
+        d.cx[k], d.cy[k], d.cz[k] = w[0, k], w[1, k], w[2, k]
+    t = [upload(a) for a in (up, uc, v2, et)]
+    for step, ref_fn in ((B.wave_step, oracle_mod.wave_step),
+                         (B.wave_step_pml, oracle_mod.wave_step_pml)):
+        out = sentinel_like(shape, dtype)
+        step(d, t[0], t[1], out, t[2], t[3], DT, H)
+        got = out.cpu().numpy()
+        ref = ref_fn(up, uc, v2, et, R, w[0], DT, H, cy=w[1], cz=w[2])
+        check_close(interior(got, R), interior(ref, R), _tol(dtype),
+                    "anisotropic %s %s" % (step.__name__, _name(dtype)))
+        check_halo_untouched(got, R, "anisotropic")
