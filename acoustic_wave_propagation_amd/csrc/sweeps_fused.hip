@@ -37,6 +37,7 @@ struct FusedShipped<double, NS> {
 
 struct FusedPlan {
     int tiles_x, tiles_y, chunk_len, nwg, threads;
+    int a_nwg, a_tiles, a_len;  // group A (whole-z columns), as in plan_geometry
 };
 
 template <typename T, int NS>
@@ -50,26 +51,44 @@ FusedPlan plan_fused(const stencil3d_desc &d, int cus) {
     p.threads = C::NT;
     const int64_t tiles = (int64_t)p.tiles_x * p.tiles_y;
     // one workgroup per compute unit (LDS and registers); minimise
-    // rounds * (chunk + pipeline fill), as for the single-sweep kernel
+    // rounds * (chunk + pipeline fill), as for the single-sweep kernel,
+    // with the same mixed chunking when the tiles outnumber one round
     const int64_t cap = cus > 0 ? cus : 256;
-    int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
-    const int64_t enough = 8 * cap / (tiles > 0 ? tiles : 1) + 1;  // see plan_geometry
-    if (maxch > enough) maxch = enough;
-    int64_t best_len = iz, best_n = 1, best_cost = -1;
-    for (int64_t nch = 1; nch <= maxch; ++nch) {
-        int64_t len = (iz + nch - 1) / nch;
-        len = (len + FS::U - 1) / FS::U * FS::U;
-        const int64_t n = (iz + len - 1) / len;
-        const int64_t rounds = (tiles * n + cap - 1) / cap;
-        const int64_t cost = rounds * (len + FS::PROLOGUE + 4);
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best_len = len;
-            best_n = n;
+    const int64_t fill = FS::PROLOGUE + 4;
+    struct Chunks {
+        int64_t len, nch, cost;
+    };
+    auto best_chunks = [&](int64_t nt) {
+        int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
+        const int64_t enough = 8 * cap / (nt > 0 ? nt : 1) + 1;  // see plan_geometry
+        if (maxch > enough) maxch = enough;
+        Chunks best{iz, 1, -1};
+        for (int64_t nch = 1; nch <= maxch; ++nch) {
+            int64_t len = (iz + nch - 1) / nch;
+            len = (len + FS::U - 1) / FS::U * FS::U;
+            const int64_t n = (iz + len - 1) / len;
+            const int64_t rounds = (nt * n + cap - 1) / cap;
+            const int64_t cost = rounds * (len + fill);
+            if (best.cost < 0 || cost < best.cost) best = Chunks{len, n, cost};
+        }
+        return best;
+    };
+    const Chunks uni = best_chunks(tiles);
+    p.a_nwg = p.a_tiles = p.a_len = 0;
+    p.chunk_len = (int)uni.len;
+    p.nwg = (int)(tiles * uni.nch);
+    const int64_t full = tiles / cap * cap, rest = tiles - full;
+    if (full > 0 && rest > 0) {
+        const int64_t blen = (iz + FS::U - 1) / FS::U * FS::U;
+        const Chunks b = best_chunks(rest);
+        if (full / cap * (blen + fill) + b.cost < uni.cost) {
+            p.a_nwg = (int)full;
+            p.a_tiles = (int)full;
+            p.a_len = (int)iz;
+            p.chunk_len = (int)b.len;
+            p.nwg = (int)(full + rest * b.nch);
         }
     }
-    p.chunk_len = (int)best_len;
-    p.nwg = (int)(tiles * best_n);
     return p;
 }
 
@@ -77,8 +96,11 @@ template <typename T, int NS>
 int launch_ns(const stencil3d_desc &d, const void *in, void *out, int cus, hipStream_t s) {
     using C = typename FusedShipped<T, NS>::Cfg;
     const FusedPlan p = plan_fused<T, NS>(d, cus);
-    const StarArgs<T> a = make_args<T, 1>(d, interior_box(d), in, out, nullptr, nullptr, nullptr,
-                                          1.0, p.tiles_x, p.tiles_y, p.chunk_len, p.nwg);
+    StarArgs<T> a = make_args<T, 1>(d, interior_box(d), in, out, nullptr, nullptr, nullptr, 1.0,
+                                    p.tiles_x, p.tiles_y, p.chunk_len, p.nwg);
+    a.ga_nwg = p.a_nwg;
+    a.ga_tiles = p.a_tiles;
+    a.ga_len = p.a_len;
     hipLaunchKernelGGL((sweeps_fused_kernel<T, 1, NS, C>), dim3(p.nwg), dim3(p.threads), 0, s, a);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }

@@ -669,3 +669,28 @@ def test_graph_capture_replays(torch_dev):
         # eager work between replays
         B.stencil3d_apply(d, f[1], outs[0])
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_jacobi_fused_mixed_chunking(torch_dev, dtype):
+    """A grid with more fused-pass tiles than one round of workgroups (300
+    fp32 / 600 fp64 tiles on 256 compute units): whole columns for the full
+    rounds, chunks for the rest.  Ten sweeps (passes 6 + 4, or 4 + 4 + 2 in
+    fp64) are bit-identical to ten single applies."""
+    torch, _ = torch_dev
+    shape = (102, 962, 642)
+    name = "f32" if dtype == np.float32 else "f64"
+    log("case jacobi mixed chunking %s %s" % (name, shape))
+    u = wl.uniform_planes(shape, 97, -1, 1, dtype=dtype)
+    d = B.desc_init(name, shape, 1, B.DIRICHLET_COPY)
+    state = upload(u)
+    for _ in range(10):
+        nxt = sentinel_like(shape, dtype)
+        B.stencil3d_apply(d, state, nxt)
+        state = nxt
+    b0, b1 = upload(u), sentinel_like(shape, dtype)
+    res = B.stencil3d_jacobi(d, b0, b1, 10)
+    assert res is b0
+    got, want = res.cpu().numpy(), state.cpu().numpy()
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), \
+        "%d points differ" % int((got != want).sum())
