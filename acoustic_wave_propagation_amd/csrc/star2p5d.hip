@@ -219,59 +219,16 @@ Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int c
     const int64_t tiles = (int64_t)g.tiles_x * g.tiles_y;
     // Split z into chunks.  About 512 threads run per compute unit (the
     // register window allows two waves per SIMD), so `cap` workgroups run at
-    // once and a set of equal chunks takes ceil(workgroups / cap) rounds;
-    // each round lasts a chunk's planes plus its pipeline fill.  For
-    // uniform chunking pick the chunk count that minimises rounds * (chunk
-    // + fill); never below 4R planes per chunk; chunk lengths are whole
-    // blocks of the kernel's z unroll (the kernel runs whole blocks).
+    // once; chunks are no shorter than about 4R planes.
     const int R = d.radius;
     const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * (g.threads >= 512 ? 1 : 512 / g.threads);
-    const int64_t fill = sh.prologue + 4;
-    struct Chunks {
-        int64_t len, nch, cost;
-    };
-    auto best_chunks = [&](int64_t nt) {
-        // more chunks than fill a few rounds of workgroups never pay; the
-        // cap keeps the search short for very tall grids
-        int64_t maxch = bz / (4 * R) > 0 ? bz / (4 * R) : 1;
-        const int64_t enough = 8 * cap / (nt > 0 ? nt : 1) + 1;
-        if (maxch > enough) maxch = enough;
-        Chunks best{bz, 1, -1};
-        for (int64_t nch = 1; nch <= maxch; ++nch) {
-            int64_t len = (bz + nch - 1) / nch;
-            len = (len + sh.unroll - 1) / sh.unroll * sh.unroll;
-            const int64_t n = (bz + len - 1) / len;
-            const int64_t rounds = (nt * n + cap - 1) / cap;
-            const int64_t cost = rounds * (len + fill);
-            if (best.cost < 0 || cost < best.cost) best = Chunks{len, n, cost};
-        }
-        return best;
-    };
-    const Chunks uni = best_chunks(tiles);
-    g.a_nwg = g.a_tiles = g.a_len = 0;
-    g.chunk_len = (int)uni.len;
-    g.nchunks = (int)uni.nch;
-    g.nwg = (int)(tiles * uni.nch);
-    // Mixed chunking, for more tiles than one round holds with a remainder:
-    // group A streams the first whole rounds of tiles through all of z in
-    // one chunk each, group B splits only the remaining tiles into chunks
-    // (e.g. 304 tiles on 256 compute units: 256 whole columns, then 48
-    // columns in 5 chunks, instead of every column in 5 chunks).  Within
-    // each group neighbouring tiles still stream the same planes together.
-    const int64_t full = tiles / cap * cap, rest = tiles - full;
-    if (full > 0 && rest > 0) {
-        const int64_t blen = (bz + sh.unroll - 1) / sh.unroll * sh.unroll;
-        const Chunks b = best_chunks(rest);
-        const int64_t cost = full / cap * (blen + fill) + b.cost;
-        if (cost < uni.cost) {
-            g.a_nwg = (int)full;
-            g.a_tiles = (int)full;
-            g.a_len = (int)bz;
-            g.chunk_len = (int)b.len;
-            g.nchunks = (int)b.nch;
-            g.nwg = (int)(full + rest * b.nch);
-        }
-    }
+    const ChunkPlan p = plan_chunks(bz, tiles, sh.unroll, 4 * R, cap, sh.prologue + 4);
+    g.nwg = (int)p.nwg;
+    g.chunk_len = (int)p.chunk_len;
+    g.nchunks = (int)p.nchunks;
+    g.a_nwg = (int)p.a_nwg;
+    g.a_tiles = (int)p.a_tiles;
+    g.a_len = (int)p.a_len;
     return g;
 }
 

@@ -47,10 +47,9 @@
 
 #include "internal.h"
 #include "stencil3d.h"
+#include "work_plan.h"
 
 namespace st {
-
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 
 template <typename T>
 struct StarArgs {
@@ -118,15 +117,6 @@ constexpr int lds_pitch(int need, int vx) {
     int p = round_up(need, vx);
     while ((p * (int)sizeof(T)) % 16 != 0 || ((p * (int)sizeof(T)) / 16) % 2 == 0) p += vx;
     return p;
-}
-
-// Bijection from the hardware workgroup id to a logical tile id such that
-// XCD k (which receives ids k, k+8, k+16, ...) owns one contiguous range of
-// logical ids.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-    const int q = n / kXcds, r = n % kXcds;
-    const int xcd = b % kXcds, i = b / kXcds;
-    return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
 }
 
 template <int B, int E, typename F>
@@ -312,33 +302,18 @@ star2p5d_kernel(StarArgs<T> a) {
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny;
-    // workgroup group (A: ids below ga_nwg), remapped within the group so
-    // that each XCD sweeps a contiguous band of the group's tiles
-    const bool ga = (int)blockIdx.x < a.ga_nwg;
+    // this workgroup's tile and z chunk (group A / B, XCD-remapped within
+    // each group)
     const int ntile = a.tiles_x * a.tiles_y;
-    const int gfirst = ga ? 0 : a.ga_nwg;            // first workgroup id of the group
-    const int gnwg = ga ? a.ga_nwg : a.nwg - a.ga_nwg;
-    const int gt0 = ga ? 0 : a.ga_tiles;             // first tile of the group
-    const int gtiles = ga ? a.ga_tiles : ntile - a.ga_tiles;
-    const int glen = ga ? a.ga_len : a.chunk_len;
-    const int gid = (int)blockIdx.x - gfirst;
-    const int wg = C::XCD ? xcd_remap(gid, gnwg) : gid;
-    const int nchunks = gnwg / gtiles;
-    int chunk, trem;
-    if (C::CMAJ) {
-        chunk = wg / gtiles;
-        trem = wg - chunk * gtiles;
-    } else {
-        trem = wg / nchunks;
-        chunk = wg - trem * nchunks;
-    }
-    trem += gt0;
-    const int tyi = trem / a.tiles_x;
-    const int txi = trem - tyi * a.tiles_x;
+    const WgWork w = wg_work((int)blockIdx.x, a.nwg, ntile, a.ga_nwg, a.ga_tiles, a.ga_len,
+                             a.chunk_len, C::XCD, C::CMAJ);
+    const int chunk = w.chunk;
+    const int tyi = w.tile / a.tiles_x;
+    const int txi = w.tile - tyi * a.tiles_x;
     const int gx0 = a.bx0 + txi * TX;
     const int gy0 = a.by0 + tyi * TY;
-    const int zs = a.bz0 + chunk * glen;
-    const int ze = min(zs + glen, a.bz1);
+    const int zs = a.bz0 + w.zoff;
+    const int ze = min(zs + w.len, a.bz1);
     const int n = ze - zs;                      // planes of this chunk
     // Odd chunks stream downwards, so two neighbouring chunks reach their
     // shared boundary planes at the same time (both at their start, or both

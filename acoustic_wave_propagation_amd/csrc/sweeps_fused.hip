@@ -50,45 +50,15 @@ FusedPlan plan_fused(const stencil3d_desc &d, int cus) {
     p.tiles_y = (int)((iy + FS::TY - 1) / FS::TY);
     p.threads = C::NT;
     const int64_t tiles = (int64_t)p.tiles_x * p.tiles_y;
-    // one workgroup per compute unit (LDS and registers); minimise
-    // rounds * (chunk + pipeline fill), as for the single-sweep kernel,
-    // with the same mixed chunking when the tiles outnumber one round
-    const int64_t cap = cus > 0 ? cus : 256;
-    const int64_t fill = FS::PROLOGUE + 4;
-    struct Chunks {
-        int64_t len, nch, cost;
-    };
-    auto best_chunks = [&](int64_t nt) {
-        int64_t maxch = iz / (4 * NS) > 0 ? iz / (4 * NS) : 1;
-        const int64_t enough = 8 * cap / (nt > 0 ? nt : 1) + 1;  // see plan_geometry
-        if (maxch > enough) maxch = enough;
-        Chunks best{iz, 1, -1};
-        for (int64_t nch = 1; nch <= maxch; ++nch) {
-            int64_t len = (iz + nch - 1) / nch;
-            len = (len + FS::U - 1) / FS::U * FS::U;
-            const int64_t n = (iz + len - 1) / len;
-            const int64_t rounds = (nt * n + cap - 1) / cap;
-            const int64_t cost = rounds * (len + fill);
-            if (best.cost < 0 || cost < best.cost) best = Chunks{len, n, cost};
-        }
-        return best;
-    };
-    const Chunks uni = best_chunks(tiles);
-    p.a_nwg = p.a_tiles = p.a_len = 0;
-    p.chunk_len = (int)uni.len;
-    p.nwg = (int)(tiles * uni.nch);
-    const int64_t full = tiles / cap * cap, rest = tiles - full;
-    if (full > 0 && rest > 0) {
-        const int64_t blen = (iz + FS::U - 1) / FS::U * FS::U;
-        const Chunks b = best_chunks(rest);
-        if (full / cap * (blen + fill) + b.cost < uni.cost) {
-            p.a_nwg = (int)full;
-            p.a_tiles = (int)full;
-            p.a_len = (int)iz;
-            p.chunk_len = (int)b.len;
-            p.nwg = (int)(full + rest * b.nch);
-        }
-    }
+    // one workgroup per compute unit (LDS and registers); chunked as for
+    // the single-sweep kernel, no shorter than about 4 planes per sweep
+    const ChunkPlan c = plan_chunks(iz, tiles, FS::U, 4 * NS, cus > 0 ? cus : 256,
+                                    FS::PROLOGUE + 4);
+    p.nwg = (int)c.nwg;
+    p.chunk_len = (int)c.chunk_len;
+    p.a_nwg = (int)c.a_nwg;
+    p.a_tiles = (int)c.a_tiles;
+    p.a_len = (int)c.a_len;
     return p;
 }
 

@@ -82,22 +82,15 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny, nz = a.nz;
-    // workgroup groups as in star2p5d_kernel: group A (ids below ga_nwg)
-    // streams tiles [0, ga_tiles) in chunks of ga_len planes, the rest the
-    // other tiles in chunks of chunk_len; each group XCD-remapped on its own
-    const bool ga = (int)blockIdx.x < a.ga_nwg;
+    // this workgroup's tile and z chunk, mapped as for star2p5d_kernel
+    // (chunk-major, XCD-remapped within each group)
     const int ntile = a.tiles_x * a.tiles_y;
-    const int gfirst = ga ? 0 : a.ga_nwg;
-    const int gnwg = ga ? a.ga_nwg : a.nwg - a.ga_nwg;
-    const int gt0 = ga ? 0 : a.ga_tiles;
-    const int gtiles = ga ? a.ga_tiles : ntile - a.ga_tiles;
-    const int glen = ga ? a.ga_len : a.chunk_len;
-    const int wg = xcd_remap((int)blockIdx.x - gfirst, gnwg);
-    const int chunk = wg / gtiles, trem = wg - chunk * gtiles + gt0;
-    const int tyi = trem / a.tiles_x, txi = trem - tyi * a.tiles_x;
+    const WgWork w = wg_work((int)blockIdx.x, a.nwg, ntile, a.ga_nwg, a.ga_tiles, a.ga_len,
+                             a.chunk_len, true, true);
+    const int tyi = w.tile / a.tiles_x, txi = w.tile - tyi * a.tiles_x;
     const int gx0 = R + txi * TX, gy0 = R + tyi * TY;  // output tile origin
-    const int zs = R + chunk * glen;
-    const int ze = min(zs + glen, nz - R);
+    const int zs = R + w.zoff;
+    const int ze = min(zs + w.len, nz - R);
     const int n = ze - zs;                    // output planes of this chunk
     const int nsteps = n + FILL;
     const int q0 = zs - (NS - 1) * R;         // plane of stage 1 at step 0

@@ -29,6 +29,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "star2p5d_kernel.h"),
+                  os.path.join(PKG, "csrc", "work_plan.h"),
                   os.path.join(PKG, "csrc", "star2p5d.hip")]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
