@@ -22,7 +22,7 @@ HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
 EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
            "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
            "wave_step", "wave_step_pml", "wave_add_source", "wave_run",
-           "wave_run_pml")
+           "wave_run_pml", "wave_run_blocked")
 
 
 class Desc(ctypes.Structure):
@@ -76,6 +76,9 @@ def lib():
                                ctypes.POINTER(ctypes.c_double), vp]),
             "wave_run_pml": (i32, [D, vp, vp, vp, vp, dp, dp, i32, i64, i64,
                                    i64, ctypes.POINTER(ctypes.c_double), vp]),
+            "wave_run_blocked": (i32, [D, vp, vp, vp, vp, vp, vp, dp, dp, i32,
+                                       i64, i64, i64,
+                                       ctypes.POINTER(ctypes.c_double), vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -195,17 +198,21 @@ def wave_add_source(d: Desc, u, ix: int, iy: int, iz: int, value: float,
     return u
 
 
+def _trace(src_trace, n: int):
+    if src_trace is None:
+        return None
+    vals = [float(v) for v in src_trace]
+    if len(vals) < n:
+        raise ValueError("src_trace needs %d values" % n)
+    return (ctypes.c_double * max(n, 1))(*vals[:max(n, 1)])
+
+
 def wave_run(d: Desc, u_prev, u, vel2, eta, dt: float, h: float, nsteps: int,
              src=(0, 0, 0), src_trace=None, stream=None, pml: bool = False):
     """Two-buffer leapfrog; returns (older, newest) tensors.  ``pml``
     calls ``wave_run_pml`` (the PML kernel's step)."""
     n = int(nsteps)
-    tr = None
-    if src_trace is not None:
-        vals = [float(v) for v in src_trace]
-        if len(vals) < n:
-            raise ValueError("src_trace needs %d values" % n)
-        tr = (ctypes.c_double * max(n, 1))(*vals[:max(n, 1)])
+    tr = _trace(src_trace, n)
     ix, iy, iz = src
     name = "wave_run_pml" if pml else "wave_run"
     _check(getattr(lib(), name)(
@@ -220,3 +227,21 @@ def wave_run_pml(d: Desc, u_prev, u, vel2, eta, dt: float, h: float,
     """wave_run with the PML kernel's step; returns (older, newest)."""
     return wave_run(d, u_prev, u, vel2, eta, dt, h, nsteps, src, src_trace,
                     stream, pml=True)
+
+
+def wave_run_blocked(d: Desc, u_prev, u, work0, work1, vel2, eta, dt: float,
+                     h: float, nsteps: int, src=(0, 0, 0), src_trace=None,
+                     stream=None):
+    """Time-blocked leapfrog over four buffers (two steps per pass where the
+    library has the kernel); returns (older, newest): level k of the field
+    lives in (u_prev, u, work0, work1)[k % 4]."""
+    n = int(nsteps)
+    tr = _trace(src_trace, n)
+    ix, iy, iz = src
+    _check(lib().wave_run_blocked(
+        ctypes.byref(d), _ptr(u_prev, d, "u_prev"), _ptr(u, d, "u"),
+        _ptr(work0, d, "work0"), _ptr(work1, d, "work1"), _ptr(vel2, d, "vel2"),
+        _ptr(eta, d, "eta"), float(dt), float(h), n, ix, iy, iz, tr,
+        _stream(u, stream)), "wave_run_blocked")
+    b = (u_prev, u, work0, work1)
+    return b[n % 4], b[(n + 1) % 4]

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstencil3d.so")
-SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "validate.cpp", "api.cpp"]
+SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "wave2.hip", "validate.cpp", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -214,4 +214,39 @@ ST_EXPORT int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u, const
                       stream, true);
 }
 
+// Time-blocked leapfrog over four buffers: u^k lives in b[k mod 4], so two
+// steps at a time read (u^{k-1}, u^k) and write (u^{k+1}, u^{k+2}) into
+// the other two buffers, which no tile of the pass reads.
+ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
+                               void *work1, const void *vel2, const void *eta, double dt,
+                               double h, int nsteps, int64_t src_x, int64_t src_y,
+                               int64_t src_z, const double *src_trace, void *stream) {
+    int st = st::check::blocked_args(d, u_prev, u, work0, work1, vel2, eta, dt, h, nsteps, src_x,
+                                     src_y, src_z, src_trace);
+    if (st) return st;
+    const int cus = current_cus(&st);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const double wscale = (dt * dt) / (h * h);
+    const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
+    void *b[4] = {u_prev, u, work0, work1};
+    const bool two = st::wave2_available(*d);
+    for (int n = 0; n < nsteps;) {
+        void *p = b[n % 4], *c = b[(n + 1) % 4], *o1 = b[(n + 2) % 4], *o2 = b[(n + 3) % 4];
+        if (two && nsteps - n >= 2) {
+            const st::Wave2Source src{src_trace != nullptr, src_x, src_y, src_z,
+                                      src_trace ? src_trace[n] : 0.0,
+                                      src_trace ? src_trace[n + 1] : 0.0};
+            st = st::launch_wave2(*d, p, c, o1, o2, vel2, eta, wscale, src, cus, s);
+            n += 2;
+        } else {
+            st = launch_wave(*d, c, o1, p, vel2, eta, wscale, cus, s, false);
+            if (!st && src_trace) st = st::launch_add_source(*d, o1, idx, src_trace[n], s);
+            n += 1;
+        }
+        if (st) return st;
+    }
+    return ST_OK;
+}
+
 }  // extern "C"

@@ -156,13 +156,29 @@ int run_args(const stencil3d_desc *d, const void *u_prev, const void *u, const v
              int64_t sz, const double *src_trace) {
     int st = wave_args(d, u_prev, u, u_prev, vel2, eta, dt, h);
     if (st) return st;
-    if (overlap(d, u_prev, u)) return ST_ERR_ALIAS;
+    // both buffers are written in turn
+    if (overlap(d, u_prev, u) || overlap(d, u, vel2) || overlap(d, u, eta)) return ST_ERR_ALIAS;
     if (nsteps < 0) return ST_ERR_ARG;
     if (src_trace) {
         if (!interior_index(d, sx, sy, sz)) return ST_ERR_BAD_INDEX;
         for (int n = 0; n < nsteps; ++n)
             if (!isfinite(src_trace[n])) return ST_ERR_ARG;
     }
+    return ST_OK;
+}
+
+int blocked_args(const stencil3d_desc *d, const void *u_prev, const void *u, const void *work0,
+                 const void *work1, const void *vel2, const void *eta, double dt, double h,
+                 int nsteps, int64_t sx, int64_t sy, int64_t sz, const double *src_trace) {
+    int st = run_args(d, u_prev, u, vel2, eta, dt, h, nsteps, sx, sy, sz, src_trace);
+    if (st) return st;
+    if ((st = pointer(d, work0)) || (st = pointer(d, work1))) return st;
+    // all four u buffers are written in turn: no overlap among them or with
+    // vel2 and eta
+    const void *others[] = {u_prev, u, vel2, eta};
+    for (const void *o : others)
+        if (overlap(d, work0, o) || overlap(d, work1, o)) return ST_ERR_ALIAS;
+    if (overlap(d, work0, work1)) return ST_ERR_ALIAS;
     return ST_OK;
 }
 

@@ -29,6 +29,9 @@ int source_args(const stencil3d_desc *d, const void *u, int64_t ix, int64_t iy, 
 int run_args(const stencil3d_desc *d, const void *u_prev, const void *u, const void *vel2,
              const void *eta, double dt, double h, int nsteps, int64_t sx, int64_t sy,
              int64_t sz, const double *src_trace);
+int blocked_args(const stencil3d_desc *d, const void *u_prev, const void *u, const void *work0,
+                 const void *work1, const void *vel2, const void *eta, double dt, double h,
+                 int nsteps, int64_t sx, int64_t sy, int64_t sz, const double *src_trace);
 
 }  // namespace check
 }  // namespace st

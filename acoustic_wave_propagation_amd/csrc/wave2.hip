@@ -1,0 +1,61 @@
+// wave2.hip -- instantiates and launches the two-step wave kernel of
+// wave2_kernel.h (temporal blocking of the leapfrog).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "wave2_kernel.h"
+
+namespace st {
+namespace {
+
+// R = 4 (the 25-point wave step), fp32.  One 512-thread workgroup per
+// compute unit, 4 x 1 points per thread: the u^n window and the u^{n+1}
+// ring take ~2 x 40 registers, 162 in all, so two waves run per SIMD (with
+// 4 x 2 points per thread and 256 threads, one: 1.1x slower per pass).  The
+// LDS holds R+1 stage-1 tiles, the stage-2 tile and the vel2/eta ring
+// (151 KB).  The extended tile is 64 x 32, the output tile 56 x 24.
+using Wave2F32 = Wave2Cfg<4, 1, 16, 32, 2>;
+
+template <typename T, int R, class C>
+int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
+             const void *vel2, const void *eta, double wscale, const Wave2Source &src, int cus,
+             hipStream_t s) {
+    using S = Wave2Shape<R, C>;
+    const int64_t ix = d.nx - 2 * R, iy = d.ny - 2 * R, iz = d.nz - 2 * R;
+    const int tiles_x = (int)((ix + S::TX - 1) / S::TX);
+    const int tiles_y = (int)((iy + S::TY - 1) / S::TY);
+    const int64_t tiles = (int64_t)tiles_x * tiles_y;
+    // chunks no shorter than about 8R planes: each costs 2R fill steps and
+    // re-reads 4R planes of u^n
+    const ChunkPlan p = plan_chunks(iz, tiles, S::U, 8 * R, cus > 0 ? cus : 256, S::PROLOGUE + 4);
+    Wave2Args<T> g;
+    g.s = make_args<T, R>(d, interior_box(d), u, out1, u_prev, vel2, eta, wscale, tiles_x, tiles_y,
+                          (int)p.chunk_len, (int)p.nwg);
+    g.s.ga_nwg = (int)p.a_nwg;
+    g.s.ga_tiles = (int)p.a_tiles;
+    g.s.ga_len = (int)p.a_len;
+    g.out2 = static_cast<T *>(out2);
+    g.sx = src.on ? (int32_t)src.x : -1;
+    g.sy = src.on ? (int32_t)src.y : -1;
+    g.sz = src.on ? (int32_t)src.z : -1;
+    g.s0 = (T)src.v0;
+    g.s1 = (T)src.v1;
+    hipLaunchKernelGGL((wave2_kernel<T, R, C>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s, g);
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
+}
+
+}  // namespace
+
+bool wave2_available(const stencil3d_desc &d) { return d.radius == 4 && d.dtype == ST_F32; }
+
+int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
+                 void *out2, const void *vel2, const void *eta, double wscale,
+                 const Wave2Source &src, int cus, hipStream_t stream) {
+    if (!wave2_available(d)) return ST_ERR_ARG;
+    return launch_t<float, 4, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
+                                        stream);
+}
+
+}  // namespace st

@@ -1,0 +1,420 @@
+// wave2_kernel.h -- two leapfrog steps of the acoustic wave update in one
+// pass over HBM (temporal blocking of the wave step).
+//
+// "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
+// way to reuse each plane across time steps.  This kernel pipelines two
+// steps in z over overlapped tiles in x and y:
+//
+//  * A workgroup owns an output tile T of TX x TY points and a z chunk; its
+//    threads cover the extended tile E = T grown by R points on each side
+//    (x in whole 16-byte groups).
+//  * Stage 1, at plane q1 = q0 + k in z step k, computes step n+1 on all of
+//    E: u^n's z neighbours from a register window (as in star2p5d_kernel),
+//    its in-plane neighbours from an LDS tile of E plus an R-wide halo ring.
+//    The ring of each plane is loaded in the step in which the neighbouring
+//    tiles load that plane as their window's leading plane (so it comes from
+//    L2) and staged into one of R+D tile sets until its step comes.
+//  * Stage 2, at plane q2 = q1 - R, computes step n+2 on E (exact on T):
+//    z neighbours of u^{n+1} from a register ring that stage 1 filled over
+//    the last 2R steps, in-plane neighbours from a second LDS tile.  u^n at
+//    q2 is still in stage 1's window; vel2 and eta at q2 were loaded by
+//    stage 1 R steps earlier and wait in an LDS ring private to each thread.
+//  * Stage 1's result is stored on T (u^{n+1}, the next pass's u_prev) and
+//    stage 2's (u^{n+2}).  Both outputs go to buffers no tile reads in the
+//    pass: neighbouring tiles read u^{n-1} and u^n on their extended tiles.
+//  * Points outside the interior keep u^n's value in step n+1 (the halos of
+//    all u fields are the same, zero for the leapfrog), so stage 2 sees the
+//    halo stage 1 would have seen in the next single step.
+//  * The point source of each step is added to that step's result at the
+//    source point, as the run's separate source kernel does.
+//
+// Per point and step the arithmetic is the same sequence of operations as
+// in star2p5d_kernel's wave step, so a pass gives bit-identical results to
+// two single steps (not in place) with their sources.
+#pragma once
+
+#include "star2p5d_kernel.h"
+
+namespace st {
+
+template <typename T>
+struct Wave2Args {
+    StarArgs<T> s;         // in = u^n, u_prev = u^{n-1}, out = u^{n+1}; weights carry dt^2/h^2
+    T *out2;               // u^{n+2}
+    int32_t sx, sy, sz;    // source point (allocated coordinates); sz = -1: no source
+    T s0, s1;              // source values of steps n+1 and n+2
+};
+
+// VX x VY points per thread, LX x LY threads covering the extended tile,
+// minimum waves per SIMD the register allocation must allow.
+template <int VX_, int VY_, int LX_, int LY_, int MINW_>
+struct Wave2Cfg {
+    static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, MINW = MINW_;
+    static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
+};
+
+template <int R, class C>
+struct Wave2Shape {
+    static constexpr int D = 1;                      // window prefetch (planes)
+    static constexpr int XE = round_up(R, C::VX);    // columns added per side
+    static constexpr int YE = R;                     // rows added per side
+    static constexpr int TX = C::EX - 2 * XE, TY = C::EY - 2 * YE;  // output tile
+    static constexpr int W0 = 2 * R + 1 + D;         // u^n window slots
+    static constexpr int LB = R + D;                 // stage-1 tile sets
+    static constexpr int U = clcm(clcm(W0, LB), 2);  // z-loop unroll
+    static constexpr int WS = ring_fit(U, 2 * R + 1);  // u^{n+1} ring slots
+    static constexpr int NV = ring_fit(U, R + 1);      // vel2/eta ring slots
+    static constexpr int FILL = 2 * R;               // steps before the first u^{n+2} plane
+    static constexpr int PROLOGUE = FILL + 2 * R + D;
+};
+
+template <typename T, int R, class C>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
+    wave2_kernel(Wave2Args<T> g) {
+    using S = Wave2Shape<R, C>;
+    const StarArgs<T> &a = g.s;
+    constexpr int VX = C::VX, VY = C::VY, LX = C::LX, NT = C::NT, EX = C::EX, EY = C::EY;
+    constexpr int D = S::D, XE = S::XE, YE = S::YE, TX = S::TX, TY = S::TY;
+    constexpr int W0 = S::W0, LB = S::LB, U = S::U, WS = S::WS, NV = S::NV;
+    constexpr int XW = (R + VX - 1) / VX;  // halo groups left and right
+    constexpr int PADL = XW * VX;          // LDS column of extended-tile x = 0
+    constexpr int LP = lds_pitch<T>(PADL + EX + XW * VX, VX);
+    constexpr int LTILE = (EY + 2 * R) * LP;
+    constexpr int NYU = 2 * R * LX;        // halo units above and below E
+    constexpr int NXU = 2 * EY * XW;       // left and right of E
+    constexpr int VBASE = (LB + 1) * LTILE;
+    constexpr int LDUMMY = VBASE + NV * 2 * VY * NT * VX;
+    constexpr uint32_t ES = sizeof(T);
+    constexpr bool DIFF = std::is_same<T, double>::value;
+    static_assert(TX > 0 && TY > 0, "extended tile too small");
+    static_assert(NYU + NXU <= NT, "one halo unit per thread at most");
+    static_assert(WS >= 2 * R + 1 && NV >= R + 1 && U % WS == 0 && U % NV == 0, "rings");
+    static_assert(D == 1, "the halo ring shares the window's leading load");
+
+    __shared__ __align__(16) T lds[LDUMMY + VX];
+    T *const tile2 = lds + LB * LTILE;     // stage 2: u^{n+1} at q2
+
+    const int tid = threadIdx.x;
+    const int nx = a.nx, ny = a.ny, nz = a.nz;
+    const int ntile = a.tiles_x * a.tiles_y;
+    const WgWork w = wg_work((int)blockIdx.x, a.nwg, ntile, a.ga_nwg, a.ga_tiles, a.ga_len,
+                             a.chunk_len, true, true);
+    const int tyi = w.tile / a.tiles_x, txi = w.tile - tyi * a.tiles_x;
+    const int gx0 = R + txi * TX, gy0 = R + tyi * TY;  // output tile origin
+    const int zs = R + w.zoff;
+    const int ze = min(zs + w.len, nz - R);
+    const int n = ze - zs;                    // output planes of this chunk
+    const int nsteps = n + S::FILL;
+    const int q0 = zs - R;                    // stage-1 plane of step 0
+    const int64_t pzb = a.pz * (int64_t)ES;
+    const int64_t totb = pzb * nz;
+    const bool xpart = gx0 + TX > nx - R;     // ragged x edge inside this tile
+
+    // ---- this thread's points: columns ex..ex+VX-1 on rows ey..ey+VY-1 -----
+    const int lx = tid % LX, ly = tid / LX;
+    const int ex0 = gx0 - XE, ey0 = gy0 - YE;  // extended tile origin
+    const int ex = ex0 + lx * VX, ey = ey0 + ly * VY;
+    auto off_of = [&](int y, int x) -> uint32_t {
+        // rows outside the array: kOOB; a group left of x = 0 reads the end
+        // of the previous row (or, before the array, zeros): values only
+        // points outside the interior use
+        return (y >= 0 && y < ny) ? (uint32_t)(((int64_t)y * nx + x) * ES) : kOOB;
+    };
+    uint32_t loff[VY], soff[VY];
+    bool rin[VY];
+    const bool tcol = lx * VX >= XE && lx * VX < XE + TX;
+#pragma unroll
+    for (int j = 0; j < VY; ++j) {
+        const int y = ey + j, ty = ly * VY + j;
+        rin[j] = y >= R && y < ny - R;
+        loff[j] = off_of(y, ex);
+        soff[j] = (tcol && ty >= YE && ty < YE + TY && rin[j] && ex < nx - R) ? loff[j] : kOOB;
+    }
+    bool cin[VX];
+#pragma unroll
+    for (int i = 0; i < VX; ++i) cin[i] = ex + i >= R && ex + i < nx - R;
+    const int nvx = max(0, min(VX, nx - R - ex));  // written columns (ragged x)
+    const int lcol = PADL + lx * VX;
+    const int lrow0 = R + ly * VY;
+    // source point among this thread's points (column and row index, or -1)
+    int si = -1, sj = -1;
+    if (g.sz >= 0 && g.sx >= ex && g.sx < ex + VX && g.sy >= ey && g.sy < ey + VY) {
+        si = g.sx - ex;
+        sj = g.sy - ey;
+    }
+
+    // ---- halo ring unit of this thread (stage-1 tile) ------------------------
+    uint32_t h_off = kOOB;
+    int h_l = -1;
+    if (tid < NYU) {
+        const int rsel = tid / LX, gi = tid - rsel * LX;
+        const int gy = rsel < R ? ey0 - R + rsel : ey0 + EY + (rsel - R);
+        h_off = off_of(gy, ex0 + gi * VX);
+        h_l = (rsel < R ? rsel : EY + rsel) * LP + PADL + gi * VX;
+    } else if (tid < NYU + NXU) {
+        const int xu = tid - NYU;
+        const int side = xu / (EY * XW), rem = xu - side * (EY * XW);
+        const int row = rem / XW, c = rem - row * XW;
+        h_off = off_of(ey0 + row, side ? ex0 + EX + c * VX : ex0 - PADL + c * VX);
+        h_l = (R + row) * LP + (side ? PADL + EX : 0) + c * VX;
+    }
+    T *const h_dst = h_l >= 0 ? lds + h_l : lds + LDUMMY;  // + set * LTILE (inactive: sink)
+    const int h_set_stride = h_l >= 0 ? LTILE : 0;
+    // this thread's slot of the vel2/eta ring (field f, row j, ring slot s)
+    auto vring = [&](int s, int f, int j) { return lds + VBASE + (((s * 2 + f) * VY + j) * NT + tid) * VX; };
+
+    T w0[W0][VY][VX];  // u^n, planes q1-R .. q1+R plus D in flight
+    T ws[WS][VY][VX];  // u^{n+1}, the last WS stage-1 planes
+    T up[VY][VX], v2[VY][VX], et[VY][VX];  // u^{n-1}, vel2, eta at q1
+    T hs[2][VX];       // halo unit in flight
+#pragma unroll
+    for (int p = 0; p < WS; ++p)
+#pragma unroll
+        for (int j = 0; j < VY; ++j)
+#pragma unroll
+            for (int i = 0; i < VX; ++i) ws[p][j][i] = T(0);
+
+    auto prsrc = [&](const T *base, int q, bool need) {
+        need = need && q >= 0 && q < nz;
+        return plane_rsrc((const char *)base + (int64_t)q * pzb, totb - (int64_t)q * pzb, need);
+    };
+    // u^n planes this chunk depends on
+    auto u_need = [&](int q) { return q >= zs - 2 * R && q < ze + 2 * R; };
+
+    // prologue: window slot s holds the plane at step offset s - R; halo
+    // rings of steps 0..LB-2 go straight to their tile sets, step LB-1's
+    // waits in hs[1] (stored in step 0)
+    static_for<0, 2 * R + D>([&](auto sc) {
+        constexpr int sl = decltype(sc)::value;
+        const int q = q0 + sl - R;
+        const rsrc_t r = prsrc(a.in, q, u_need(q));
+#pragma unroll
+        for (int j = 0; j < VY; ++j) bload<T, VX>(r, loff[j], w0[sl][j]);
+    });
+    {
+        T hp[LB - 1][VX];
+        static_for<0, LB - 1>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            bload<T, VX>(prsrc(a.in, q0 + h, u_need(q0 + h)), h_off, hp[h]);
+        });
+        bload<T, VX>(prsrc(a.in, q0 + LB - 1, u_need(q0 + LB - 1)), h_off, hs[1]);
+        static_for<0, LB - 1>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            lds_store_group<T, VX>(h_dst + h * h_set_stride, hp[h]);
+        });
+    }
+
+    // in-plane and z sums of one stage: the same operations, in the same
+    // order, as star2p5d_kernel; zv(dz, j, i) is the stage input at plane
+    // offset dz of the thread's own point (j, i)
+    auto laplacian = [&](const T *tile, auto zv, T (&acc_out)[VY][VX]) {
+        T xs[VY][VX + 2 * R];  // row segment, columns ex-R .. ex+VX+R-1
+        T lg[VY][VX], rg[VY][VX];
+#pragma unroll
+        for (int j = 0; j < VY; ++j) {
+            const T *row = tile + (lrow0 + j) * LP + lcol;
+            if constexpr (R <= VX) {
+                lds_load_group<T, VX>(row - VX, lg[j]);
+                lds_load_group<T, VX>(row + VX, rg[j]);
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    xs[j][m] = lg[j][VX - R + m];
+                    xs[j][R + VX + m] = rg[j][m];
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    xs[j][m] = row[m - R];
+                    xs[j][R + VX + m] = row[VX + m];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < VX; ++i) xs[j][R + i] = zv(std::integral_constant<int, 0>{}, j, i);
+        }
+        T ys[2 * R][VX];  // rows ey-R..ey-1 and ey+VY..ey+VY+R-1
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < VX; ++i) {
+                ys[r][i] = tile[(lrow0 - R + r) * LP + lcol + i];
+                ys[R + r][i] = tile[(lrow0 + VY + r) * LP + lcol + i];
+            }
+#pragma unroll
+        for (int j = 0; j < VY; ++j)
+#pragma unroll
+            for (int i = 0; i < VX; ++i) {
+                const T ctr = zv(std::integral_constant<int, 0>{}, j, i);
+                T acc = (DIFF ? a.ccd : a.cc) * ctr;
+                static_for<1, R + 1>([&](auto kzc) {
+                    constexpr int kz = decltype(kzc)::value;
+                    const T zm = zv(std::integral_constant<int, -kz>{}, j, i);
+                    const T zp = zv(std::integral_constant<int, kz>{}, j, i);
+                    const T xm = xs[j][R + i - kz], xp = xs[j][R + i + kz];
+                    const int qm = j - kz, qp = j + kz;
+                    const T ym = qm < 0 ? ys[R + qm][i]
+                                        : zv(std::integral_constant<int, 0>{}, qm < 0 ? 0 : qm, i);
+                    const T yp = qp >= VY ? ys[R + qp - VY][i]
+                                          : zv(std::integral_constant<int, 0>{}, qp >= VY ? 0 : qp, i);
+                    if constexpr (DIFF) {
+                        acc = fma(a.cz[kz - 1], (zm - ctr) + (zp - ctr), acc);
+                        acc = fma(a.cy[kz - 1], (ym - ctr) + (yp - ctr), acc);
+                        acc = fma(a.cx[kz - 1], (xm - ctr) + (xp - ctr), acc);
+                    } else {
+                        acc = fma(a.cz[kz - 1], zm + zp, acc);
+                        acc = fma(a.cy[kz - 1], ym + yp, acc);
+                        acc = fma(a.cx[kz - 1], xm + xp, acc);
+                    }
+                });
+                acc_out[j][i] = acc;
+            }
+        if constexpr (R < VX) {
+#pragma unroll
+            for (int j = 0; j < VY; ++j)
+#pragma unroll
+                for (int i = 0; i < VX; ++i) asm volatile("" ::"v"(lg[j][i]), "v"(rg[j][i]));
+        }
+    };
+    // T's interior points of plane q (ragged x: whole groups in one access,
+    // the partial group of a row element by element)
+    auto store = [&](T *base, int q, bool st, const T (&res)[VY][VX]) {
+        const rsrc_t ro = prsrc(base, q, st);
+        if (!xpart) {
+#pragma unroll
+            for (int j = 0; j < VY; ++j) bstore<T, VX>(ro, soff[j], res[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VY; ++j) {
+                bstore<T, VX>(ro, nvx == VX ? soff[j] : kOOB, res[j]);
+#pragma unroll
+                for (int i = 0; i < VX - 1; ++i)
+                    bstore1<T>(ro, i < nvx && nvx < VX ? soff[j] + i * ES : kOOB, res[j][i]);
+            }
+        }
+    };
+
+    for (int k0 = 0; k0 < nsteps; k0 += U) {
+        static_for<0, U>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr int CS = (kk + R) % W0;            // window slot of plane q1
+            constexpr int LEAD = (kk + 2 * R + D) % W0;  // slot the prefetch fills
+            constexpr int C2 = kk % W0;                  // window slot of plane q2 = q1 - R
+            constexpr int SET = kk % LB;                 // stage-1 tile set of this step
+            constexpr int HSET = (kk + LB - 1) % LB;     // set whose halo is stored now
+            constexpr int HLD = kk % 2, HST = (kk + 1) % 2;
+            constexpr int WC = kk % WS;                  // ring slot of plane q1
+            constexpr int WC2 = ((kk - R) % WS + WS) % WS;  // ring slot of plane q2
+            constexpr int VW = kk % NV, VR = ((kk - R) % NV + NV) % NV;
+            const int k = k0 + kk;
+            const int q1 = q0 + k, q2 = q1 - R;
+            const bool in1 = q1 >= R && q1 < nz - R;
+
+            // 1. stage 1's epilogue fields of plane q1 first (used at the
+            //    end of this step), then the window's leading plane and the
+            //    halo ring of step k + LB -- the same plane (D = 1)
+            {
+                const bool need = in1 && k < nsteps;
+                const rsrc_t rp = prsrc(a.u_prev, q1, need), rv = prsrc(a.vel2, q1, need),
+                             re = prsrc(a.eta, q1, need);
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    bload<T, VX>(rp, loff[j], up[j]);
+                    bload<T, VX>(rv, loff[j], v2[j]);
+                    bload<T, VX>(re, loff[j], et[j]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const int q = q1 + R + D;
+                const rsrc_t r = prsrc(a.in, q, u_need(q));
+#pragma unroll
+                for (int j = 0; j < VY; ++j) bload<T, VX>(r, loff[j], w0[LEAD][j]);
+                bload<T, VX>(r, h_off, hs[HLD]);
+            }
+
+            // 2. centre rows of both tiles (the stage-2 tile has one set:
+            //    wait until every thread has read last step's)
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < VY; ++j) {
+                lds_store_group<T, VX>(lds + SET * LTILE + (lrow0 + j) * LP + lcol, w0[CS][j]);
+                lds_store_group<T, VX>(tile2 + (lrow0 + j) * LP + lcol, ws[WC2][j]);
+            }
+            __syncthreads();
+            // halo ring of step k + LB - 1 into its set, last read in step k-1
+            lds_store_group<T, VX>(h_dst + HSET * h_set_stride, hs[HST]);
+
+            // 3. stage 1: step n+1 at plane q1 on E
+            {
+                T acc[VY][VX], res[VY][VX];
+                laplacian(lds + SET * LTILE,
+                          [&](auto dzc, int j, int i) -> T {
+                              constexpr int dz = decltype(dzc)::value;
+                              return w0[((CS + dz) % W0 + W0) % W0][j][i];
+                          },
+                          acc);
+#pragma unroll
+                for (int j = 0; j < VY; ++j)
+#pragma unroll
+                    for (int i = 0; i < VX; ++i) {
+                        const T ctr = w0[CS][j][i];
+                        const T e = et[j][i];
+                        const T u1 = (T(2) * ctr - (T(1) - e) * up[j][i] + v2[j][i] * acc[j][i]) /
+                                     (T(1) + e);
+                        res[j][i] = (in1 && rin[j] && cin[i]) ? u1 : ctr;
+                    }
+                if (q1 == g.sz && sj >= 0) {
+#pragma unroll
+                    for (int j = 0; j < VY; ++j)
+#pragma unroll
+                        for (int i = 0; i < VX; ++i)
+                            if (j == sj && i == si) res[j][i] += g.s0;
+                }
+#pragma unroll
+                for (int j = 0; j < VY; ++j)
+#pragma unroll
+                    for (int i = 0; i < VX; ++i) ws[WC][j][i] = res[j][i];
+                store(a.out, q1, k >= R && k < n + R, res);
+            }
+
+            // 4. stage 2: step n+2 at plane q2 on E (exact on T)
+            {
+                T v2b[VY][VX], etb[VY][VX], acc[VY][VX], res[VY][VX];
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    lds_load_group<T, VX>(vring(VR, 0, j), v2b[j]);
+                    lds_load_group<T, VX>(vring(VR, 1, j), etb[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    lds_store_group<T, VX>(vring(VW, 0, j), v2[j]);
+                    lds_store_group<T, VX>(vring(VW, 1, j), et[j]);
+                }
+                laplacian(tile2,
+                          [&](auto dzc, int j, int i) -> T {
+                              constexpr int dz = decltype(dzc)::value;
+                              return ws[((WC2 + dz) % WS + WS) % WS][j][i];
+                          },
+                          acc);
+#pragma unroll
+                for (int j = 0; j < VY; ++j)
+#pragma unroll
+                    for (int i = 0; i < VX; ++i) {
+                        const T ctr = ws[WC2][j][i];
+                        const T e = etb[j][i];
+                        res[j][i] = (T(2) * ctr - (T(1) - e) * w0[C2][j][i] + v2b[j][i] * acc[j][i]) /
+                                    (T(1) + e);
+                    }
+                if (q2 == g.sz && sj >= 0) {
+#pragma unroll
+                    for (int j = 0; j < VY; ++j)
+#pragma unroll
+                        for (int i = 0; i < VX; ++i)
+                            if (j == sj && i == si) res[j][i] += g.s1;
+                }
+                store(g.out2, q2, k >= 2 * R && k < n + 2 * R, res);
+            }
+        });
+    }
+}
+
+}  // namespace st

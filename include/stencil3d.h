@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define ST_ABI_VERSION 3
+#define ST_ABI_VERSION 4
 #define ST_MAX_R 4
 
 /* element types */
@@ -233,6 +233,39 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
                  const void *vel2, const void *eta, double dt, double h,
                  int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
                  const double *src_trace, void *stream);
+
+/*
+ * Time-blocked leapfrog: the wave_step time loop of wave_run, two steps per
+ * pass over memory where the library has a two-step kernel (R = 4, ST_F32;
+ * "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
+ * way to reuse planes across time steps), single steps otherwise and for
+ * an odd last step.  Four caller-owned fields of d's shape rotate: with
+ * b = {u_prev, u, work0, work1}, the field of time level k (u_prev holds
+ * level 0, u level 1) lives in b[k mod 4].  A two-step pass reads levels
+ * k-1 and k and writes k+1 and k+2 into the two other buffers (its tiles
+ * overlap, so no level can be overwritten in place).  On return the newest
+ * field (level nsteps + 1) is in b[(nsteps + 1) mod 4] and the one before
+ * it in b[nsteps mod 4]; for a multiple of 4 steps that is u and u_prev,
+ * as wave_run leaves them for an even count.  work0 and work1 are only
+ * written on the interior; their input values are ignored.
+ *
+ * Results are bit-identical to single steps with their sources
+ * (wave_step(b[k-1], b[k] -> b[k+1]), then wave_add_source), with these
+ * conditions: outside the interior all four u fields must hold the same
+ * values (zero, as a leapfrog from zero halos keeps them), since a pass
+ * takes level k+1's halo to be level k's; and d->pml_width is ignored by
+ * the two-step passes (eta is read on the whole interior; the eta-free
+ * inner box of wave_step gives the same values up to the sign of a zero).
+ * Same arguments as wave_run otherwise.  Errors: those of wave_run, plus
+ * ST_ERR_NULL / ST_ERR_ALIGN for work0 or work1 and ST_ERR_ALIAS where any
+ * two of the four u buffers, vel2 and eta overlap (vel2 and eta may be the
+ * same buffer).
+ */
+int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u,
+                     void *work0, void *work1, const void *vel2,
+                     const void *eta, double dt, double h, int nsteps,
+                     int64_t src_x, int64_t src_y, int64_t src_z,
+                     const double *src_trace, void *stream);
 
 #ifdef __cplusplus
 }

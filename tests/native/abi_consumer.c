@@ -46,6 +46,9 @@ static int cpu_checks(void) {
     EXPECT(wave_run_pml(&d, (void *)64, (void *)1000000, (void *)3000000, (void *)4000000,
                         1e-3, 10.0, -1, 10, 10, 10, NULL, NULL) == ST_ERR_ARG);
     EXPECT(wave_add_source(&d, (void *)64, 0, 5, 5, 1.0, NULL) == ST_ERR_BAD_INDEX);
+    EXPECT(wave_run_blocked(&d, (void *)64, (void *)1000000, (void *)2000000, (void *)2000000,
+                            (void *)3000000, (void *)4000000, 1e-3, 10.0, 2, 10, 10, 10, NULL,
+                            NULL) == ST_ERR_ALIAS);
     printf("cpu checks ok\n");
     return 0;
 }

@@ -65,7 +65,7 @@ def test_exports_nothing_else(L):
 
 def test_struct_layout_and_version(L):
     assert ctypes.sizeof(B.Desc) == 168
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
     d = B.desc_init("f32", (10, 11, 12), 4)
     assert d.struct_size == 168 and d.nx == 12 and d.ny == 11 and d.nz == 10
     assert d.pml_width == 0
@@ -195,6 +195,33 @@ def test_entry_points_reject_before_enqueue(L):
                    None) == c["ST_ERR_BAD_INDEX"]
         assert run(by, U[0], U[1], U[0], U[4], 1e-3, 10.0, 3, 10, 10, 10,
                    None, None) == c["ST_ERR_ALIAS"]
+        # u is written in every other step: it must not overlap vel2 or eta
+        assert run(by, U[0], U[1], U[1], U[4], 1e-3, 10.0, 3, 10, 10, 10,
+                   None, None) == c["ST_ERR_ALIAS"]
+        assert run(by, U[0], U[1], U[3], U[1] + 4, 1e-3, 10.0, 3, 10, 10, 10,
+                   None, None) == c["ST_ERR_ALIAS"]
+    # the time-blocked run: four u buffers, all written in turn
+    V = [0x40000000 + i * (n + 4096) for i in range(6)]
+    blk = L.wave_run_blocked
+    ok = (V[0], V[1], V[2], V[3], V[4], V[5])
+
+    def b(*ptrs, nsteps=4, sx=10, trace=None):
+        return blk(by, *ptrs, 1e-3, 10.0, nsteps, sx, 10, 10, trace, None)
+    assert b(*ok, nsteps=-1) == c["ST_ERR_ARG"]
+    assert b(*ok, nsteps=3, trace=tr) == c["ST_ERR_ARG"]
+    assert b(*ok, nsteps=3, sx=2, trace=tr) == c["ST_ERR_BAD_INDEX"]
+    assert b(V[0], V[1], None, V[3], V[4], V[5]) == c["ST_ERR_NULL"]
+    assert b(V[0], V[1], V[2], None, V[4], V[5]) == c["ST_ERR_NULL"]
+    assert b(V[0], V[1], V[2] + 2, V[3], V[4], V[5]) == c["ST_ERR_ALIGN"]
+    for i in range(4):
+        for j in range(6):
+            if i == j or (i, j) == (4, 5):
+                continue
+            p = list(ok)
+            p[i] = p[j] + 4 * (i % 2)  # the same buffer, or a shifted overlap
+            assert b(*p) == c["ST_ERR_ALIAS"], (i, j)
+    # vel2 and eta may share a buffer
+    assert b(V[0], V[1], V[2], V[3], V[4], V[4], nsteps=-1) == c["ST_ERR_ARG"]
 
 
 def test_binding_checks_tensors(L):

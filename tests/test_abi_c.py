@@ -12,7 +12,11 @@ EXE = os.path.join(HERE, "native", "abi_consumer")
 
 
 def _consumer():
-    if not os.path.exists(EXE):
+    # rebuilt when missing or older than its source or the header
+    srcs = [os.path.join(HERE, "native", "abi_consumer.c"),
+            os.path.join(os.path.dirname(HERE), "include", "stencil3d.h")]
+    if not os.path.exists(EXE) or any(os.path.getmtime(s) > os.path.getmtime(EXE)
+                                      for s in srcs):
         runpy.run_path(os.path.join(HERE, "native", "build_consumer.py"),
                        run_name="build_consumer")["build"]()
     return EXE

@@ -1,0 +1,242 @@
+"""The time-blocked leapfrog (wave_run_blocked: two wave steps per pass over
+HBM) on an MI355X.
+
+Its two-step kernel does, per point and step, the operations of the single
+wave step in the same order, so the first bar is bit-identity: every pass
+must equal two single steps (wave_step into fresh buffers, then
+wave_add_source) bit for bit, and a whole run must equal wave_run's.  The
+single step is checked against the CPU oracle elsewhere; the oracle is also
+applied here directly (teacher-forced, fp32 max|err| <= 1e-5 max|ref| per
+step) on small grids.  The u fields' halos are zero, as the entry point
+requires; the work buffers' halos carry a sentinel, which must survive.
+"""
+import numpy as np
+import pytest
+
+from acoustic_wave_propagation_amd import binding as B
+from acoustic_wave_propagation_amd import workloads as wl
+
+from gpu_common import (F32_TOL, SENTINEL, check_close, check_halo_untouched,
+                        device, interior, log, upload, upload_planes)
+
+pytestmark = pytest.mark.gpu
+
+R = 4
+DT, H = 1e-3, 10.0
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    d = device()
+    B.lib()
+    return torch, d
+
+
+def _zero_halo(a):
+    b = np.zeros_like(a)
+    b[R:-R, R:-R, R:-R] = a[R:-R, R:-R, R:-R]
+    return b
+
+
+def _fields(shape, seed, eta_hi=0.1):
+    up = _zero_halo(wl.uniform_planes(shape, seed, -1, 1))
+    uc = _zero_halo(wl.uniform_planes(shape, seed + 1, -1, 1))
+    v2 = wl.uniform_planes(shape, seed + 2, 1.5e3 ** 2, 4.5e3 ** 2)
+    et = wl.uniform_planes(shape, seed + 3, 0.0, eta_hi)
+    return up, uc, v2, et
+
+
+def _sentinel(torch, shape):
+    return torch.full(shape, SENTINEL, dtype=torch.float32, device=device())
+
+
+def _single_steps(torch, d, up, uc, v2, et, nsteps, src, trace):
+    """nsteps single steps into fresh zero-halo buffers, each followed by
+    its source; returns the list of levels 0..nsteps+1 (device tensors)."""
+    lv = [up.clone(), uc.clone()]
+    for n in range(nsteps):
+        nxt = torch.zeros_like(uc)
+        B.wave_step(d, lv[-2], lv[-1], nxt, v2, et, DT, H)
+        if trace is not None:
+            B.wave_add_source(d, nxt, *src, float(np.float32(trace[n])))
+        lv.append(nxt)
+    return lv
+
+
+def _same_interior(got, want, what):
+    g, w = interior(got, R), interior(want, R)
+    bad = int((g != w).sum())
+    if bad:
+        diff = float((g - w).abs().max())
+        raise AssertionError("%s: %d interior points differ (max |diff| %.3e)"
+                             % (what, bad, diff))
+
+
+@pytest.mark.parametrize("shape", [
+    (20, 40, 70),      # one tile in x and y
+    (45, 61, 139),     # ragged tiles in x and y, one z chunk
+    (130, 57, 121),    # several z chunks
+    (17, 33, 9 + 56),  # one output column of tiles, thin z
+])
+def test_one_pass_bit_identical_to_two_steps(torch_dev, shape):
+    torch, _ = torch_dev
+    log("case blocked pass %s" % (shape,))
+    up, uc, v2, et = (upload(a) for a in _fields(shape, 1100 + shape[0]))
+    d = B.desc_init("f32", shape, R)
+    nz, ny, nx = shape
+    src = (nx // 2, ny // 3, nz // 2)
+    trace = [0.25, -0.5]
+    w0, w1 = _sentinel(torch, shape), _sentinel(torch, shape)
+    old, new = B.wave_run_blocked(d, up.clone(), uc.clone(), w0, w1, v2, et,
+                                  DT, H, 2, src, trace)
+    assert old.data_ptr() == w0.data_ptr() and new.data_ptr() == w1.data_ptr()
+    lv = _single_steps(torch, d, up, uc, v2, et, 2, src, trace)
+    torch.cuda.synchronize()
+    _same_interior(w0, lv[2], "step 1 of the pass")
+    _same_interior(w1, lv[3], "step 2 of the pass")
+    for t, name in ((w0, "work0"), (w1, "work1")):
+        check_halo_untouched(t.cpu().numpy(), R, name)
+
+
+def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
+    """Both steps of a pass against the oracle's wave step, teacher-forced,
+    with the sponge-like eta of the real workload replaced by random eta
+    (every point differs)."""
+    torch, _ = torch_dev
+    shape = (37, 53, 131)
+    up, uc, v2, et = _fields(shape, 1200)
+    d = B.desc_init("f32", shape, R)
+    c = list(d.cx[:R + 1])
+    nz, ny, nx = shape
+    src = (60, 30, 20)
+    trace = [0.75, -1.25]
+    w0, w1 = _sentinel(torch, shape), _sentinel(torch, shape)
+    B.wave_run_blocked(d, upload(up), upload(uc), w0, w1, upload(v2),
+                       upload(et), DT, H, 2, src, trace)
+    a = w0.cpu().numpy()
+    ref1 = oracle_mod.wave_step(up, uc, v2, et, R, c, DT, H)
+    ref1[src[2], src[1], src[0]] += np.float32(trace[0])
+    check_close(interior(a, R), interior(ref1, R), F32_TOL, "blocked step 1")
+    a0 = _zero_halo(a)  # the pass takes level 2's halo to be zero, as u's
+    ref2 = oracle_mod.wave_step(uc, a0, v2, et, R, c, DT, H)
+    ref2[src[2], src[1], src[0]] += np.float32(trace[1])
+    check_close(interior(w1.cpu().numpy(), R), interior(ref2, R), F32_TOL,
+                "blocked step 2")
+    assert abs(float(interior(a, R)[src[2] - R, src[1] - R, src[0] - R]) -
+               float(interior(ref1, R)[src[2] - R, src[1] - R, src[0] - R])) \
+        < 1e-4, "source missing in step 1"
+
+
+@pytest.mark.parametrize("nsteps", [0, 1, 2, 3, 4, 5, 7])
+def test_run_equals_wave_run(torch_dev, nsteps):
+    """A whole run, passes plus an odd last single step, against wave_run
+    (two buffers, in place): same bits for both returned levels, and the
+    levels sit in the buffers the rotation rule names."""
+    torch, _ = torch_dev
+    shape = (41, 50, 97)
+    up, uc, v2, et = (upload(a) for a in _fields(shape, 1300 + nsteps))
+    d = B.desc_init("f32", shape, R)
+    src = (40, 20, 17)
+    trace = [0.1 * (k + 1) * (-1) ** k for k in range(max(nsteps, 1))]
+    bufs = [up.clone(), uc.clone(), torch.zeros_like(uc), torch.zeros_like(uc)]
+    old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, nsteps, src, trace)
+    assert old.data_ptr() == bufs[nsteps % 4].data_ptr()
+    assert new.data_ptr() == bufs[(nsteps + 1) % 4].data_ptr()
+    a, b = B.wave_run(d, up.clone(), uc.clone(), v2, et, DT, H, nsteps, src,
+                      trace)
+    torch.cuda.synchronize()
+    _same_interior(old, a, "run of %d steps, older level" % nsteps)
+    _same_interior(new, b, "run of %d steps, newest level" % nsteps)
+
+
+def test_mixed_chunking_and_source_in_the_overlap(torch_dev):
+    """More tiles than compute units (groups A and B of the launch), with the
+    source on a point that several extended tiles compute (next to a tile
+    corner), over two passes."""
+    torch, _ = torch_dev
+    # 56 x 24 output tiles: 10 x 30 = 300 tiles; 200 planes make the
+    # mixed plan (256 whole columns, 44 in chunks) the cheaper one
+    shape = (208, 8 + 24 * 30, 8 + 56 * 10)
+    log("case blocked mixed chunking %s" % (shape,))
+    up, uc, v2, et = (upload(a) for a in _fields(shape, 1400))
+    d = B.desc_init("f32", shape, R)
+    src = (R + 56 * 3, R + 24 * 7 - 1, 13)  # last row of a tile, first column of the next
+    trace = [0.5, -0.25, 0.125, 1.0]
+    bufs = [up.clone(), uc.clone(), torch.zeros_like(uc), torch.zeros_like(uc)]
+    old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4, src, trace)
+    lv = _single_steps(torch, d, up, uc, v2, et, 4, src, trace)
+    torch.cuda.synchronize()
+    _same_interior(old, lv[4], "mixed chunking, level 4")
+    _same_interior(new, lv[5], "mixed chunking, level 5")
+
+
+def test_no_source_and_pml_width(torch_dev):
+    """Without a source trace; with pml_width set the single steps of
+    wave_run split the interior into data regions (eta-free inner box) while
+    the passes read eta everywhere: equal up to the sign of zero."""
+    torch, _ = torch_dev
+    shape = (60, 70, 90)
+    up, uc, v2, _ = _fields(shape, 1500)
+    w = np.zeros(shape, np.float32)
+    w[R:-R, R:-R, R:-R] = 0.1  # eta zero inside a 10-point shell
+    w[R + 10:-R - 10, R + 10:-R - 10, R + 10:-R - 10] = 0.0
+    up, uc, v2, et = upload(up), upload(uc), upload(v2), upload(w)
+    d = B.desc_init("f32", shape, R)
+    d.pml_width = 10
+    bufs = [up.clone(), uc.clone(), torch.zeros_like(uc), torch.zeros_like(uc)]
+    old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, 6)
+    a, b = B.wave_run(d, up.clone(), uc.clone(), v2, et, DT, H, 6)
+    torch.cuda.synchronize()
+    assert torch.equal(interior(old, R), interior(a, R))
+    assert torch.equal(interior(new, R), interior(b, R))
+
+
+def test_blocked_1024_two_steps(torch_dev):
+    """The full 1032^3 workload fields (vel2, 32-point sponge, Ricker source
+    at the centre) in the launch configuration the benchmark times: one pass
+    against two single steps, bit for bit, over the whole interior."""
+    torch, _ = torch_dev
+    w = wl.WAVE_1024
+    e = w.extra
+    log("case blocked 1024 %s" % (w.shape,))
+    vel2 = upload_planes(lambda a, b: wl.vel2_planes(w, a, b), w.shape,
+                         w.np_dtype)
+    eta = upload_planes(lambda a, b: wl.eta_planes(w, a, b), w.shape,
+                        w.np_dtype)
+    # nonzero levels so that every term of the update matters
+    up = upload_planes(lambda a, b: _zero_halo_slab(w.shape, 881, a, b),
+                       w.shape, w.np_dtype)
+    uc = upload_planes(lambda a, b: _zero_halo_slab(w.shape, 882, a, b),
+                       w.shape, w.np_dtype)
+    d = B.desc_init("f32", w.shape, R)
+    src = wl.source_point(w)
+    trace = [float(v) for v in wl.source_trace(w)[:2]]
+    w0 = torch.zeros_like(uc)
+    w1 = torch.zeros_like(uc)
+    B.wave_run_blocked(d, up, uc, w0, w1, vel2, eta, e["dt"], e["h"], 2, src,
+                       trace)
+    ref = torch.zeros_like(uc)
+    B.wave_step(d, up, uc, ref, vel2, eta, e["dt"], e["h"])
+    B.wave_add_source(d, ref, *src, float(np.float32(trace[0])))
+    torch.cuda.synchronize()
+    _same_interior(w0, ref, "1024 step 1")
+    B.wave_step(d, uc, ref, up, vel2, eta, e["dt"], e["h"])  # level 3 over level 0
+    B.wave_add_source(d, up, *src, float(np.float32(trace[1])))
+    torch.cuda.synchronize()
+    _same_interior(w1, up, "1024 step 2")
+    del vel2, eta, up, uc, w0, w1, ref
+    torch.cuda.empty_cache()
+
+
+def _zero_halo_slab(shape, seed, z0, z1):
+    a = wl.uniform_planes(shape, seed, -1, 1, z0, z1)
+    nz = shape[0]
+    for k in range(z1 - z0):
+        if z0 + k < R or z0 + k >= nz - R:
+            a[k] = 0
+    a[:, :R] = 0
+    a[:, -R:] = 0
+    a[:, :, :R] = 0
+    a[:, :, -R:] = 0
+    return a
