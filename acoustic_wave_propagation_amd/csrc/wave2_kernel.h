@@ -18,7 +18,9 @@
 //    z neighbours of u^{n+1} from a register ring that stage 1 filled over
 //    the last 2R steps, in-plane neighbours from a second LDS tile.  u^n at
 //    q2 is still in stage 1's window; vel2 and eta at q2 were loaded by
-//    stage 1 R steps earlier and wait in an LDS ring private to each thread.
+//    stage 1 R steps earlier and wait in an LDS ring private to each thread
+//    (threads with points in T only).  Two sets of the stage-2 tile and R+D
+//    of the stage-1 tile leave one barrier per z step.
 //  * Stage 1's result is stored on T (u^{n+1}, the next pass's u_prev) and
 //    stage 2's (u^{n+2}).  Both outputs go to buffers no tile reads in the
 //    pass: neighbouring tiles read u^{n-1} and u^n on their extended tiles.
@@ -82,17 +84,20 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     constexpr int LTILE = (EY + 2 * R) * LP;
     constexpr int NYU = 2 * R * LX;        // halo units above and below E
     constexpr int NXU = 2 * EY * XW;       // left and right of E
-    constexpr int VBASE = (LB + 1) * LTILE;
-    constexpr int LDUMMY = VBASE + NV * 2 * VY * NT * VX;
+    constexpr int NTT = (TX / VX) * (TY / VY);  // threads whose points lie in T
+    constexpr int VBASE = (LB + 2) * LTILE;
+    constexpr int LDUMMY = VBASE + NV * 2 * VY * NTT * VX;
     constexpr uint32_t ES = sizeof(T);
     constexpr bool DIFF = std::is_same<T, double>::value;
     static_assert(TX > 0 && TY > 0, "extended tile too small");
     static_assert(NYU + NXU <= NT, "one halo unit per thread at most");
     static_assert(WS >= 2 * R + 1 && NV >= R + 1 && U % WS == 0 && U % NV == 0, "rings");
     static_assert(D == 1, "the halo ring shares the window's leading load");
+    static_assert(XE % VX == 0 && YE % VY == 0 && TY % VY == 0, "whole threads in T");
+    static_assert(64 % LX == 0, "a wave covers whole thread rows");
 
     __shared__ __align__(16) T lds[LDUMMY + VX];
-    T *const tile2 = lds + LB * LTILE;     // stage 2: u^{n+1} at q2
+    T *const tile2 = lds + LB * LTILE;     // stage 2: u^{n+1} at q2, two sets
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny, nz = a.nz;
@@ -161,7 +166,15 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     T *const h_dst = h_l >= 0 ? lds + h_l : lds + LDUMMY;  // + set * LTILE (inactive: sink)
     const int h_set_stride = h_l >= 0 ? LTILE : 0;
     // this thread's slot of the vel2/eta ring (field f, row j, ring slot s)
-    auto vring = [&](int s, int f, int j) { return lds + VBASE + (((s * 2 + f) * VY + j) * NT + tid) * VX; };
+    // vel2/eta ring slot of this thread (threads with points in T only)
+    const bool tthr = tcol && ly * VY >= YE && ly * VY < YE + TY;
+    const int tt = (ly - YE / VY) * (TX / VX) + (lx - XE / VX);
+    // whether this thread's wave has a row in T (uniform over the wave)
+    const int wrow0 = __builtin_amdgcn_readfirstlane(tid / 64) * 64 / LX * VY;
+    const bool wave_in_t = wrow0 < YE + TY && wrow0 + 64 / LX * VY > YE;
+    auto vring = [&](int s, int f, int j) {
+        return lds + VBASE + (((s * 2 + f) * VY + j) * NTT + tt) * VX;
+    };
 
     T w0[W0][VY][VX];  // u^n, planes q1-R .. q1+R plus D in flight
     T ws[WS][VY][VX];  // u^{n+1}, the last WS stage-1 planes
@@ -304,6 +317,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             constexpr int WC = kk % WS;                  // ring slot of plane q1
             constexpr int WC2 = ((kk - R) % WS + WS) % WS;  // ring slot of plane q2
             constexpr int VW = kk % NV, VR = ((kk - R) % NV + NV) % NV;
+            constexpr int T2 = kk % 2;                   // stage-2 tile set
             const int k = k0 + kk;
             const int q1 = q0 + k, q2 = q1 - R;
             const bool in1 = q1 >= R && q1 < nz - R;
@@ -331,13 +345,12 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 bload<T, VX>(r, h_off, hs[HLD]);
             }
 
-            // 2. centre rows of both tiles (the stage-2 tile has one set:
-            //    wait until every thread has read last step's)
-            __syncthreads();
+            // 2. centre rows of both tiles of this step (the stage-1 set was
+            //    last read R+D steps ago, the stage-2 set two steps ago)
 #pragma unroll
             for (int j = 0; j < VY; ++j) {
                 lds_store_group<T, VX>(lds + SET * LTILE + (lrow0 + j) * LP + lcol, w0[CS][j]);
-                lds_store_group<T, VX>(tile2 + (lrow0 + j) * LP + lcol, ws[WC2][j]);
+                lds_store_group<T, VX>(tile2 + T2 * LTILE + (lrow0 + j) * LP + lcol, ws[WC2][j]);
             }
             __syncthreads();
             // halo ring of step k + LB - 1 into its set, last read in step k-1
@@ -376,20 +389,23 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 store(a.out, q1, k >= R && k < n + R, res);
             }
 
-            // 4. stage 2: step n+2 at plane q2 on E (exact on T)
-            {
-                T v2b[VY][VX], etb[VY][VX], acc[VY][VX], res[VY][VX];
+            // 4. stage 2: step n+2 at plane q2 on E (exact on T); waves
+            //    without a row of T skip it
+            if (wave_in_t) {
+                T v2b[VY][VX] = {}, etb[VY][VX] = {}, acc[VY][VX], res[VY][VX];
+                if (tthr) {
 #pragma unroll
-                for (int j = 0; j < VY; ++j) {
-                    lds_load_group<T, VX>(vring(VR, 0, j), v2b[j]);
-                    lds_load_group<T, VX>(vring(VR, 1, j), etb[j]);
-                }
+                    for (int j = 0; j < VY; ++j) {
+                        lds_load_group<T, VX>(vring(VR, 0, j), v2b[j]);
+                        lds_load_group<T, VX>(vring(VR, 1, j), etb[j]);
+                    }
 #pragma unroll
-                for (int j = 0; j < VY; ++j) {
-                    lds_store_group<T, VX>(vring(VW, 0, j), v2[j]);
-                    lds_store_group<T, VX>(vring(VW, 1, j), et[j]);
+                    for (int j = 0; j < VY; ++j) {
+                        lds_store_group<T, VX>(vring(VW, 0, j), v2[j]);
+                        lds_store_group<T, VX>(vring(VW, 1, j), et[j]);
+                    }
                 }
-                laplacian(tile2,
+                laplacian(tile2 + T2 * LTILE,
                           [&](auto dzc, int j, int i) -> T {
                               constexpr int dz = decltype(dzc)::value;
                               return ws[((WC2 + dz) % WS + WS) % WS][j][i];
