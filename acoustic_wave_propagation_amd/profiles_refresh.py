@@ -33,15 +33,16 @@ CMDS = {
     "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_tcc -o tcc"
     + BENCH + "--only-headline --steps 5 --warmup 2",
     "wave_trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_wave -o wave"
-    + BENCH + "--only-wave both --no-cpu --steps 2",
+    + BENCH + "--only-wave all --no-cpu --steps 2",
 }
-for _v in ("wave", "pml"):
+for _v in ("wave", "pml", "blocked"):
     for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         CMDS["%s_%s" % (_v, _n)] = (
             PRE + "--pmc %s -T -d $RAW/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
             + BENCH + "--only-wave %s --calib --no-cpu --steps 1" % _v)
 HEADLINE_BYTES = 1098907648  # algorithmic bytes of one 512^3 R=4 fp32 apply
 WAVE_BYTES = 21575499776     # one 1024^3 R=4 fp32 wave (or PML) step
+PASS_BYTES = WAVE_BYTES + 4 * 1024 ** 3  # a two-step pass: one more field written
 
 
 def main(argv=None):
@@ -64,14 +65,15 @@ def main(argv=None):
         "star2p5d_r4_512cube_counters.md":
             P.counters_md([db("pmc_sq", "sq"), db("pmc_tcc", "tcc")],
                           "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
-        "wave_and_pml_r4_1024cube_trace.md":
+        "wave_pml_blocked_r4_1024cube_trace.md":
             P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"]),
     }
-    for v in ("wave", "pml"):
+    for v in ("wave", "pml", "blocked"):
         out["%s_r4_1024cube_traffic.md" % v] = P.traffic_md(
             db("pmc_%s_fetch" % v, "fetch"), db("pmc_%s_write" % v, "write"),
-            "star2p5d_kernel", "%s_r4_f32" % v, 1 << 30,
-            CMDS["%s_fetch" % v], CMDS["%s_write" % v], WAVE_BYTES)
+            "wave2_kernel" if v == "blocked" else "star2p5d_kernel",
+            "%s_r4_f32" % v, 1 << 30, CMDS["%s_fetch" % v],
+            CMDS["%s_write" % v], PASS_BYTES if v == "blocked" else WAVE_BYTES)
     for name, text in out.items():
         with open(os.path.join(prof, name), "w") as f:
             f.write(text)

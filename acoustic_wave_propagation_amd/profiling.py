@@ -30,7 +30,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "star2p5d_kernel.h"),
                   os.path.join(PKG, "csrc", "work_plan.h"),
-                  os.path.join(PKG, "csrc", "star2p5d.hip")]
+                  os.path.join(PKG, "csrc", "star2p5d.hip"),
+                  os.path.join(PKG, "csrc", "wave2_kernel.h"),
+                  os.path.join(PKG, "csrc", "wave2.hip")]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 

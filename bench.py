@@ -18,8 +18,9 @@ bounded number of whole-grid applications.
 --calib adds a plain device copy of known size (for the counter runs that
 turn FETCH_SIZE / WRITE_SIZE into bytes); --only-headline skips everything
 but the timed stencil launches, --only-others runs only the Jacobi and fp64
-workloads, --only-wave {wave,pml,both} only the 1032^3 leapfrog with those
-step kinds (all for profiler runs).
+workloads, --only-wave {wave,pml,regions,blocked,both,all} only the 1032^3
+leapfrog with those step kinds (both: wave and pml; all: also blocked; all
+for profiler runs).
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
           "R=4 25-pt stencil at 512³ fp32")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "star2p5d_r4_512cube_traffic.md")
 WAVE_TRAFFIC = {v: os.path.join(ROOT, "profiles", "%s_r4_1024cube_traffic.md" % v)
-                for v in ("wave", "pml")}
+                for v in ("wave", "pml", "blocked")}
 
 
 def log(msg):
@@ -213,11 +214,13 @@ def bench_headline(torch, B, wl, args):
     return res, host
 
 
-def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
+def bench_wave(torch, B, wl, args,
+               variants=("wave", "pml", "regions", "blocked")):
     """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
-    the pointwise step ("wave"), the PML kernel's step ("pml") and the
+    the pointwise step ("wave"), the PML kernel's step ("pml"), the
     pointwise step launched as data regions ("regions": pml_width = the
-    sponge width, so the inner box runs without the eta stream)."""
+    sponge width, so the inner box runs without the eta stream) and the
+    time-blocked run ("blocked": two steps per pass over four buffers)."""
     w = wl.WAVE_1024
     e = w.extra
     dev = torch.device("cuda:0")
@@ -235,6 +238,8 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
     eta = up(lambda a, b: wl.eta_planes(w, a, b))
     u_prev = torch.zeros_like(vel2)
     u = torch.zeros_like(vel2)
+    work = ([torch.zeros_like(vel2) for _ in range(2)] if "blocked" in variants
+            else None)
     d = B.desc_init("f32", shp, w.radius)
     # pml_width stays 0: one launch reading eta everywhere is faster on this
     # grid than the data-region launches (thin x slabs of the sponge)
@@ -257,8 +262,14 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
     res = {}
     for v in variants:
         dv = dr if v == "regions" else d
-        fn = lambda: B.wave_run(dv, u_prev, u, vel2, eta, e["dt"], e["h"],
-                                w.sweeps, src, trace, pml=(v == "pml"))
+        if v == "blocked":
+            # 20 steps = 10 passes; the fields end in (u_prev, u) again
+            fn = lambda: B.wave_run_blocked(d, u_prev, u, work[0], work[1],
+                                            vel2, eta, e["dt"], e["h"],
+                                            w.sweeps, src, trace)
+        else:
+            fn = lambda: B.wave_run(dv, u_prev, u, vel2, eta, e["dt"], e["h"],
+                                    w.sweeps, src, trace, pml=(v == "pml"))
         wall, durs = timed_launches(torch, fn, runs, 1)
         per = float(durs.mean()) / w.sweeps
         ach = nbytes / per / 1e9
@@ -272,6 +283,18 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
                                         "%s_r4_f32" % v, WAVE_TRAFFIC[v])
                                     if v in WAVE_TRAFFIC else None,
                                     algorithmic_bytes_per_step=nbytes))
+        if v == "blocked":
+            # what a pass of two steps moves: the single step's reads plus
+            # a second written field
+            pass_b = nbytes + 4 * w.interior_points
+            res[v]["roofline"]["note"] = (
+                "achieved: per-step equivalent (20.09 B/point per step, "
+                "as for the single step); the pass itself moves "
+                "pass_bytes per two steps")
+            res[v]["roofline"]["pass_bytes"] = pass_b
+            res[v]["roofline"]["traffic_per"] = "pass (one launch, two steps)"
+            res[v]["roofline"]["achieved_pass_bytes"] = round(
+                pass_b / (2 * per) / 1e9, 1)
         if v == "regions":
             true_b = nbytes - 4 * inner
             res[v]["roofline"]["true_bytes_per_step"] = true_b
@@ -280,18 +303,19 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
             res[v]["pml_width"] = e["sponge"]
         log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % ({"wave": "wave", "pml": "wave, PML step",
-                "regions": "wave, data regions"}[v], res[v]["value"],
+                "regions": "wave, data regions",
+                "blocked": "wave, time-blocked"}[v], res[v]["value"],
                res[v]["ms_per_step"], ach))
-    del vel2, eta, u_prev, u
+    del vel2, eta, u_prev, u, work
     torch.cuda.empty_cache()
     for v in variants:
-        if v == "regions":  # the same update as "wave": the same oracle
+        if v in ("regions", "blocked"):  # the same update as "wave"
             continue
         res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
             wl, w, args.cpu_budget / 4, pml=(v == "pml"))
-    if "regions" in res:
-        res["regions"]["cpu_baseline"] = res.get("wave", {}).get(
-            "cpu_baseline")
+    for v in ("regions", "blocked"):
+        if v in res:
+            res[v]["cpu_baseline"] = res.get("wave", {}).get("cpu_baseline")
     if "wave" not in res:
         return res
     out = dict(workload=w.name, **res["wave"])
@@ -303,6 +327,8 @@ def bench_wave(torch, B, wl, args, variants=("wave", "pml", "regions")):
         out["pml_step"] = res["pml"]
     if "regions" in res:
         out["data_regions"] = res["regions"]
+    if "blocked" in res:
+        out["time_blocked"] = res["blocked"]
     return out
 
 
@@ -469,7 +495,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-others", action="store_true",
                     help="run only the Jacobi and fp64 workloads (profiling)")
-    ap.add_argument("--only-wave", choices=("wave", "pml", "regions", "both"),
+    ap.add_argument("--only-wave",
+                    choices=("wave", "pml", "regions", "blocked", "both",
+                             "all"),
                     help="run only the 1032^3 leapfrog with that step "
                          "(profiling)")
     args = ap.parse_args()
@@ -489,8 +517,9 @@ def main():
 
     if args.only_wave:
         bench_wave(torch, B, wl, args,
-                   variants=("wave", "pml") if args.only_wave == "both"
-                   else (args.only_wave,))
+                   variants={"both": ("wave", "pml"),
+                             "all": ("wave", "pml", "blocked")}.get(
+                                 args.only_wave, (args.only_wave,)))
         if args.calib:
             calib_copy(torch)
         return
