@@ -48,10 +48,14 @@ struct Wave2Args {
 };
 
 // VX x VY points per thread, LX x LY threads covering the extended tile,
-// minimum waves per SIMD the register allocation must allow.
-template <int VX_, int VY_, int LX_, int LY_, int MINW_>
+// minimum waves per SIMD the register allocation must allow, and where
+// stage 2 takes vel2 and eta from: an LDS ring that stage 1 fills (VRING)
+// or a second load from memory (L2 or the Infinity Cache: the workgroup
+// read those planes R steps earlier).
+template <int VX_, int VY_, int LX_, int LY_, int MINW_, bool VRING_ = true>
 struct Wave2Cfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, MINW = MINW_;
+    static constexpr bool VRING = VRING_;
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
 
@@ -86,7 +90,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     constexpr int NXU = 2 * EY * XW;       // left and right of E
     constexpr int NTT = (TX / VX) * (TY / VY);  // threads whose points lie in T
     constexpr int VBASE = (LB + 2) * LTILE;
-    constexpr int LDUMMY = VBASE + NV * 2 * VY * NTT * VX;
+    constexpr int LDUMMY = VBASE + (C::VRING ? NV * 2 * VY * NTT * VX : 0);
     constexpr uint32_t ES = sizeof(T);
     constexpr bool DIFF = std::is_same<T, double>::value;
     static_assert(TX > 0 && TY > 0, "extended tile too small");
@@ -321,6 +325,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             const int k = k0 + kk;
             const int q1 = q0 + k, q2 = q1 - R;
             const bool in1 = q1 >= R && q1 < nz - R;
+            T v2b[VY][VX] = {}, etb[VY][VX] = {};  // vel2, eta at q2 (stage 2)
 
             // 1. stage 1's epilogue fields of plane q1 first (used at the
             //    end of this step), then the window's leading plane and the
@@ -334,6 +339,16 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     bload<T, VX>(rp, loff[j], up[j]);
                     bload<T, VX>(rv, loff[j], v2[j]);
                     bload<T, VX>(re, loff[j], et[j]);
+                }
+            }
+            if constexpr (!C::VRING) {
+                // stage 2's vel2 and eta of plane q2 (threads with points in T)
+                const bool need = q2 >= R && q2 < nz - R;
+                const rsrc_t rv = prsrc(a.vel2, q2, need), re = prsrc(a.eta, q2, need);
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    bload<T, VX>(rv, tthr ? loff[j] : kOOB, v2b[j]);
+                    bload<T, VX>(re, tthr ? loff[j] : kOOB, etb[j]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -392,8 +407,8 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             // 4. stage 2: step n+2 at plane q2 on E (exact on T); waves
             //    without a row of T skip it
             if (wave_in_t) {
-                T v2b[VY][VX] = {}, etb[VY][VX] = {}, acc[VY][VX], res[VY][VX];
-                if (tthr) {
+                T acc[VY][VX], res[VY][VX];
+                if (C::VRING && tthr) {
 #pragma unroll
                     for (int j = 0; j < VY; ++j) {
                         lds_load_group<T, VX>(vring(VR, 0, j), v2b[j]);
