@@ -10,13 +10,14 @@
 namespace st {
 namespace {
 
-// R = 4 (the 25-point wave step), fp32.  One 512-thread workgroup per
-// compute unit, 4 x 1 points per thread: the u^n window and the u^{n+1}
-// ring take ~2 x 40 registers, 162 in all, so two waves run per SIMD (with
-// 4 x 2 points per thread and 256 threads, one: 1.1x slower per pass).  The
-// LDS holds R+1 stage-1 tiles, the stage-2 tile and the vel2/eta ring
-// (151 KB).  The extended tile is 64 x 32, the output tile 56 x 24.
-using Wave2F32 = Wave2Cfg<4, 1, 16, 32, 2>;
+// R = 4 (the 25-point wave step), fp32.  One 640-thread workgroup per
+// compute unit, 4 x 1 points per thread (157 VGPRs: up to three waves per
+// SIMD); the extended tile is 64 x 40, the output tile 56 x 32.  The halo
+// units wait in private LDS slots (PSTAGE), which leaves room for the
+// vel2/eta ring and two stage-2 tile sets (143 KB).  Measured on the 1032^3
+// run (ms per step): 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40
+// as shipped 3.355, 64 x 48 with one stage-2 set 3.352.
+using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2>;
 
 template <typename T, int R, class C>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,

@@ -52,10 +52,17 @@ struct Wave2Args {
 // stage 2 takes vel2 and eta from: an LDS ring that stage 1 fills (VRING)
 // or a second load from memory (L2 or the Infinity Cache: the workgroup
 // read those planes R steps earlier).
-template <int VX_, int VY_, int LX_, int LY_, int MINW_, bool VRING_ = true>
+//
+// PSTAGE: each halo unit waits its R+D steps in LDS slots private to the
+// thread that loads it (16 bytes each) and is placed into a double-buffered
+// stage-1 tile one step ahead, instead of waiting in R+D full tile sets.
+// T2S: stage-2 tile sets (2: one barrier per z step; 1: two).
+template <int VX_, int VY_, int LX_, int LY_, int MINW_, bool VRING_ = true,
+          bool PSTAGE_ = false, int T2S_ = 2>
 struct Wave2Cfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, MINW = MINW_;
-    static constexpr bool VRING = VRING_;
+    static constexpr bool VRING = VRING_, PSTAGE = PSTAGE_;
+    static constexpr int T2S = T2S_;
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
 
@@ -89,8 +96,12 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     constexpr int NYU = 2 * R * LX;        // halo units above and below E
     constexpr int NXU = 2 * EY * XW;       // left and right of E
     constexpr int NTT = (TX / VX) * (TY / VY);  // threads whose points lie in T
-    constexpr int VBASE = (LB + 2) * LTILE;
-    constexpr int LDUMMY = VBASE + (C::VRING ? NV * 2 * VY * NTT * VX : 0);
+    constexpr int S1 = C::PSTAGE ? 2 : LB;      // stage-1 tile sets
+    constexpr int T2S = C::T2S;                 // stage-2 tile sets
+    constexpr int VBASE = (S1 + T2S) * LTILE;
+    constexpr int SBASE = VBASE + (C::VRING ? NV * 2 * VY * NTT * VX : 0);
+    constexpr int NU = NYU + NXU;               // halo units
+    constexpr int LDUMMY = SBASE + (C::PSTAGE ? LB * NU * VX : 0);
     constexpr uint32_t ES = sizeof(T);
     constexpr bool DIFF = std::is_same<T, double>::value;
     static_assert(TX > 0 && TY > 0, "extended tile too small");
@@ -99,9 +110,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     static_assert(D == 1, "the halo ring shares the window's leading load");
     static_assert(XE % VX == 0 && YE % VY == 0 && TY % VY == 0, "whole threads in T");
     static_assert(64 % LX == 0, "a wave covers whole thread rows");
+    static_assert(T2S == 1 || T2S == 2, "one or two stage-2 tile sets");
 
     __shared__ __align__(16) T lds[LDUMMY + VX];
-    T *const tile2 = lds + LB * LTILE;     // stage 2: u^{n+1} at q2, two sets
+    T *const tile2 = lds + S1 * LTILE;     // stage 2: u^{n+1} at q2
 
     const int tid = threadIdx.x;
     const int nx = a.nx, ny = a.ny, nz = a.nz;
@@ -169,6 +181,9 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     }
     T *const h_dst = h_l >= 0 ? lds + h_l : lds + LDUMMY;  // + set * LTILE (inactive: sink)
     const int h_set_stride = h_l >= 0 ? LTILE : 0;
+    // private staging slot s of this thread's halo unit (PSTAGE)
+    T *const h_stage = h_l >= 0 ? lds + SBASE + tid * VX : lds + LDUMMY;
+    const int h_stage_stride = h_l >= 0 ? NU * VX : 0;
     // this thread's slot of the vel2/eta ring (field f, row j, ring slot s)
     // vel2/eta ring slot of this thread (threads with points in T only)
     const bool tthr = tcol && ly * VY >= YE && ly * VY < YE + TY;
@@ -217,7 +232,15 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
         bload<T, VX>(prsrc(a.in, q0 + LB - 1, u_need(q0 + LB - 1)), h_off, hs[1]);
         static_for<0, LB - 1>([&](auto hc) {
             constexpr int h = decltype(hc)::value;
-            lds_store_group<T, VX>(h_dst + h * h_set_stride, hp[h]);
+            if constexpr (C::PSTAGE) {
+                // step 0's unit straight into its tile, the others staged
+                if constexpr (h == 0)
+                    lds_store_group<T, VX>(h_dst, hp[h]);
+                else
+                    lds_store_group<T, VX>(h_stage + h * h_stage_stride, hp[h]);
+            } else {
+                lds_store_group<T, VX>(h_dst + h * h_set_stride, hp[h]);
+            }
         });
     }
 
@@ -321,7 +344,9 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             constexpr int WC = kk % WS;                  // ring slot of plane q1
             constexpr int WC2 = ((kk - R) % WS + WS) % WS;  // ring slot of plane q2
             constexpr int VW = kk % NV, VR = ((kk - R) % NV + NV) % NV;
-            constexpr int T2 = kk % 2;                   // stage-2 tile set
+            constexpr int T2 = kk % T2S;                 // stage-2 tile set
+            constexpr int S1SET = kk % S1;               // stage-1 tile set
+            constexpr int NXT = (kk + 1) % LB;           // staging slot of step k+1
             const int k = k0 + kk;
             const int q1 = q0 + k, q2 = q1 - R;
             const bool in1 = q1 >= R && q1 < nz - R;
@@ -360,21 +385,34 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 bload<T, VX>(r, h_off, hs[HLD]);
             }
 
-            // 2. centre rows of both tiles of this step (the stage-1 set was
-            //    last read R+D steps ago, the stage-2 set two steps ago)
+            // 2. centre rows of both tiles of this step (a stage-1 set is
+            //    rewritten S1 steps after its last read, a stage-2 set T2S
+            //    steps after; with one stage-2 set, wait for every thread)
+            if constexpr (T2S == 1) __syncthreads();
 #pragma unroll
             for (int j = 0; j < VY; ++j) {
-                lds_store_group<T, VX>(lds + SET * LTILE + (lrow0 + j) * LP + lcol, w0[CS][j]);
+                lds_store_group<T, VX>(lds + S1SET * LTILE + (lrow0 + j) * LP + lcol, w0[CS][j]);
                 lds_store_group<T, VX>(tile2 + T2 * LTILE + (lrow0 + j) * LP + lcol, ws[WC2][j]);
             }
             __syncthreads();
-            // halo ring of step k + LB - 1 into its set, last read in step k-1
-            lds_store_group<T, VX>(h_dst + HSET * h_set_stride, hs[HST]);
+            if constexpr (!C::PSTAGE) {
+                // halo ring of step k + LB - 1 into its set, last read in
+                // step k-1
+                lds_store_group<T, VX>(h_dst + HSET * h_set_stride, hs[HST]);
+            } else {
+                // the halo unit of step k + LB - 1 into its private slot;
+                // step k+1's from its slot into the other tile set, last
+                // read in step k-1
+                lds_store_group<T, VX>(h_stage + HSET * h_stage_stride, hs[HST]);
+                T hv[VX];
+                lds_load_group<T, VX>(h_stage + NXT * h_stage_stride, hv);
+                lds_store_group<T, VX>(h_dst + (S1SET ^ 1) * h_set_stride, hv);
+            }
 
             // 3. stage 1: step n+1 at plane q1 on E
             {
                 T acc[VY][VX], res[VY][VX];
-                laplacian(lds + SET * LTILE,
+                laplacian(lds + S1SET * LTILE,
                           [&](auto dzc, int j, int i) -> T {
                               constexpr int dz = decltype(dzc)::value;
                               return w0[((CS + dz) % W0 + W0) % W0][j][i];
