@@ -19,7 +19,7 @@ import tempfile
 
 from .build import CSRC, FLAGS, INCLUDE, hipcc
 
-SOURCES = ["star2p5d.hip", "sweeps_fused.hip"]
+SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "wave2.hip"]
 FIELDS = {
     "VGPRs": "vgprs", "AGPRs": "agprs", "TotalSGPRs": "sgprs",
     "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy",
