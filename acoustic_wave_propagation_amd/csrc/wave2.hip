@@ -10,7 +10,7 @@
 namespace st {
 namespace {
 
-// R = 4 (the 25-point wave step), fp32.  One 640-thread workgroup per
+// fp32, every radius (R = 4: the 25-point wave step).  One 640-thread workgroup per
 // compute unit, 4 x 1 points per thread (157 VGPRs: up to three waves per
 // SIMD); the extended tile is 64 x 40, the output tile 56 x 32.  The halo
 // units wait in private LDS slots (PSTAGE), which leaves room for the
@@ -49,12 +49,19 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
 
 }  // namespace
 
-bool wave2_available(const stencil3d_desc &d) { return d.radius == 4 && d.dtype == ST_F32; }
+bool wave2_available(const stencil3d_desc &d) {
+    return d.dtype == ST_F32 && d.radius >= 1 && d.radius <= 4;
+}
 
 int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
                  void *out2, const void *vel2, const void *eta, double wscale,
                  const Wave2Source &src, int cus, hipStream_t stream) {
     if (!wave2_available(d)) return ST_ERR_ARG;
+    switch (d.radius) {
+    case 1: return launch_t<float, 1, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+    case 2: return launch_t<float, 2, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+    case 3: return launch_t<float, 3, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+    }
     return launch_t<float, 4, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
                                         stream);
 }

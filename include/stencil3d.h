@@ -236,7 +236,8 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
 
 /*
  * Time-blocked leapfrog: the wave_step time loop of wave_run, two steps per
- * pass over memory where the library has a two-step kernel (R = 4, ST_F32;
+ * pass over memory where the library has a two-step kernel (ST_F32, every
+ * radius;
  * "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
  * way to reuse planes across time steps), single steps otherwise and for
  * an odd last step.  Four caller-owned fields of d's shape rotate: with

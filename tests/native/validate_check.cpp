@@ -95,6 +95,31 @@ int main() {
     EXPECT(run_args(&d, A, B, D, E, 1e-3, 10.0, 3, 0, 4, 4, tr) == ST_ERR_BAD_INDEX);
     EXPECT(run_args(&d, A, base + 8, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_ALIAS);
     EXPECT(run_args(&d, A, B, A, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_ALIAS);
+    // u is written in every other step: no overlap with vel2 or eta
+    EXPECT(run_args(&d, A, B, B, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_ALIAS);
+    EXPECT(run_args(&d, A, B, D, base + 4100, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_ALIAS);
+
+    // time-blocked run: four u buffers written in turn, vel2 and eta
+    const void *F = base + 20480, *G = base + 24576;
+    EXPECT(blocked_args(&d, A, B, C, F, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_OK);
+    EXPECT(blocked_args(&d, A, B, C, F, D, D, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_OK);
+    EXPECT(blocked_args(&d, A, B, C, F, D, E, 1e-3, 10.0, -1, 4, 4, 4, tr) == ST_ERR_ARG);
+    EXPECT(blocked_args(&d, A, B, C, F, D, E, 1e-3, 10.0, 3, 0, 4, 4, tr) == ST_ERR_BAD_INDEX);
+    EXPECT(blocked_args(&d, A, B, nullptr, F, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_NULL);
+    EXPECT(blocked_args(&d, A, B, C, base + 20482, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) ==
+           ST_ERR_ALIGN);
+    const void *bufs[6] = {A, B, C, F, D, E};
+    for (int i = 0; i < 4; ++i)        // a u buffer ...
+        for (int j = 0; j < 6; ++j) {  // ... on any other buffer, exact or shifted
+            if (i == j) continue;
+            for (int shift = 0; shift <= 4; shift += 4) {
+                const void *p[6] = {bufs[0], bufs[1], bufs[2], bufs[3], bufs[4], bufs[5]};
+                p[i] = (const char *)bufs[j] + shift;
+                EXPECT(blocked_args(&d, p[0], p[1], p[2], p[3], p[4], p[5], 1e-3, 10.0, 3, 4, 4,
+                                    4, tr) == ST_ERR_ALIAS);
+            }
+        }
+    EXPECT(blocked_args(&d, A, B, C, G, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_OK);
 
     // messages
     EXPECT(strcmp(message(ST_OK), "ok") == 0);

@@ -33,15 +33,15 @@ def torch_dev():
     return torch, d
 
 
-def _zero_halo(a):
+def _zero_halo(a, r=R):
     b = np.zeros_like(a)
-    b[R:-R, R:-R, R:-R] = a[R:-R, R:-R, R:-R]
+    b[r:-r, r:-r, r:-r] = a[r:-r, r:-r, r:-r]
     return b
 
 
-def _fields(shape, seed, eta_hi=0.1):
-    up = _zero_halo(wl.uniform_planes(shape, seed, -1, 1))
-    uc = _zero_halo(wl.uniform_planes(shape, seed + 1, -1, 1))
+def _fields(shape, seed, eta_hi=0.1, r=R):
+    up = _zero_halo(wl.uniform_planes(shape, seed, -1, 1), r)
+    uc = _zero_halo(wl.uniform_planes(shape, seed + 1, -1, 1), r)
     v2 = wl.uniform_planes(shape, seed + 2, 1.5e3 ** 2, 4.5e3 ** 2)
     et = wl.uniform_planes(shape, seed + 3, 0.0, eta_hi)
     return up, uc, v2, et
@@ -64,8 +64,8 @@ def _single_steps(torch, d, up, uc, v2, et, nsteps, src, trace):
     return lv
 
 
-def _same_interior(got, want, what):
-    g, w = interior(got, R), interior(want, R)
+def _same_interior(got, want, what, r=R):
+    g, w = interior(got, r), interior(want, r)
     bad = int((g != w).sum())
     if bad:
         diff = float((g - w).abs().max())
@@ -73,17 +73,18 @@ def _same_interior(got, want, what):
                              % (what, bad, diff))
 
 
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
 @pytest.mark.parametrize("shape", [
-    (20, 40, 70),      # one tile in x and y
+    (20, 40, 70),      # one tile in x and y (R = 4)
     (45, 61, 139),     # ragged tiles in x and y, one z chunk
-    (130, 57, 121),    # several z chunks
+    (130, 77, 121),    # several z chunks
     (17, 33, 9 + 56),  # one output column of tiles, thin z
 ])
-def test_one_pass_bit_identical_to_two_steps(torch_dev, shape):
+def test_one_pass_bit_identical_to_two_steps(torch_dev, shape, r):
     torch, _ = torch_dev
-    log("case blocked pass %s" % (shape,))
-    up, uc, v2, et = (upload(a) for a in _fields(shape, 1100 + shape[0]))
-    d = B.desc_init("f32", shape, R)
+    log("case blocked pass R=%d %s" % (r, shape))
+    up, uc, v2, et = (upload(a) for a in _fields(shape, 1100 + shape[0], r=r))
+    d = B.desc_init("f32", shape, r)
     nz, ny, nx = shape
     src = (nx // 2, ny // 3, nz // 2)
     trace = [0.25, -0.5]
@@ -93,10 +94,10 @@ def test_one_pass_bit_identical_to_two_steps(torch_dev, shape):
     assert old.data_ptr() == w0.data_ptr() and new.data_ptr() == w1.data_ptr()
     lv = _single_steps(torch, d, up, uc, v2, et, 2, src, trace)
     torch.cuda.synchronize()
-    _same_interior(w0, lv[2], "step 1 of the pass")
-    _same_interior(w1, lv[3], "step 2 of the pass")
+    _same_interior(w0, lv[2], "step 1 of the pass", r)
+    _same_interior(w1, lv[3], "step 2 of the pass", r)
     for t, name in ((w0, "work0"), (w1, "work1")):
-        check_halo_untouched(t.cpu().numpy(), R, name)
+        check_halo_untouched(t.cpu().numpy(), r, name)
 
 
 def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
@@ -128,15 +129,20 @@ def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
         < 1e-4, "source missing in step 1"
 
 
-@pytest.mark.parametrize("nsteps", [0, 1, 2, 3, 4, 5, 7])
-def test_run_equals_wave_run(torch_dev, nsteps):
+@pytest.mark.parametrize("dtype,r,nsteps", [
+    ("f32", 4, 0), ("f32", 4, 1), ("f32", 4, 2), ("f32", 4, 3), ("f32", 4, 4),
+    ("f32", 4, 5), ("f32", 4, 7), ("f32", 1, 6), ("f32", 3, 5),
+    ("f64", 4, 5), ("f64", 2, 4)])  # fp64: no two-step kernel, single steps
+def test_run_equals_wave_run(torch_dev, dtype, r, nsteps):
     """A whole run, passes plus an odd last single step, against wave_run
     (two buffers, in place): same bits for both returned levels, and the
     levels sit in the buffers the rotation rule names."""
     torch, _ = torch_dev
     shape = (41, 50, 97)
-    up, uc, v2, et = (upload(a) for a in _fields(shape, 1300 + nsteps))
-    d = B.desc_init("f32", shape, R)
+    np_t = np.float32 if dtype == "f32" else np.float64
+    up, uc, v2, et = (upload(a.astype(np_t))
+                      for a in _fields(shape, 1300 + nsteps, r=r))
+    d = B.desc_init(dtype, shape, r)
     src = (40, 20, 17)
     trace = [0.1 * (k + 1) * (-1) ** k for k in range(max(nsteps, 1))]
     bufs = [up.clone(), uc.clone(), torch.zeros_like(uc), torch.zeros_like(uc)]
@@ -146,8 +152,8 @@ def test_run_equals_wave_run(torch_dev, nsteps):
     a, b = B.wave_run(d, up.clone(), uc.clone(), v2, et, DT, H, nsteps, src,
                       trace)
     torch.cuda.synchronize()
-    _same_interior(old, a, "run of %d steps, older level" % nsteps)
-    _same_interior(new, b, "run of %d steps, newest level" % nsteps)
+    _same_interior(old, a, "run of %d steps, older level" % nsteps, r)
+    _same_interior(new, b, "run of %d steps, newest level" % nsteps, r)
 
 
 def test_mixed_chunking_and_source_in_the_overlap(torch_dev):
@@ -155,13 +161,13 @@ def test_mixed_chunking_and_source_in_the_overlap(torch_dev):
     source on a point that several extended tiles compute (next to a tile
     corner), over two passes."""
     torch, _ = torch_dev
-    # 56 x 24 output tiles: 10 x 30 = 300 tiles; 200 planes make the
-    # mixed plan (256 whole columns, 44 in chunks) the cheaper one
-    shape = (208, 8 + 24 * 30, 8 + 56 * 10)
+    # 56 x 32 output tiles (R = 4): 10 x 30 = 300 tiles; 200 planes make
+    # the mixed plan (256 whole columns, 44 in chunks) the cheaper one
+    shape = (208, 8 + 32 * 30, 8 + 56 * 10)
     log("case blocked mixed chunking %s" % (shape,))
     up, uc, v2, et = (upload(a) for a in _fields(shape, 1400))
     d = B.desc_init("f32", shape, R)
-    src = (R + 56 * 3, R + 24 * 7 - 1, 13)  # last row of a tile, first column of the next
+    src = (R + 56 * 3, R + 32 * 7 - 1, 13)  # last row of a tile, first column of the next
     trace = [0.5, -0.25, 0.125, 1.0]
     bufs = [up.clone(), uc.clone(), torch.zeros_like(uc), torch.zeros_like(uc)]
     old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4, src, trace)
