@@ -13,14 +13,16 @@
 //    its in-plane neighbours from an LDS tile of E plus an R-wide halo ring.
 //    The ring of each plane is loaded in the step in which the neighbouring
 //    tiles load that plane as their window's leading plane (so it comes from
-//    L2) and staged into one of R+D tile sets until its step comes.
+//    L2) and waits until its step comes: each 16-byte unit in LDS slots
+//    private to the thread that loaded it, placed into a double-buffered
+//    tile one step ahead (PSTAGE), or the whole ring in one of R+D tile sets.
 //  * Stage 2, at plane q2 = q1 - R, computes step n+2 on E (exact on T):
 //    z neighbours of u^{n+1} from a register ring that stage 1 filled over
 //    the last 2R steps, in-plane neighbours from a second LDS tile.  u^n at
 //    q2 is still in stage 1's window; vel2 and eta at q2 were loaded by
 //    stage 1 R steps earlier and wait in an LDS ring private to each thread
-//    (threads with points in T only).  Two sets of the stage-2 tile and R+D
-//    of the stage-1 tile leave one barrier per z step.
+//    (threads with points in T only).  Two sets of each tile leave one
+//    barrier per z step.
 //  * Stage 1's result is stored on T (u^{n+1}, the next pass's u_prev) and
 //    stage 2's (u^{n+2}).  Both outputs go to buffers no tile reads in the
 //    pass: neighbouring tiles read u^{n-1} and u^n on their extended tiles.
