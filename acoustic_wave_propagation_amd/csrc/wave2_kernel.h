@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     // private staging slot s of this thread's halo unit (PSTAGE)
     T *const h_stage = h_l >= 0 ? lds + SBASE + tid * VX : lds + LDUMMY;
     const int h_stage_stride = h_l >= 0 ? NU * VX : 0;
-    // this thread's slot of the vel2/eta ring (field f, row j, ring slot s)
-    // vel2/eta ring slot of this thread (threads with points in T only)
+    // this thread's slot of the vel2/eta ring: ring slot s, field f, row j
+    // (threads with points in T only)
     const bool tthr = tcol && ly * VY >= YE && ly * VY < YE + TY;
     const int tt = (ly - YE / VY) * (TX / VX) + (lx - XE / VX);
     // whether this thread's wave has a row in T (uniform over the wave)
@@ -215,9 +215,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     // u^n planes this chunk depends on
     auto u_need = [&](int q) { return q >= zs - 2 * R && q < ze + 2 * R; };
 
-    // prologue: window slot s holds the plane at step offset s - R; halo
-    // rings of steps 0..LB-2 go straight to their tile sets, step LB-1's
-    // waits in hs[1] (stored in step 0)
+    // prologue: window slot s holds the plane at step offset s - R; the halo
+    // units of steps 0..LB-2 go to their tile sets (PSTAGE: step 0's to its
+    // tile, the others to their private slots), step LB-1's waits in hs[1]
+    // (stored in step 0)
     static_for<0, 2 * R + D>([&](auto sc) {
         constexpr int sl = decltype(sc)::value;
         const int q = q0 + sl - R;
