@@ -293,6 +293,9 @@ def bench_wave(torch, B, wl, args,
                 "pass_bytes per two steps")
             res[v]["roofline"]["pass_bytes"] = pass_b
             res[v]["roofline"]["traffic_per"] = "pass (one launch, two steps)"
+            res[v]["roofline"]["limited_by"] = (
+                "on-chip work (VALU and LDS of the overlapped first step), "
+                "not HBM: see achieved_pass_bytes")
             res[v]["roofline"]["achieved_pass_bytes"] = round(
                 pass_b / (2 * per) / 1e9, 1)
         if v == "regions":
