@@ -402,10 +402,11 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 // halo ring of step k + LB - 1 into its set, last read in
                 // step k-1
                 lds_store_group<T, VX>(h_dst + HSET * h_set_stride, hs[HST]);
-            } else {
+            } else if (h_l >= 0) {
                 // the halo unit of step k + LB - 1 into its private slot;
                 // step k+1's from its slot into the other tile set, last
-                // read in step k-1
+                // read in step k-1 (threads without a unit skip this: many
+                // lanes reading one sink address are served one by one)
                 lds_store_group<T, VX>(h_stage + HSET * h_stage_stride, hs[HST]);
                 T hv[VX];
                 lds_load_group<T, VX>(h_stage + NXT * h_stage_stride, hv);
