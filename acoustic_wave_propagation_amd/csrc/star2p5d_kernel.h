@@ -119,6 +119,16 @@ constexpr int lds_pitch(int need, int vx) {
     return p;
 }
 
+// LDS row pitch of 4 mod 8 16-byte groups (at least `need` elements, a
+// multiple of the group width): rows 4, 36 or 44 apart start 256 bytes
+// apart modulo 512.
+template <typename T>
+constexpr int pair_pitch(int need, int vx) {
+    int p = round_up(need, vx);
+    while ((p * (int)sizeof(T)) % 16 != 0 || ((p * (int)sizeof(T)) / 16) % 8 != 4) p += vx;
+    return p;
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     if constexpr (B < E) {

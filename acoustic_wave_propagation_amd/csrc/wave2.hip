@@ -17,7 +17,7 @@ namespace {
 // vel2/eta ring and two stage-2 tile sets (143 KB).  Measured on the 1032^3
 // run (ms per step): 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40
 // as shipped 3.355, 64 x 48 with one stage-2 set 3.352.
-using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2>;
+using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>;
 
 template <typename T, int R, class C>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,

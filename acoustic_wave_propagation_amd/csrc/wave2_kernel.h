@@ -59,11 +59,22 @@ struct Wave2Args {
 // thread that loads it (16 bytes each) and is placed into a double-buffered
 // stage-1 tile one step ahead, instead of waiting in R+D full tile sets.
 // T2S: stage-2 tile sets (2: one barrier per z step; 1: two).
+//
+// PAIR: which tile rows the two 16-lane thread rows of a half-wave take.
+// The LDS serves a half-wave's 16-byte accesses from a 512-byte window of
+// banks (measured: 32-lane tile rows run free of bank conflicts, 16-lane
+// rows 304 bytes apart lose ~40% of LDS cycles to them), so the two rows'
+// 256-byte runs must lie 256 bytes apart modulo 512.  With a row pitch of
+// 4 mod 8 16-byte groups that holds for rows 4 (and 36, 44) apart: output
+// rows are paired 4 apart in blocks of 8, the R rows above the output tile
+// with the R rows below it (whole waves, which skip stage 2), and the halo
+// rows above with those below.  Shapes the pairing does not tile keep the
+// plain row order.
 template <int VX_, int VY_, int LX_, int LY_, int MINW_, bool VRING_ = true,
-          bool PSTAGE_ = false, int T2S_ = 2>
+          bool PSTAGE_ = false, int T2S_ = 2, bool PAIR_ = false>
 struct Wave2Cfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, MINW = MINW_;
-    static constexpr bool VRING = VRING_, PSTAGE = PSTAGE_;
+    static constexpr bool VRING = VRING_, PSTAGE = PSTAGE_, PAIR = PAIR_;
     static constexpr int T2S = T2S_;
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
@@ -93,7 +104,13 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     constexpr int W0 = S::W0, LB = S::LB, U = S::U, WS = S::WS, NV = S::NV;
     constexpr int XW = (R + VX - 1) / VX;  // halo groups left and right
     constexpr int PADL = XW * VX;          // LDS column of extended-tile x = 0
-    constexpr int LP = lds_pitch<T>(PADL + EX + XW * VX, VX);
+    // row pairing where the shape allows it (else the plain row order)
+    constexpr int PPG = pair_pitch<T>(PADL + EX + XW * VX, VX) * (int)sizeof(T) / 16;
+    constexpr bool PAIR = C::PAIR && LX == 16 && VY == 1 && (2 * R) % 4 == 0 &&
+                          (EY - 2 * R) % 8 == 0 && (4 * PPG) % 32 == 16 &&
+                          ((EY - R) * PPG) % 32 == 16 && ((EY + R) * PPG) % 32 == 16;
+    constexpr int LP = PAIR ? pair_pitch<T>(PADL + EX + XW * VX, VX)
+                            : lds_pitch<T>(PADL + EX + XW * VX, VX);
     constexpr int LTILE = (EY + 2 * R) * LP;
     constexpr int NYU = 2 * R * LX;        // halo units above and below E
     constexpr int NXU = 2 * EY * XW;       // left and right of E
@@ -134,7 +151,15 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     const bool xpart = gx0 + TX > nx - R;     // ragged x edge inside this tile
 
     // ---- this thread's points: columns ex..ex+VX-1 on rows ey..ey+VY-1 -----
-    const int lx = tid % LX, ly = tid / LX;
+    // thread row slot -> tile row (PAIR: see the configuration)
+    const int slot = tid / LX;
+    auto row_of = [&](int sl) -> int {
+        if (!PAIR) return sl;
+        if (sl < 2 * R) return (sl & 1) ? EY - R + (sl >> 1) : (sl >> 1);
+        const int t = sl - 2 * R, b = t >> 3, r = t & 7;
+        return R + 8 * b + (r >> 1) + (r & 1) * 4;
+    };
+    const int lx = tid % LX, ly = row_of(slot);
     const int ex0 = gx0 - XE, ey0 = gy0 - YE;  // extended tile origin
     const int ex = ex0 + lx * VX, ey = ey0 + ly * VY;
     auto off_of = [&](int y, int x) -> uint32_t {
@@ -170,7 +195,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     uint32_t h_off = kOOB;
     int h_l = -1;
     if (tid < NYU) {
-        const int rsel = tid / LX, gi = tid - rsel * LX;
+        const int u = tid / LX, gi = tid - u * LX;
+        // row of the ring: 0..R-1 above the tile, R..2R-1 below (PAIR: the
+        // two rows of a half-wave are the i-th above and the i-th below)
+        const int rsel = PAIR ? ((u & 1) ? R + (u >> 1) : (u >> 1)) : u;
         const int gy = rsel < R ? ey0 - R + rsel : ey0 + EY + (rsel - R);
         h_off = off_of(gy, ex0 + gi * VX);
         h_l = (rsel < R ? rsel : EY + rsel) * LP + PADL + gi * VX;
@@ -189,10 +217,11 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     // this thread's slot of the vel2/eta ring: ring slot s, field f, row j
     // (threads with points in T only)
     const bool tthr = tcol && ly * VY >= YE && ly * VY < YE + TY;
-    const int tt = (ly - YE / VY) * (TX / VX) + (lx - XE / VX);
+    const int tt = (PAIR ? slot - 2 * R : ly - YE / VY) * (TX / VX) + (lx - XE / VX);
     // whether this thread's wave has a row in T (uniform over the wave)
     const int wrow0 = __builtin_amdgcn_readfirstlane(tid / 64) * 64 / LX * VY;
-    const bool wave_in_t = wrow0 < YE + TY && wrow0 + 64 / LX * VY > YE;
+    const bool wave_in_t = PAIR ? wrow0 + 64 / LX - 1 >= 2 * R
+                                   : wrow0 < YE + TY && wrow0 + 64 / LX * VY > YE;
     auto vring = [&](int s, int f, int j) {
         return lds + VBASE + (((s * 2 + f) * VY + j) * NTT + tt) * VX;
     };
