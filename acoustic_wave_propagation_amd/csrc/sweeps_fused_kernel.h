@@ -40,10 +40,22 @@ namespace st {
 // planes of input prefetch, LB sets of LDS tiles (2: one barrier per z step;
 // 1: half the LDS, a second barrier before the tiles are rewritten),
 // nontemporal stores.
-template <int VX_, int VY_, int LX_, int LY_, int D_ = 1, int LB_ = 2, bool NTS_ = true>
+//
+// DENSE: the LDS layout of a tile.  The thread rows here are 34 or 36
+// lanes, so a half-wave spans two of them; the LDS serves a half-wave's
+// 16-byte accesses from a 512-byte bank window, and with padded rows the
+// gap at a row boundary puts lanes on the same banks.  Dense: tile row t
+// lies in plane t mod VY at row t / VY, rows EX elements apart with no
+// padding, so the lanes of any access (all at the same row offset) touch
+// one contiguous run.  The columns left and right of the extended tile
+// then overlap the neighbouring rows' data: only edge points, which are
+// never exact, read them.  Otherwise: padded rows of an odd number of
+// 16-byte groups.
+template <int VX_, int VY_, int LX_, int LY_, int D_ = 1, int LB_ = 2, bool NTS_ = true,
+          bool DENSE_ = true>
 struct FusedCfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, D = D_, LB = LB_;
-    static constexpr bool NTS = NTS_;
+    static constexpr bool NTS = NTS_, DENSE = DENSE_;
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
 
@@ -69,7 +81,9 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
     constexpr int PADL = XW * VX;
     constexpr int LP = lds_pitch<T>(PADL + C::EX + XW * VX, VX);
     constexpr int LROWS = C::EY + 2 * R;
-    constexpr int LTILE = LROWS * LP;
+    constexpr int PLANE = LROWS / VY * C::EX + 2 * PADL;  // DENSE: one plane
+    constexpr int LTILE = C::DENSE ? VY * PLANE : LROWS * LP;
+    static_assert(!C::DENSE || LROWS % VY == 0, "whole rows per plane");
     constexpr uint32_t ES = sizeof(T);
     constexpr int SAUX = C::NTS ? kAuxNT : 0;
     constexpr bool DIFF = std::is_same<T, double>::value;
@@ -123,8 +137,15 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < VX; ++i) cin[i] = ex + i >= R && ex + i < nx - R;
     const int nvx = max(0, min(VX, nx - R - ex));  // written columns (ragged x)
-    const int lcol = PADL + lx * VX;
+    const int lcol = lx * VX;
     const int lrow0 = R + ly * VY;
+    // element of this thread's first column in tile row lrow0 + jr (jr >= -R)
+    auto trow = [&](int jr) -> int {
+        if constexpr (C::DENSE)
+            return (R + jr) % VY * PLANE + PADL + (ly + (R + jr) / VY) * C::EX + lcol;
+        else
+            return (lrow0 + jr) * LP + PADL + lcol;
+    };
 
     T w0[W0][VY][VX];             // input planes q_1-R .. q_1+R plus D in flight
     T ws[NS - 1][WS][VY][VX];     // sweeps 1..NS-1, 2R+1 planes each
@@ -175,9 +196,9 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
 #pragma unroll
                 for (int j = 0; j < VY; ++j) {
                     if constexpr (s == 0)
-                        lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, w0[CS][j]);
+                        lds_store_group<T, VX>(tile + trow(j), w0[CS][j]);
                     else
-                        lds_store_group<T, VX>(tile + (lrow0 + j) * LP + lcol, ws[s - 1][CC][j]);
+                        lds_store_group<T, VX>(tile + trow(j), ws[s - 1][CC][j]);
                 }
             });
             __syncthreads();
@@ -207,7 +228,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                 T lg[VY][VX], rg[VY][VX];
 #pragma unroll
                 for (int j = 0; j < VY; ++j) {
-                    const T *row = tile + (lrow0 + j) * LP + lcol;
+                    const T *row = tile + trow(j);
                     if constexpr (R <= VX) {
                         lds_load_group<T, VX>(row - VX, lg[j]);
                         lds_load_group<T, VX>(row + VX, rg[j]);
@@ -231,8 +252,8 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int i = 0; i < VX; ++i) {
-                        ys[r][i] = tile[(lrow0 - R + r) * LP + lcol + i];
-                        ys[R + r][i] = tile[(lrow0 + VY + r) * LP + lcol + i];
+                        ys[r][i] = tile[trow(r - R) + i];
+                        ys[R + r][i] = tile[trow(VY + r) + i];
                     }
                 T res[VY][VX];
 #pragma unroll
