@@ -8,22 +8,27 @@
 namespace st {
 
 constexpr int kMaxFusedSweeps = 8;
+constexpr int kPlanExact = 256;  // sweeps planned exactly by the dynamic program
 
 // `sweeps` Jacobi sweeps as passes of 1..maxns sweeps each.  Every pass
 // moves the field to the other buffer, so the number of passes must have the
 // parity of `sweeps` (the result then lands where one sweep per pass would
-// leave it).  Long runs start with passes of the size that is cheapest per
-// sweep; the tail -- at least 4*maxns sweeps, or all of them -- is split by
-// dynamic programming over the relative pass costs cost[1..maxns].
+// leave it).  Up to kPlanExact sweeps the split is the cheapest one under
+// the relative pass costs cost[1..maxns] (dynamic programming over the
+// count and the parity); longer runs start with passes of the size that is
+// cheapest per sweep and leave the last kPlanExact/2 or more sweeps to the
+// dynamic program.  (The cheapest size per sweep alone is not always best:
+// at costs 1, 1.42, 1.525, 1.842 for 1..4 sweeps, 21 sweeps are cheapest
+// as seven passes of three.)
 struct PassPlan {
     int bulk_ns;                        // size of the bulk passes
     int64_t bulk;                       // bulk passes, run first
     int ntail;                          // then tail[0..ntail-1]
-    int tail[5 * kMaxFusedSweeps];
+    int tail[kPlanExact + kMaxFusedSweeps];
 };
 
 inline PassPlan plan_passes(int sweeps, int maxns, const double *cost) {
-    constexpr int kTail = 5 * kMaxFusedSweeps;
+    constexpr int kTail = kPlanExact + kMaxFusedSweeps;
     PassPlan p;
     if (maxns < 1) maxns = 1;
     if (maxns > kMaxFusedSweeps) maxns = kMaxFusedSweeps;
@@ -31,9 +36,9 @@ inline PassPlan plan_passes(int sweeps, int maxns, const double *cost) {
     p.bulk_ns = 1;
     for (int ns = 2; ns <= maxns; ++ns)
         if (cost[ns] * p.bulk_ns < cost[p.bulk_ns] * ns) p.bulk_ns = ns;
-    const int keep = 4 * maxns;  // sweeps left to the dynamic program, at least
-    p.bulk = sweeps > keep ? (sweeps - keep) / p.bulk_ns : 0;
-    const int r = sweeps - (int)(p.bulk * p.bulk_ns);  // < keep + bulk_ns <= kTail
+    const int keep = kPlanExact / 2;  // sweeps left to the dynamic program, at least
+    p.bulk = sweeps > kPlanExact ? (sweeps - keep) / p.bulk_ns : 0;
+    const int r = sweeps - (int)(p.bulk * p.bulk_ns);  // <= kPlanExact < kTail
     const int want = (int)((sweeps - p.bulk) & 1);     // parity of the tail's pass count
     double best[kTail + 1][2];
     int last[kTail + 1][2];
@@ -53,8 +58,8 @@ inline PassPlan plan_passes(int sweeps, int maxns, const double *cost) {
                     last[i][par] = ns;
                 }
             }
-    // (r, want) is reachable: with bulk passes r >= 4*maxns >= 2, and two
-    // passes of one sweep or one of two fix either parity; without, r
+    // (r, want) is reachable: with bulk passes r >= kPlanExact/2 >= 2, and
+    // two passes of one sweep or one of two fix either parity; without, r
     // passes of one sweep have parity r = sweeps.
     int rev[kTail];
     p.ntail = 0;

@@ -17,17 +17,17 @@ namespace {
 // 128 x 16 (fp32) and 64 x 16 (fp64) for every NS; the extended tile adds
 // whole 16-byte groups in x and NS rows in y on each side.  4 x 2 (fp32) or
 // 2 x 2 (fp64) points per thread keep the input window and the NS-1
-// intermediate rings within two waves per SIMD.  Up to 4 sweeps two sets of
-// LDS tiles fit (one barrier per z step); 5 and 6 sweeps use one set.
-// Measured on 512^3 fp32, ms per pass for NS = 2..6: 0.328, 0.379, 0.444,
-// 0.574, 0.676 (one single sweep: 0.231); fp64 NS = 2..4: 0.547, 0.694,
-// 0.865 (one sweep: ~0.49).
+// intermediate rings within two waves per SIMD.  Up to 5 sweeps two sets of
+// (dense) LDS tiles fit (one barrier per z step); 6 sweeps use one set.
+// Kernel time per pass on a 512^3 interior, fp32 (rocprofv3 trace of
+// Jacobi calls): NS = 3..6: 0.322, 0.389, 0.460, 0.570 ms (one single
+// sweep: 0.211); fp64 NS = 2..4: 0.547, 0.694, 0.865 (one sweep: ~0.49).
 template <typename T, int NS>
 struct FusedShipped;
 template <int NS>
 struct FusedShipped<float, NS> {
     static constexpr int XE = (NS + 3) / 4 * 4;
-    using Cfg = FusedCfg<4, 2, (128 + 2 * XE) / 4, (16 + 2 * NS) / 2, 1, NS <= 4 ? 2 : 1>;
+    using Cfg = FusedCfg<4, 2, (128 + 2 * XE) / 4, (16 + 2 * NS) / 2, 1, NS <= 5 ? 2 : 1>;
 };
 template <int NS>
 struct FusedShipped<double, NS> {
@@ -106,8 +106,9 @@ int fused_max_sweeps(const stencil3d_desc &d) {
 
 const double *fused_pass_costs(const stencil3d_desc &d) {
     // time of a pass of ns sweeps relative to one single sweep (index ns),
-    // measured on 512^3 grids
-    static const double f32[] = {0.0, 1.0, 1.42, 1.64, 1.92, 2.48, 2.93};
+    // measured on 512^3 grids (fp32 ns = 2: an older measurement; no call
+    // plan isolates it, and at 0.71 per sweep it is the dearest fused pass)
+    static const double f32[] = {0.0, 1.0, 1.42, 1.525, 1.842, 2.176, 2.696};
     static const double f64[] = {0.0, 1.0, 1.12, 1.42, 1.77};
     return d.dtype == ST_F64 ? f64 : f32;
 }

@@ -23,7 +23,7 @@ static double brute(int n, int par, int maxns, const double *cost, double (*memo
 }
 
 int main() {
-    const double f32[] = {0.0, 1.0, 1.42, 1.64, 1.92, 2.48, 2.93};
+    const double f32[] = {0.0, 1.0, 1.42, 1.525, 1.842, 2.176, 2.696};
     const double flat[] = {0.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0};
     struct Case { int maxns; const double *cost; } cases[] = {{1, f32}, {2, f32}, {4, f32}, {6, f32}, {8, flat}};
     int bad = 0, checked = 0;
@@ -53,6 +53,24 @@ int main() {
             }
         }
     }
+    // long runs (bulk passes first): valid splits of the right parity
+    for (const Case &c : cases)
+        for (int s : {257, 300, 1001, 123457}) {
+            const st::PassPlan p = st::plan_passes(s, c.maxns, c.cost);
+            long total = (long)p.bulk * p.bulk_ns, passes = p.bulk;
+            bool ok = p.bulk > 0 && p.bulk_ns >= 1 && p.bulk_ns <= c.maxns;
+            for (int k = 0; k < p.ntail; ++k) {
+                ok = ok && p.tail[k] >= 1 && p.tail[k] <= c.maxns;
+                total += p.tail[k];
+                ++passes;
+            }
+            ok = ok && total == s && (passes & 1) == (s & 1);
+            ++checked;
+            if (!ok) {
+                ++bad;
+                std::printf("FAIL long maxns=%d sweeps=%d\n", c.maxns, s);
+            }
+        }
     const st::PassPlan ten = st::plan_passes(10, 6, f32);
     std::printf("10 sweeps, up to 6 fused:");
     for (long k = 0; k < ten.bulk; ++k) std::printf(" %d", ten.bulk_ns);

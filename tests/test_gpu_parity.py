@@ -675,7 +675,7 @@ def test_graph_capture_replays(torch_dev):
 def test_jacobi_fused_mixed_chunking(torch_dev, dtype):
     """A grid with more fused-pass tiles than one round of workgroups (300
     fp32 / 600 fp64 tiles on 256 compute units): whole columns for the full
-    rounds, chunks for the rest.  Ten sweeps (passes 6 + 4, or 4 + 4 + 2 in
+    rounds, chunks for the rest.  Ten sweeps (passes 5 + 5, or 4 + 4 + 2 in
     fp64) are bit-identical to ten single applies."""
     torch, _ = torch_dev
     shape = (102, 962, 642)
