@@ -10,13 +10,15 @@
 namespace st {
 namespace {
 
-// fp32, every radius (R = 4: the 25-point wave step).  One 640-thread workgroup per
-// compute unit, 4 x 1 points per thread (157 VGPRs: up to three waves per
-// SIMD); the extended tile is 64 x 40, the output tile 56 x 32.  The halo
-// units wait in private LDS slots (PSTAGE), which leaves room for the
-// vel2/eta ring and two stage-2 tile sets (143 KB).  Measured on the 1032^3
-// run (ms per step): 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40
-// as shipped 3.355, 64 x 48 with one stage-2 set 3.352.
+// fp32, every radius (R = 4: the 25-point wave step).  One 640-thread
+// workgroup per compute unit, 4 x 1 points per thread (156 VGPRs at R = 4:
+// up to three waves per SIMD); the extended tile is 64 x 40, the output
+// tile 56 x 32.  The halo units wait in private LDS slots (PSTAGE), which
+// leaves room for the vel2/eta ring and two stage-2 tile sets; thread rows
+// are paired for conflict-free LDS access where the shape allows (PAIR,
+// R = 4: 80-float rows, 146 KB).  Measured on the 1032^3 run (ms per step):
+// 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40 as shipped
+// 3.29-3.40 (box to box), 64 x 48 with one stage-2 set 3.352.
 using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>;
 
 template <typename T, int R, class C>
