@@ -15,8 +15,9 @@ divided by what the same counter read for that copy (the copy is the
 runtime's copyBuffer kernel that the benchmark's --calib flag launches).
 `counters` tabulates the mean per dispatch of every counter of any number of
 `--pmc` runs for one kernel, with L2 hit rate and LDS ratios derived.
-The output also records a hash of the kernel sources, so a consumer can tell
-whether the figures still describe the current kernel.
+The output also records a hash of the kernel sources (comments and
+whitespace ignored), so a consumer can tell whether the figures still
+describe the current kernel.
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ import argparse
 import glob
 import hashlib
 import os
+import re
 import sqlite3
 import sys
 
@@ -36,11 +38,20 @@ KERNEL_SOURCES = [os.path.join(PKG, "csrc", "star2p5d_kernel.h"),
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what
+    the compiler sees, so that editing a comment leaves the hash alone.
+    (String literals in these sources contain no comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -65,6 +65,14 @@ def test_recorded_traffic_tracks_the_kernel_source(tmp_path):
     assert b.recorded_traffic("k_r4", str(tmp_path / "missing.md")) is None
 
 
+def test_kernel_hash_ignores_comments():
+    from acoustic_wave_propagation_amd.profiling import code_only
+    a = "int f(int x) {  // the value\n  return x + 1; /* one\n more */ }\n"
+    b = "int f(int x) { return x + 1; }  // other words\n"
+    assert code_only(a) == code_only(b) == "int f(int x) { return x + 1; }"
+    assert code_only("return x + 2;") != code_only("return x + 1;")
+
+
 def _pmc_db(path, counter, rows):
     db = sqlite3.connect(path)
     db.execute("create table pmc_events (dispatch_id integer, name text, "
