@@ -20,6 +20,9 @@ namespace {
 // 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40 as shipped
 // 3.29-3.40 (box to box), 64 x 48 with one stage-2 set 3.352.
 using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>;
+// fp64: 2 x 1 points per thread (16-byte groups), same thread layout; the
+// extended tile is 32 x 40, the output tile 24 x 32 at R = 4.
+using Wave2F64 = Wave2Cfg<2, 1, 16, 40, 3, true, true, 2, true>;
 
 template <typename T, int R, class C>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
@@ -51,14 +54,21 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
 
 }  // namespace
 
-bool wave2_available(const stencil3d_desc &d) {
-    return d.dtype == ST_F32 && d.radius >= 1 && d.radius <= 4;
-}
+bool wave2_available(const stencil3d_desc &d) { return d.radius >= 1 && d.radius <= 4; }
 
 int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
                  void *out2, const void *vel2, const void *eta, double wscale,
                  const Wave2Source &src, int cus, hipStream_t stream) {
     if (!wave2_available(d)) return ST_ERR_ARG;
+    if (d.dtype == ST_F64) {
+        switch (d.radius) {
+        case 1: return launch_t<double, 1, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+        case 2: return launch_t<double, 2, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+        case 3: return launch_t<double, 3, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
+        }
+        return launch_t<double, 4, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
+                                             stream);
+    }
     switch (d.radius) {
     case 1: return launch_t<float, 1, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
     case 2: return launch_t<float, 2, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);

@@ -236,7 +236,7 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
 
 /*
  * Time-blocked leapfrog: the wave_step time loop of wave_run, two steps per
- * pass over memory where the library has a two-step kernel (ST_F32, every
+ * pass over memory (two-step kernels for both element types and every
  * radius;
  * "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
  * way to reuse planes across time steps), single steps otherwise and for

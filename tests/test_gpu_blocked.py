@@ -59,7 +59,7 @@ def _single_steps(torch, d, up, uc, v2, et, nsteps, src, trace):
         nxt = torch.zeros_like(uc)
         B.wave_step(d, lv[-2], lv[-1], nxt, v2, et, DT, H)
         if trace is not None:
-            B.wave_add_source(d, nxt, *src, float(np.float32(trace[n])))
+            B.wave_add_source(d, nxt, *src, float(trace[n]))  # rounded to d's type
         lv.append(nxt)
     return lv
 
@@ -100,6 +100,31 @@ def test_one_pass_bit_identical_to_two_steps(torch_dev, shape, r):
         check_halo_untouched(t.cpu().numpy(), r, name)
 
 
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [(45, 61, 139), (130, 77, 71)])
+def test_one_pass_bit_identical_f64(torch_dev, shape, r):
+    """The fp64 two-step pass (2 x 1 points per thread, 32 x 40 extended
+    tiles) against two fp64 single steps, bit for bit."""
+    torch, _ = torch_dev
+    log("case blocked pass f64 R=%d %s" % (r, shape))
+    up, uc, v2, et = (upload(a.astype(np.float64))
+                      for a in _fields(shape, 1700 + shape[0], r=r))
+    d = B.desc_init("f64", shape, r)
+    nz, ny, nx = shape
+    src = (nx // 3, ny // 2, nz // 2)
+    trace = [0.25, -0.5]
+    w0 = torch.full(shape, SENTINEL, dtype=torch.float64, device=device())
+    w1 = torch.full(shape, SENTINEL, dtype=torch.float64, device=device())
+    B.wave_run_blocked(d, up.clone(), uc.clone(), w0, w1, v2, et, DT, H, 2,
+                       src, trace)
+    lv = _single_steps(torch, d, up, uc, v2, et, 2, src, trace)
+    torch.cuda.synchronize()
+    _same_interior(w0, lv[2], "f64 step 1 of the pass", r)
+    _same_interior(w1, lv[3], "f64 step 2 of the pass", r)
+    for t, name in ((w0, "work0"), (w1, "work1")):
+        check_halo_untouched(t.cpu().numpy(), r, name)
+
+
 def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
     """Both steps of a pass against the oracle's wave step, teacher-forced,
     with the sponge-like eta of the real workload replaced by random eta
@@ -132,7 +157,7 @@ def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
 @pytest.mark.parametrize("dtype,r,nsteps", [
     ("f32", 4, 0), ("f32", 4, 1), ("f32", 4, 2), ("f32", 4, 3), ("f32", 4, 4),
     ("f32", 4, 5), ("f32", 4, 7), ("f32", 1, 6), ("f32", 3, 5),
-    ("f64", 4, 5), ("f64", 2, 4)])  # fp64: no two-step kernel, single steps
+    ("f64", 4, 5), ("f64", 2, 4), ("f64", 1, 3), ("f64", 3, 6)])
 def test_run_equals_wave_run(torch_dev, dtype, r, nsteps):
     """A whole run, passes plus an odd last single step, against wave_run
     (two buffers, in place): same bits for both returned levels, and the
