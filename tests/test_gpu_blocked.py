@@ -318,3 +318,26 @@ def test_blocked_run_graph_capture(torch_dev):
         # eager work between replays
         B.wave_step(d, up, uc, bufs[2], v2, et, DT, H)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+def test_smallest_grids(torch_dev, dtype, r):
+    """Every extent 2R+1 (one interior point) and a one-plane interior on a
+    wider face: runs of 4 steps against wave_run, bit for bit."""
+    torch, _ = torch_dev
+    np_t = np.float32 if dtype == "f32" else np.float64
+    for shape in ((2 * r + 1,) * 3, (2 * r + 1, 2 * r + 9, 2 * r + 70)):
+        up, uc, v2, et = (upload(a.astype(np_t))
+                          for a in _fields(shape, 1800 + r, r=r))
+        d = B.desc_init(dtype, shape, r)
+        src = (r, r, r)
+        trace = [0.5, -0.25, 0.125, 1.0]
+        bufs = [up.clone(), uc.clone(), torch.zeros_like(uc),
+                torch.zeros_like(uc)]
+        old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4, src, trace)
+        a, b = B.wave_run(d, up.clone(), uc.clone(), v2, et, DT, H, 4, src,
+                          trace)
+        torch.cuda.synchronize()
+        _same_interior(old, a, "%s R=%d %s older" % (dtype, r, shape), r)
+        _same_interior(new, b, "%s R=%d %s newest" % (dtype, r, shape), r)
