@@ -86,7 +86,8 @@ struct Wave2Shape {
     static constexpr int YE = R;                     // rows added per side
     static constexpr int TX = C::EX - 2 * XE, TY = C::EY - 2 * YE;  // output tile
     static constexpr int W0 = 2 * R + 1 + D;         // u^n window slots
-    static constexpr int LB = R + D;                 // stage-1 tile sets
+    static constexpr int LB = R + D;                 // steps a halo ring waits: stage-1
+                                                     // tile sets, or staging slots (PSTAGE)
     static constexpr int U = clcm(clcm(W0, LB), 2);  // z-loop unroll
     static constexpr int WS = ring_fit(U, 2 * R + 1);  // u^{n+1} ring slots
     static constexpr int NV = ring_fit(U, R + 1);      // vel2/eta ring slots
