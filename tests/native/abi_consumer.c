@@ -85,9 +85,59 @@ static int gpu_run(const char *path) {
     return 0;
 }
 
+/* Two leapfrog steps through wave_run_blocked (R = 4, fp32): u_prev and u
+ * random on the interior, zero halos; vel2 and eta random; a point source.
+ * Writes u_prev, u, vel2, eta, work0 (level 2) and work1 (level 3). */
+static int gpu_blocked(const char *path) {
+    const int64_t nx = 41, ny = 23, nz = 19, R = 4;
+    const size_t n = (size_t)(nx * ny * nz), bytes = n * sizeof(float);
+    float *h[6];
+    void *dv[6] = {NULL, NULL, NULL, NULL, NULL, NULL};
+    stencil3d_desc d;
+    uint32_t s = 777u;
+    for (int f = 0; f < 6; ++f) {
+        h[f] = (float *)calloc(n, sizeof(float));
+        EXPECT(h[f] != NULL);
+    }
+    for (int64_t z = 0; z < nz; ++z)
+        for (int64_t y = 0; y < ny; ++y)
+            for (int64_t x = 0; x < nx; ++x) {
+                const size_t i = (size_t)((z * ny + y) * nx + x);
+                const int in = x >= R && x < nx - R && y >= R && y < ny - R && z >= R && z < nz - R;
+                for (int f = 0; f < 4; ++f) { /* LCG in [0, 1) */
+                    s = s * 1664525u + 1013904223u;
+                    const double r = (double)(s >> 8) / 16777216.0;
+                    if (f < 2) h[f][i] = in ? (float)(2.0 * r - 1.0) : 0.0f;  /* u_prev, u */
+                    else if (f == 2) h[f][i] = (float)(2.25e6 + r * (2.025e7 - 2.25e6));
+                    else h[f][i] = (float)(0.1 * r);
+                }
+            }
+    for (int f = 0; f < 6; ++f) {
+        EXPECT(hipMalloc(&dv[f], bytes) == hipSuccess);
+        EXPECT(hipMemcpy(dv[f], h[f], bytes, hipMemcpyHostToDevice) == hipSuccess);
+    }
+    const double trace[2] = {0.5, -0.25};
+    EXPECT(stencil3d_desc_init(&d, ST_F32, nx, ny, nz, (int)R, ST_BC_HALO_UNTOUCHED) == ST_OK);
+    EXPECT(wave_run_blocked(&d, dv[0], dv[1], dv[4], dv[5], dv[2], dv[3], 1e-3, 10.0, 2, 20, 11,
+                            9, trace, NULL) == ST_OK);
+    EXPECT(hipDeviceSynchronize() == hipSuccess);
+    FILE *fp = fopen(path, "wb");
+    EXPECT(fp != NULL);
+    for (int f = 0; f < 6; ++f) {
+        if (f >= 4) EXPECT(hipMemcpy(h[f], dv[f], bytes, hipMemcpyDeviceToHost) == hipSuccess);
+        EXPECT(fwrite(h[f], 1, bytes, fp) == bytes);
+        hipFree(dv[f]);
+    }
+    fclose(fp);
+    for (int f = 0; f < 6; ++f) free(h[f]);
+    printf("gpu blocked run ok\n");
+    return 0;
+}
+
 int main(int argc, char **argv) {
     if (argc >= 2 && strcmp(argv[1], "cpu") == 0) return cpu_checks();
     if (argc >= 3 && strcmp(argv[1], "gpu") == 0) return gpu_run(argv[2]);
-    fprintf(stderr, "usage: %s cpu | gpu OUT.bin\n", argv[0]);
+    if (argc >= 3 && strcmp(argv[1], "blocked") == 0) return gpu_blocked(argv[2]);
+    fprintf(stderr, "usage: %s cpu | gpu OUT.bin | blocked OUT.bin\n", argv[0]);
     return 2;
 }
