@@ -341,3 +341,30 @@ def test_smallest_grids(torch_dev, dtype, r):
         torch.cuda.synchronize()
         _same_interior(old, a, "%s R=%d %s older" % (dtype, r, shape), r)
         _same_interior(new, b, "%s R=%d %s newest" % (dtype, r, shape), r)
+
+
+def test_blocked_deterministic_and_side_stream(torch_dev):
+    """No atomics: five repeated blocked runs (mixed chunking: more tiles
+    than compute units) are bitwise identical, also on a non-default stream."""
+    torch, _ = torch_dev
+    shape = (120, 8 + 32 * 30, 8 + 56 * 10)
+    up, uc, v2, et = (upload(a) for a in _fields(shape, 1900))
+    d = B.desc_init("f32", shape, R)
+    src, trace = (100, 200, 60), [0.5, -0.25, 0.125, 1.0]
+    runs = []
+    for k in range(6):
+        bufs = [up.clone(), uc.clone(), torch.zeros_like(uc),
+                torch.zeros_like(uc)]
+        if k < 5:
+            B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4, src, trace)
+        else:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4, src, trace)
+            s.synchronize()
+        torch.cuda.synchronize()
+        runs.append([b.cpu().numpy() for b in bufs[:2]])
+    for r in runs[1:]:
+        for a, b in zip(r, runs[0]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
