@@ -175,6 +175,23 @@ ST_EXPORT int wave_add_source(const stencil3d_desc *d, void *u, int64_t ix, int6
     return st::launch_add_source(*d, u, idx, value, static_cast<hipStream_t>(stream));
 }
 
+// The two-buffer leapfrog for steps n0 .. n1-1: a holds the older level,
+// b the newer; each step writes the next level over the older one in place
+// and adds its source, then the roles swap.
+static int leapfrog(const stencil3d_desc &d, void *a, void *b, const void *vel2,
+                    const void *eta, double wscale, int n0, int n1, int64_t idx,
+                    const double *src_trace, int cus, hipStream_t s, bool pml) {
+    for (int n = n0; n < n1; ++n) {
+        int st = launch_wave(d, b, a, a, vel2, eta, wscale, cus, s, pml);
+        if (st) return st;
+        if (src_trace && (st = st::launch_add_source(d, a, idx, src_trace[n], s))) return st;
+        void *t = a;
+        a = b;
+        b = t;
+    }
+    return ST_OK;
+}
+
 static int run_common(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2,
                       const void *eta, double dt, double h, int nsteps, int64_t src_x,
                       int64_t src_y, int64_t src_z, const double *src_trace, void *stream,
@@ -184,19 +201,9 @@ static int run_common(const stencil3d_desc *d, void *u_prev, void *u, const void
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const double wscale = (dt * dt) / (h * h);
     const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
-    void *a = u_prev, *b = u;  // a: older, b: newer
-    for (int n = 0; n < nsteps; ++n) {
-        st = launch_wave(*d, b, a, a, vel2, eta, wscale, cus, s, pml);
-        if (st) return st;
-        if (src_trace && (st = st::launch_add_source(*d, a, idx, src_trace[n], s))) return st;
-        void *t = a;
-        a = b;
-        b = t;
-    }
-    return ST_OK;
+    return leapfrog(*d, u_prev, u, vel2, eta, (dt * dt) / (h * h), 0, nsteps, idx, src_trace,
+                    cus, static_cast<hipStream_t>(stream), pml);
 }
 
 ST_EXPORT int wave_run(const stencil3d_desc *d, void *u_prev, void *u, const void *vel2,
@@ -216,7 +223,40 @@ ST_EXPORT int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u, const
 
 // Time-blocked leapfrog over four buffers: u^k lives in b[k mod 4], so two
 // steps at a time read (u^{k-1}, u^k) and write (u^{k+1}, u^{k+2}) into
-// the other two buffers, which no tile of the pass reads.
+// the other two buffers, which no tile of the pass reads.  A pass reads
+// its inputs' non-interior points too, and the levels it writes keep u's
+// there, so the work buffers' non-interior points are first set from u
+// (two copy kernels: graph-safe, and whatever the buffers held before is
+// never read).
+static int blocked_loop(const stencil3d_desc &d, void *u_prev, void *u, void *work0, void *work1,
+                        const void *vel2, const void *eta, double wscale, int nsteps,
+                        int64_t src_x, int64_t src_y, int64_t src_z, const double *src_trace,
+                        int cus, hipStream_t s) {
+    if (nsteps <= 0) return ST_OK;
+    int st = st::launch_shell_copy(d, u, work0, s);
+    if (!st) st = st::launch_shell_copy(d, u, work1, s);
+    if (st) return st;
+    const int64_t idx = src_x + d.nx * (src_y + d.ny * src_z);
+    void *b[4] = {u_prev, u, work0, work1};
+    const bool two = st::wave2_available(d);
+    for (int n = 0; n < nsteps;) {
+        void *p = b[n % 4], *c = b[(n + 1) % 4], *o1 = b[(n + 2) % 4], *o2 = b[(n + 3) % 4];
+        if (two && nsteps - n >= 2) {
+            const st::Wave2Source src{src_trace != nullptr, src_x, src_y, src_z,
+                                      src_trace ? src_trace[n] : 0.0,
+                                      src_trace ? src_trace[n + 1] : 0.0};
+            st = st::launch_wave2(d, p, c, o1, o2, vel2, eta, wscale, src, cus, s);
+            n += 2;
+        } else {
+            st = launch_wave(d, c, o1, p, vel2, eta, wscale, cus, s, false);
+            if (!st && src_trace) st = st::launch_add_source(d, o1, idx, src_trace[n], s);
+            n += 1;
+        }
+        if (st) return st;
+    }
+    return ST_OK;
+}
+
 ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
                                void *work1, const void *vel2, const void *eta, double dt,
                                double h, int nsteps, int64_t src_x, int64_t src_y,
@@ -226,27 +266,8 @@ ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, v
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const double wscale = (dt * dt) / (h * h);
-    const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
-    void *b[4] = {u_prev, u, work0, work1};
-    const bool two = st::wave2_available(*d);
-    for (int n = 0; n < nsteps;) {
-        void *p = b[n % 4], *c = b[(n + 1) % 4], *o1 = b[(n + 2) % 4], *o2 = b[(n + 3) % 4];
-        if (two && nsteps - n >= 2) {
-            const st::Wave2Source src{src_trace != nullptr, src_x, src_y, src_z,
-                                      src_trace ? src_trace[n] : 0.0,
-                                      src_trace ? src_trace[n + 1] : 0.0};
-            st = st::launch_wave2(*d, p, c, o1, o2, vel2, eta, wscale, src, cus, s);
-            n += 2;
-        } else {
-            st = launch_wave(*d, c, o1, p, vel2, eta, wscale, cus, s, false);
-            if (!st && src_trace) st = st::launch_add_source(*d, o1, idx, src_trace[n], s);
-            n += 1;
-        }
-        if (st) return st;
-    }
-    return ST_OK;
+    return blocked_loop(*d, u_prev, u, work0, work1, vel2, eta, (dt * dt) / (h * h), nsteps,
+                        src_x, src_y, src_z, src_trace, cus, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,10 +1,10 @@
 // sweeps_fused_kernel.h -- NS Jacobi sweeps of the star stencil in one pass
 // over HBM (temporal blocking), for the ping-pong entry point.
 //
-// "Accelerating High-Order Stencils on GPUs" names semi-stencil and
-// wavefront blocking as the ways to reuse a plane across several time steps;
-// this kernel does wavefront (pipelined) blocking in z combined with
-// overlapped tiles in x and y:
+// The semi-stencil section of "Accelerating High-Order Stencils on GPUs"
+// runs its time steps concurrently; the scheme here is this library's own:
+// wavefront (pipelined) blocking in z combined with overlapped tiles in x
+// and y, so each plane crosses HBM once per NS sweeps:
 //
 //  * A workgroup owns an output tile T of TX x TY points and a z chunk.  Its
 //    threads cover the extended tile E = T grown by NS*R points on each side

@@ -1,9 +1,10 @@
 // wave2_kernel.h -- two leapfrog steps of the acoustic wave update in one
 // pass over HBM (temporal blocking of the wave step).
 //
-// "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
-// way to reuse each plane across time steps.  This kernel pipelines two
-// steps in z over overlapped tiles in x and y:
+// The semi-stencil section of "Accelerating High-Order Stencils on GPUs"
+// runs its time steps concurrently; the scheme here is this library's own:
+// it pipelines two steps in z over overlapped tiles in x and y, so each
+// plane crosses HBM once per two steps:
 //
 //  * A workgroup owns an output tile T of TX x TY points and a z chunk; its
 //    threads cover the extended tile E = T grown by R points on each side

@@ -147,10 +147,12 @@ int stencil3d_apply(const stencil3d_desc *d, const void *in, void *out,
  * between the buffers, writing interiors only.  The result is in buf0 if
  * sweeps is even, else in buf1 -- bit-identical to one stencil3d_apply
  * (ST_BC_DIRICHLET_COPY) per sweep.  For R = 1 the library fuses up to 6
- * (fp32) or 4 (fp64) sweeps into one pass over HBM (temporal blocking,
- * "Accelerating High-Order Stencils on GPUs", which lists it among the ways
- * past the one-read-one-write floor); the buffer that does not hold the
- * result then holds an earlier sweep, not necessarily sweeps-1.
+ * (fp32) or 4 (fp64) sweeps into one pass over HBM (temporal blocking: the
+ * semi-stencil section of "Accelerating High-Order Stencils on GPUs" runs
+ * its time steps concurrently; the scheme here, a wavefront in z over
+ * overlapped XY tiles, is this library's own design).  The buffer that does
+ * not hold the result then holds an earlier sweep, not necessarily
+ * sweeps-1.
  * d->boundary is ignored.  sweeps >= 0 (ST_ERR_ARG); buffers must not
  * overlap.
  */
@@ -237,24 +239,28 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
 /*
  * Time-blocked leapfrog: the wave_step time loop of wave_run, two steps per
  * pass over memory (two-step kernels for both element types and every
- * radius;
- * "Accelerating High-Order Stencils on GPUs" names wavefront blocking as a
- * way to reuse planes across time steps), single steps otherwise and for
- * an odd last step.  Four caller-owned fields of d's shape rotate: with
+ * radius), single steps otherwise and for an odd last step.  The
+ * semi-stencil section of "Accelerating High-Order Stencils on GPUs" runs
+ * its time steps concurrently; the two-step wavefront over overlapped XY
+ * tiles is this library's own design.  Four caller-owned fields of d's
+ * shape rotate: with
  * b = {u_prev, u, work0, work1}, the field of time level k (u_prev holds
  * level 0, u level 1) lives in b[k mod 4].  A two-step pass reads levels
  * k-1 and k and writes k+1 and k+2 into the two other buffers (its tiles
  * overlap, so no level can be overwritten in place).  On return the newest
  * field (level nsteps + 1) is in b[(nsteps + 1) mod 4] and the one before
  * it in b[nsteps mod 4]; for a multiple of 4 steps that is u and u_prev,
- * as wave_run leaves them for an even count.  work0 and work1 are only
- * written on the interior; their input values are ignored.
+ * as wave_run leaves them for an even count.  work0 and work1 need no
+ * initial values: for nsteps > 0 the call first sets their non-interior
+ * points from u (two copy kernels on stream), then writes their interiors
+ * as levels are computed; nsteps = 0 enqueues nothing.
  *
  * Results are bit-identical to single steps with their sources
  * (wave_step(b[k-1], b[k] -> b[k+1]), then wave_add_source), with these
- * conditions: outside the interior all four u fields must hold the same
- * values (zero, as a leapfrog from zero halos keeps them), since a pass
- * takes level k+1's halo to be level k's; and d->pml_width is ignored by
+ * conditions: outside the interior u_prev and u must hold the same values
+ * (zero, as a leapfrog from zero halos keeps them), since a pass takes
+ * level k+1's non-interior points to be level k's; and d->pml_width is
+ * ignored by
  * the two-step passes (eta is read on the whole interior; the eta-free
  * inner box of wave_step gives the same values up to the sign of a zero).
  * Same arguments as wave_run otherwise.  Errors: those of wave_run, plus

@@ -7,8 +7,9 @@ must equal two single steps (wave_step into fresh buffers, then
 wave_add_source) bit for bit, and a whole run must equal wave_run's.  The
 single step is checked against the CPU oracle elsewhere; the oracle is also
 applied here directly (teacher-forced, fp32 max|err| <= 1e-5 max|ref| per
-step) on small grids.  The u fields' halos are zero, as the entry point
-requires; the work buffers' halos carry a sentinel, which must survive.
+step) on small grids.  u_prev and u share their halo (zero, or a constant),
+as the entry point requires; the work buffers start as a sentinel or NaN,
+and the call must set their non-interior points from u.
 """
 import numpy as np
 import pytest
@@ -97,7 +98,7 @@ def test_one_pass_bit_identical_to_two_steps(torch_dev, shape, r):
     _same_interior(w0, lv[2], "step 1 of the pass", r)
     _same_interior(w1, lv[3], "step 2 of the pass", r)
     for t, name in ((w0, "work0"), (w1, "work1")):
-        check_halo_untouched(t.cpu().numpy(), r, name)
+        check_halo_untouched(t.cpu().numpy(), r, name, value=0.0)
 
 
 @pytest.mark.parametrize("r", [1, 2, 3, 4])
@@ -122,7 +123,7 @@ def test_one_pass_bit_identical_f64(torch_dev, shape, r):
     _same_interior(w0, lv[2], "f64 step 1 of the pass", r)
     _same_interior(w1, lv[3], "f64 step 2 of the pass", r)
     for t, name in ((w0, "work0"), (w1, "work1")):
-        check_halo_untouched(t.cpu().numpy(), r, name)
+        check_halo_untouched(t.cpu().numpy(), r, name, value=0.0)
 
 
 def test_one_pass_matches_the_oracle(oracle_mod, torch_dev):
@@ -368,3 +369,44 @@ def test_blocked_deterministic_and_side_stream(torch_dev):
     for r in runs[1:]:
         for a, b in zip(r, runs[0]):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("nsteps", [3, 4, 5])
+def test_uninitialised_work_buffers(torch_dev, dtype, nsteps):
+    """work0 and work1 filled with NaN everywhere, as an uninitialised
+    workspace may be, and u_prev and u sharing a nonzero halo: the call sets
+    the work buffers' non-interior points from u before any pass reads them,
+    so from the second pass on (and in the odd last single step) every level
+    equals wave_run's bit for bit, no NaN appears, and all four buffers end
+    with u's halo."""
+    torch, _ = torch_dev
+    shape = (43, 52, 101)
+    r = R
+    np_t = np.float32 if dtype == "f32" else np.float64
+    log("case blocked NaN workspace %s %d steps" % (dtype, nsteps))
+    halo = 0.25
+    fields = _fields(shape, 2000 + nsteps, r=r)
+    up, uc = (a.astype(np_t) for a in fields[:2])
+    for a in (up, uc):
+        m = np.ones(shape, bool)
+        m[r:-r, r:-r, r:-r] = False
+        a[m] = halo
+    up, uc = upload(up), upload(uc)
+    v2, et = (upload(a.astype(np_t)) for a in fields[2:])
+    d = B.desc_init(dtype, shape, r)
+    src = (50, 25, 20)
+    trace = [0.2 * (k + 1) * (-1) ** k for k in range(nsteps)]
+    nan = float("nan")
+    bufs = [up.clone(), uc.clone(), torch.full_like(uc, nan),
+            torch.full_like(uc, nan)]
+    old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, nsteps, src, trace)
+    a, b = B.wave_run(d, up.clone(), uc.clone(), v2, et, DT, H, nsteps, src,
+                      trace)
+    torch.cuda.synchronize()
+    _same_interior(old, a, "NaN workspace, %d steps, older level" % nsteps, r)
+    _same_interior(new, b, "NaN workspace, %d steps, newest level" % nsteps, r)
+    for k, t in enumerate(bufs):
+        h = t.cpu().numpy()
+        assert not np.isnan(h).any(), "buffer %d holds NaN" % k
+        check_halo_untouched(h, r, "buffer %d" % k, value=halo)
