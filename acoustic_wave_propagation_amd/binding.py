@@ -22,7 +22,10 @@ HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
 EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
            "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
            "wave_step", "wave_step_pml", "wave_add_source", "wave_run",
-           "wave_run_pml", "wave_run_blocked")
+           "wave_run_pml", "wave_run_blocked", "wave_run_blocked_noalloc")
+
+# largest field wave_run_blocked_noalloc accepts (ST_NOALLOC_FIELD_BYTES_MAX)
+NOALLOC_FIELD_BYTES_MAX = 32 << 20
 
 
 class Desc(ctypes.Structure):
@@ -79,6 +82,10 @@ def lib():
             "wave_run_blocked": (i32, [D, vp, vp, vp, vp, vp, vp, dp, dp, i32,
                                        i64, i64, i64,
                                        ctypes.POINTER(ctypes.c_double), vp]),
+            "wave_run_blocked_noalloc": (i32, [D, vp, vp, vp, vp, dp, dp, i32,
+                                               i64, i64, i64,
+                                               ctypes.POINTER(ctypes.c_double),
+                                               vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -245,3 +252,18 @@ def wave_run_blocked(d: Desc, u_prev, u, work0, work1, vel2, eta, dt: float,
         _stream(u, stream)), "wave_run_blocked")
     b = (u_prev, u, work0, work1)
     return b[n % 4], b[(n + 1) % 4]
+
+
+def wave_run_blocked_noalloc(d: Desc, u_prev, u, vel2, eta, dt: float,
+                             h: float, nsteps: int, src=(0, 0, 0),
+                             src_trace=None, stream=None):
+    """The time-blocked leapfrog with the library's static workspace (no
+    allocation); result placement as wave_run: returns (older, newest)."""
+    n = int(nsteps)
+    tr = _trace(src_trace, n)
+    ix, iy, iz = src
+    _check(lib().wave_run_blocked_noalloc(
+        ctypes.byref(d), _ptr(u_prev, d, "u_prev"), _ptr(u, d, "u"),
+        _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"), float(dt), float(h), n,
+        ix, iy, iz, tr, _stream(u, stream)), "wave_run_blocked_noalloc")
+    return (u_prev, u) if n % 2 == 0 else (u, u_prev)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstencil3d.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "wave2.hip",
+SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "wave2.hip", "noalloc.hip",
            "validate.cpp", "api.cpp"]
 ARCH = "gfx950"
 

@@ -270,4 +270,36 @@ ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, v
                         src_x, src_y, src_z, src_trace, cus, static_cast<hipStream_t>(stream));
 }
 
+// wave_run_blocked with the two work fields in the library's static
+// workspace: two-step passes for the first 4 * floor(nsteps / 4) steps
+// (after which the levels are back in u_prev and u), then the remaining
+// steps as in-place single steps, so the result sits where wave_run leaves
+// it.  Calls no allocating routine.
+ST_EXPORT int wave_run_blocked_noalloc(const stencil3d_desc *d, void *u_prev, void *u,
+                                       const void *vel2, const void *eta, double dt, double h,
+                                       int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
+                                       const double *src_trace, void *stream) {
+    int st = st::check::noalloc_args(d, u_prev, u, vel2, eta, dt, h, nsteps, src_x, src_y,
+                                     src_z, src_trace);
+    if (st) return st;
+    const int cus = current_cus(&st);
+    if (st) return st;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if ((st = st::noalloc_scratch(&ws, &ws_bytes))) return st;
+    const size_t fb = (size_t)d->nx * d->ny * d->nz * st::check::elem_size(d);
+    const size_t stride = (fb + 255) / 256 * 256;
+    if (2 * stride > ws_bytes) return ST_ERR_WORKSPACE;
+    void *work0 = ws, *work1 = static_cast<char *>(ws) + stride;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const double wscale = (dt * dt) / (h * h);
+    const int bulk = nsteps / 4 * 4;
+    st = blocked_loop(*d, u_prev, u, work0, work1, vel2, eta, wscale, bulk, src_x, src_y, src_z,
+                      src_trace, cus, s);
+    if (st) return st;
+    const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
+    return leapfrog(*d, u_prev, u, vel2, eta, wscale, bulk, nsteps, idx, src_trace, cus, s,
+                    false);
+}
+
 }  // extern "C"

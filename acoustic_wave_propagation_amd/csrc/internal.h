@@ -97,6 +97,11 @@ int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, voi
 int launch_shell_copy(const stencil3d_desc &d, const void *in, void *out,
                       hipStream_t stream);
 
+// Device address and size of this device's static workspace (the two
+// fields of wave_run_blocked_noalloc), looked up on the first call per
+// device.  Returns ST_OK or ST_ERR_DEVICE.
+int noalloc_scratch(void **ptr, size_t *bytes);
+
 // u[idx] += value (one thread).
 int launch_add_source(const stencil3d_desc &d, void *u, int64_t idx,
                       double value, hipStream_t stream);

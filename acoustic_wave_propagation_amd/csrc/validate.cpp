@@ -68,6 +68,8 @@ const char *message(int code) {
     case ST_ERR_ALIGN: return "pointer not aligned to the element size";
     case ST_ERR_LAUNCH: return "HIP kernel launch failed";
     case ST_ERR_DEVICE: return "no usable HIP device";
+    case ST_ERR_WORKSPACE:
+        return "field larger than the static workspace of wave_run_blocked_noalloc";
     }
     return "unknown status code";
 }
@@ -179,6 +181,15 @@ int blocked_args(const stencil3d_desc *d, const void *u_prev, const void *u, con
     for (const void *o : others)
         if (overlap(d, work0, o) || overlap(d, work1, o)) return ST_ERR_ALIAS;
     if (overlap(d, work0, work1)) return ST_ERR_ALIAS;
+    return ST_OK;
+}
+
+int noalloc_args(const stencil3d_desc *d, const void *u_prev, const void *u, const void *vel2,
+                 const void *eta, double dt, double h, int nsteps, int64_t sx, int64_t sy,
+                 int64_t sz, const double *src_trace) {
+    int st = run_args(d, u_prev, u, vel2, eta, dt, h, nsteps, sx, sy, sz, src_trace);
+    if (st) return st;
+    if (field_bytes(d) > (size_t)ST_NOALLOC_FIELD_BYTES_MAX) return ST_ERR_WORKSPACE;
     return ST_OK;
 }
 

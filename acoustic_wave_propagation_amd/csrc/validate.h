@@ -33,5 +33,10 @@ int blocked_args(const stencil3d_desc *d, const void *u_prev, const void *u, con
                  const void *work1, const void *vel2, const void *eta, double dt, double h,
                  int nsteps, int64_t sx, int64_t sy, int64_t sz, const double *src_trace);
 
+// run_args, plus: one field fits the static workspace (ST_ERR_WORKSPACE).
+int noalloc_args(const stencil3d_desc *d, const void *u_prev, const void *u, const void *vel2,
+                 const void *eta, double dt, double h, int nsteps, int64_t sx, int64_t sy,
+                 int64_t sz, const double *src_trace);
+
 }  // namespace check
 }  // namespace st

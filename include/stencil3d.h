@@ -12,7 +12,9 @@
  * Conventions shared by every entry point:
  *  - Pointers named in/out/u/... are DEVICE pointers (hipMalloc or torch
  *    allocations), aligned to the element size, owned by the caller.  The
- *    library allocates no device memory and keeps no pointer after return.
+ *    library allocates no device memory and keeps no pointer after return
+ *    (wave_run_blocked_noalloc uses a static device array of the library's
+ *    own instead).
  *  - stream is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns without synchronising.
  *  - Return value: ST_OK (0) or a negative ST_ERR_* code.  Every argument
@@ -20,7 +22,9 @@
  *    partial work; no C++ exception crosses this boundary.  ST_ERR_LAUNCH
  *    reports a HIP error seen right after the launch.
  *  - Thread safety: calls may come from any host thread; the library holds
- *    no mutable state besides a per-device cache of the compute-unit count.
+ *    no mutable state besides per-device caches (compute-unit count, the
+ *    static workspace's address).  Overlapping wave_run_blocked_noalloc
+ *    calls on one GPU race on its workspace.
  *  - Graph capture: a call only enqueues kernel launches on stream (no
  *    allocation, synchronisation, memset or copy), so it may be captured
  *    into a HIP graph and replayed.  Host arguments are read when the call
@@ -35,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ST_ABI_VERSION 4
+#define ST_ABI_VERSION 5
 #define ST_MAX_R 4
 
 /* element types */
@@ -61,6 +65,12 @@ extern "C" {
 #define ST_ERR_ALIGN (-11)      /* pointer not aligned to the element size   */
 #define ST_ERR_LAUNCH (-12)     /* HIP reported an error at launch           */
 #define ST_ERR_DEVICE (-13)     /* no usable HIP device                      */
+#define ST_ERR_WORKSPACE (-14)  /* field too large for the static workspace  */
+
+/* Largest field (nx*ny*nz*element size, bytes) that
+ * wave_run_blocked_noalloc accepts: its two work fields live in a static
+ * device array of twice this size (64 MiB per GPU). */
+#define ST_NOALLOC_FIELD_BYTES_MAX (32u << 20)
 
 /*
  * Problem descriptor.  cx/cy/cz hold the per-axis weights: index 0 is that
@@ -273,6 +283,40 @@ int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u,
                      const void *eta, double dt, double h, int nsteps,
                      int64_t src_x, int64_t src_y, int64_t src_z,
                      const double *src_trace, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * time-blocked leapfrog of wave_run_blocked with its two work fields taken
+ * from a static device array inside the library (2 x
+ * ST_NOALLOC_FIELD_BYTES_MAX bytes, held by each GPU the library runs on
+ * until the process ends) instead of from the caller.  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.  The
+ * array's device address is looked up once per device on its first call.
+ *
+ * Arguments, rules and results are wave_run's: the newest field ends in u
+ * for an even nsteps, else in u_prev, the other buffer holding the level
+ * before it, bit-identical to wave_run (and to wave_run_blocked) under
+ * wave_run_blocked's condition that u_prev and u hold the same
+ * non-interior values.  Internally: two-step passes for the first
+ * 4*floor(nsteps/4) steps (which leave the levels in u_prev and u), then
+ * the remaining steps as in-place single steps.
+ *
+ * Errors: those of wave_run, plus ST_ERR_WORKSPACE (before anything is
+ * enqueued) if one field exceeds ST_NOALLOC_FIELD_BYTES_MAX.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (each call first sets the non-interior points it reads and
+ * writes every interior point before reading it, so no state leaks from
+ * one call into the next).  Calls that overlap in time on one GPU -- from
+ * two streams, or two host threads -- race on the array and give wrong
+ * results; serialise them.
+ */
+int wave_run_blocked_noalloc(const stencil3d_desc *d, void *u_prev, void *u,
+                             const void *vel2, const void *eta, double dt,
+                             double h, int nsteps, int64_t src_x,
+                             int64_t src_y, int64_t src_z,
+                             const double *src_trace, void *stream);
 
 #ifdef __cplusplus
 }

@@ -121,9 +121,30 @@ int main() {
         }
     EXPECT(blocked_args(&d, A, B, C, G, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_OK);
 
+    // no-allocation run: run_args plus the workspace limit
+    EXPECT(noalloc_args(&d, A, B, D, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_OK);
+    EXPECT(noalloc_args(&d, A, B, D, E, 1e-3, 10.0, -1, 4, 4, 4, tr) == ST_ERR_ARG);
+    EXPECT(noalloc_args(&d, A, B, B, E, 1e-3, 10.0, 3, 4, 4, 4, tr) == ST_ERR_ALIAS);
+    {
+        stencil3d_desc big;
+        // 128 x 128 x 512 fp32 = 32 MiB: the limit itself; one plane more is over
+        EXPECT(init(&big, ST_F32, 128, 128, 512, 4, 0) == ST_OK);
+        const char *far = (const char *)0x100000000;
+        const void *P = far, *Q = far + (64 << 20), *S = far + (128 << 20),
+                   *T = far + (192 << 20);
+        EXPECT(noalloc_args(&big, P, Q, S, T, 1e-3, 10.0, 3, 8, 8, 8, tr) == ST_OK);
+        big.nz = 513;
+        EXPECT(noalloc_args(&big, P, Q, S, T, 1e-3, 10.0, 3, 8, 8, 8, tr) == ST_ERR_WORKSPACE);
+        big.nz = 256;
+        big.dtype = ST_F64;  // 128 x 128 x 256 fp64 = 32 MiB
+        EXPECT(noalloc_args(&big, P, Q, S, T, 1e-3, 10.0, 3, 8, 8, 8, tr) == ST_OK);
+        big.nz = 257;
+        EXPECT(noalloc_args(&big, P, Q, S, T, 1e-3, 10.0, 3, 8, 8, 8, tr) == ST_ERR_WORKSPACE);
+    }
+
     // messages
     EXPECT(strcmp(message(ST_OK), "ok") == 0);
-    for (int c = ST_ERR_DEVICE; c < 0; ++c)  // every code has its own message
+    for (int c = ST_ERR_WORKSPACE; c < 0; ++c)  // every code has its own message
         EXPECT(strcmp(message(c), message(-99)) != 0);
     EXPECT(strcmp(message(-99), "unknown status code") == 0);
 

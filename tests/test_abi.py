@@ -65,7 +65,7 @@ def test_exports_nothing_else(L):
 
 def test_struct_layout_and_version(L):
     assert ctypes.sizeof(B.Desc) == 168
-    assert B.abi_version() == 4
+    assert B.abi_version() == 5
     d = B.desc_init("f32", (10, 11, 12), 4)
     assert d.struct_size == 168 and d.nx == 12 and d.ny == 11 and d.nz == 10
     assert d.pml_width == 0
@@ -222,6 +222,35 @@ def test_entry_points_reject_before_enqueue(L):
             assert b(*p) == c["ST_ERR_ALIAS"], (i, j)
     # vel2 and eta may share a buffer
     assert b(V[0], V[1], V[2], V[3], V[4], V[4], nsteps=-1) == c["ST_ERR_ARG"]
+    # the no-allocation variant: wave_run's rules, plus the workspace limit,
+    # all checked before the device is touched
+    na = L.wave_run_blocked_noalloc
+    assert na(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, -1, 10, 10, 10, None,
+              None) == c["ST_ERR_ARG"]
+    assert na(by, U[0], U[1], U[3], U[4], 1e-3, 10.0, 3, 2, 10, 10, tr,
+              None) == c["ST_ERR_BAD_INDEX"]
+    assert na(by, U[0], U[1], U[1], U[4], 1e-3, 10.0, 3, 10, 10, 10, None,
+              None) == c["ST_ERR_ALIAS"]
+    assert na(by, U[0], None, U[3], U[4], 1e-3, 10.0, 3, 10, 10, 10, None,
+              None) == c["ST_ERR_NULL"]
+    cap = B.NOALLOC_FIELD_BYTES_MAX
+    # largest fp32 cube within the limit, and one plane more
+    nx = ny = 128
+    nz_ok = cap // (4 * nx * ny)
+    for nz, code in ((nz_ok + 1, c["ST_ERR_WORKSPACE"]),
+                     (nz_ok, None)):
+        big = B.desc_init("f32", (nz, ny, nx), 4)
+        m = nz * ny * nx * 4
+        W = [0x100000000 + i * (m + 4096) for i in range(4)]
+        r = na(ctypes.byref(big), W[0], W[1], W[2], W[3], 1e-3, 10.0, -1
+               if code is None else 2, 10, 10, 10, None, None)
+        # within the limit only the bad step count is reported
+        assert r == (code if code is not None else c["ST_ERR_ARG"]), (nz, r)
+    f64 = B.desc_init("f64", (nz_ok // 2 + 1, ny, nx), 4)
+    m = (nz_ok // 2 + 1) * ny * nx * 8
+    W = [0x100000000 + i * (m + 4096) for i in range(4)]
+    assert na(ctypes.byref(f64), W[0], W[1], W[2], W[3], 1e-3, 10.0, 2, 10,
+              10, 10, None, None) == c["ST_ERR_WORKSPACE"]
 
 
 def test_binding_checks_tensors(L):
