@@ -32,7 +32,12 @@ namespace {
 // The wave tiles load a step's u_prev, vel2 and eta first, ahead of the
 // stencil-input prefetch, so that waiting for them does not drain the
 // prefetch (1032^3 fp32 step: 4.04 against 4.13 ms).
-using F32Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
+// The fp32 apply numbers its workgroups tile-major (the z chunks of a tile
+// are neighbours, so each XCD streams all chunks of a band of tiles):
+// 0.2040 against 0.2056 ms chunk-major on 520^3 (4 chunks of 128 planes),
+// though it fetches more (the band edges' halo rows come from another XCD's
+// L2 or the Infinity Cache).
+using F32Apply = TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, false, true, true>;
 using F32ApplyR1 = TileCfg<4, 4, 64, 8, 1, 0, true, 2, false, true, true, true>;
 using F32ApplyR1Wide = TileCfg<4, 4, 128, 4, 1, 0, true, 2, false, true, true, true>;
 using F32Wave = TileCfg<4, 2, 32, 16, 1, 0, true, 2, false, true, true, false, false, 1, false, true>;
@@ -145,9 +150,9 @@ int launch_r(const stencil3d_desc &d, const Geometry &g, const void *in, void *o
     return ST_ERR_RADIUS;
 }
 
-// Tile shape, threads and z unroll of a kernel variant.
+// Tile shape, threads and pipeline fill of a kernel variant.
 struct Shape {
-    int tile_x, tile_y, threads, unroll, prologue;
+    int tile_x, tile_y, threads, prologue;
     bool exists;
 };
 
@@ -156,7 +161,7 @@ Shape shape_of() {
     using KC = KindCfg<T, R, K>;
     using C = typename KC::Cfg;
     using RG = Rings<R, KC::wave, C, KC::pml>;
-    return Shape{C::TX, C::TY, C::NT, RG::U, 2 * R + RG::D, kind_exists<T, R>(K)};
+    return Shape{C::TX, C::TY, C::NT, 2 * R + RG::D, kind_exists<T, R>(K)};
 }
 
 template <typename T, int R>
@@ -222,7 +227,7 @@ Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int c
     // once; chunks are no shorter than about 4R planes.
     const int R = d.radius;
     const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * (g.threads >= 512 ? 1 : 512 / g.threads);
-    const ChunkPlan p = plan_chunks(bz, tiles, sh.unroll, 4 * R, cap, sh.prologue + 4);
+    const ChunkPlan p = plan_chunks(bz, tiles, 4 * R, cap, sh.prologue + 4);
     g.nwg = (int)p.nwg;
     g.chunk_len = (int)p.chunk_len;
     g.nchunks = (int)p.nchunks;

@@ -137,6 +137,23 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// The z loop of the streaming kernels: step(kc, k0) for the steps k = k0 +
+// kc in [0, n), kc a compile-time constant in [0, U).  Whole blocks of U
+// steps run without any condition (the instruction stream is the same in
+// every block, so the compiler's wait counts only cover loads that are at
+// least a step old); the final partial block skips each step past n.  n is
+// the same for every thread of the workgroup, so the barriers inside a step
+// stay matched, and a chunk of any length costs its own steps only.
+template <int U, typename F>
+__device__ __forceinline__ void zsteps(int n, F &&step) {
+    int k0 = 0;
+    for (; k0 + U <= n; k0 += U) static_for<0, U>([&](auto kc) { step(kc, k0); });
+    if (k0 < n)
+        static_for<0, U>([&](auto kc) {
+            if (decltype(kc)::value == 0 || k0 + decltype(kc)::value < n) step(kc, k0);
+        });
+}
+
 // ---- buffer addressing -----------------------------------------------------
 // Every plane is addressed through a buffer resource (V#) whose base is the
 // plane start (uniform, scalar registers) and whose num_records ends at the
@@ -480,12 +497,10 @@ star2p5d_kernel(StarArgs<T> a) {
         load_eta_halo(0, true, std::integral_constant<int, 0>{});
     }
 
-    // Whole blocks of U steps, with no exit inside a block: the instruction
-    // stream is then the same every block and the compiler's wait counts
-    // only cover loads at least D-1 steps old.  Steps past the chunk end run
-    // on empty resources (no memory traffic, stores dropped).
-    for (int k0 = 0; k0 < n; k0 += U) {
-        static_for<0, U>([&](auto kc) {
+    // Steps of the chunk (zsteps: whole blocks of U, then a partial one).
+    // Loads of planes past the chunk's needs get empty resources (no memory
+    // traffic).
+    zsteps<U>(n, [&](auto kc, const int k0) {
             constexpr int kk = decltype(kc)::value;
             constexpr int CS = (kk + R) % W;           // window slot of step k
             constexpr int LEAD = (kk + 2 * R + D) % W;  // slot of offset R+D
@@ -649,8 +664,7 @@ star2p5d_kernel(StarArgs<T> a) {
                         bstore1<T>(ro, i < nvx && nvx < VX ? soff[j] + i * ES : kOOB, res[j][i]);
                 }
             }
-        });
-    }
+    });
 }
 
 // out = in on every non-interior point.  The non-interior points are the

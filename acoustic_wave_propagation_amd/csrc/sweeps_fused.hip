@@ -52,8 +52,7 @@ FusedPlan plan_fused(const stencil3d_desc &d, int cus) {
     const int64_t tiles = (int64_t)p.tiles_x * p.tiles_y;
     // one workgroup per compute unit (LDS and registers); chunked as for
     // the single-sweep kernel, no shorter than about 4 planes per sweep
-    const ChunkPlan c = plan_chunks(iz, tiles, FS::U, 4 * NS, cus > 0 ? cus : 256,
-                                    FS::PROLOGUE + 4);
+    const ChunkPlan c = plan_chunks(iz, tiles, 4 * NS, cus > 0 ? cus : 256, FS::PROLOGUE + 4);
     p.nwg = (int)c.nwg;
     p.chunk_len = (int)c.chunk_len;
     p.a_nwg = (int)c.a_nwg;

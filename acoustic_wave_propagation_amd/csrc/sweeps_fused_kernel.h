@@ -171,8 +171,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
         for (int j = 0; j < VY; ++j) bload<T, VX>(r, loff[j], w0[sl][j]);
     });
 
-    for (int k0 = 0; k0 < nsteps; k0 += U) {
-        static_for<0, U>([&](auto kc) {
+    zsteps<U>(nsteps, [&](auto kc, const int k0) {
             constexpr int kk = decltype(kc)::value;
             constexpr int CS = (kk + R) % W0;          // window slot of plane q_1
             constexpr int LEAD = (kk + 2 * R + D) % W0;
@@ -317,8 +316,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                     }
                 }
             });
-        });
-    }
+    });
 }
 
 }  // namespace st

@@ -35,7 +35,7 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
     const int64_t tiles = (int64_t)tiles_x * tiles_y;
     // chunks no shorter than about 8R planes: each costs 2R fill steps and
     // re-reads 4R planes of u^n
-    const ChunkPlan p = plan_chunks(iz, tiles, S::U, 8 * R, cus > 0 ? cus : 256, S::PROLOGUE + 4);
+    const ChunkPlan p = plan_chunks(iz, tiles, 8 * R, cus > 0 ? cus : 256, S::PROLOGUE + 4);
     Wave2Args<T> g;
     g.s = make_args<T, R>(d, interior_box(d), u, out1, u_prev, vel2, eta, wscale, tiles_x, tiles_y,
                           (int)p.chunk_len, (int)p.nwg);

@@ -366,8 +366,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
         }
     };
 
-    for (int k0 = 0; k0 < nsteps; k0 += U) {
-        static_for<0, U>([&](auto kc) {
+    zsteps<U>(nsteps, [&](auto kc, const int k0) {
             constexpr int kk = decltype(kc)::value;
             constexpr int CS = (kk + R) % W0;            // window slot of plane q1
             constexpr int LEAD = (kk + 2 * R + D) % W0;  // slot the prefetch fills
@@ -517,8 +516,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 }
                 store(g.out2, q2, k >= 2 * R && k < n + 2 * R, res);
             }
-        });
-    }
+    });
 }
 
 }  // namespace st

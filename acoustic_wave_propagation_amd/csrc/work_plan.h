@@ -36,14 +36,19 @@ struct ChunkPlan {
 // which `cap` workgroups run at once.  A set of equal chunks takes
 // ceil(workgroups / cap) rounds, each lasting a chunk's planes plus the
 // pipeline fill `fill`; the chunk count minimising rounds * (length + fill)
-// is taken, with chunks no shorter than min_len planes (roughly) and chunk
-// lengths whole multiples of the kernel's z unroll.  When the tiles fill
+// is taken, with chunks no shorter than min_len planes (roughly).  Chunks
+// are as equal as the depth allows (ceil(depth / count) planes, the last
+// one shorter by less than the count): the kernels run any chunk length at
+// the cost of its own steps, and the longest chunk sets a round's time.
+// (Rounding the 512 planes of a 520^3 grid up to whole 12-step unroll
+// blocks, 132 + 132 + 132 + 116, left the workgroups of the short chunk
+// idle for the last 8% of the launch.)  When the tiles fill
 // whole rounds with some left over, group A instead streams the whole
 // rounds' tiles through all of z and only the remaining tiles are chunked
 // (e.g. 304 tiles on 256 compute units: 256 whole columns, then 48 columns
 // in 5 chunks, rather than every column in 5 chunks) if that costs less.
-inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t unroll, int64_t min_len,
-                             int64_t cap, int64_t fill) {
+inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t min_len, int64_t cap,
+                             int64_t fill) {
     struct Chunks {
         int64_t len, nch, cost;
     };
@@ -55,8 +60,7 @@ inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t unroll, int64
         if (maxch > enough) maxch = enough;
         Chunks b{depth, 1, -1};
         for (int64_t nch = 1; nch <= maxch; ++nch) {
-            int64_t len = (depth + nch - 1) / nch;
-            len = (len + unroll - 1) / unroll * unroll;
+            const int64_t len = (depth + nch - 1) / nch;
             const int64_t n = (depth + len - 1) / len;
             const int64_t rounds = (nt * n + cap - 1) / cap;
             const int64_t cost = rounds * (len + fill);
@@ -68,9 +72,8 @@ inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t unroll, int64
     ChunkPlan p{tiles * uni.nch, uni.len, uni.nch, 0, 0, 0};
     const int64_t full = tiles / cap * cap, rest = tiles - full;
     if (full > 0 && rest > 0) {
-        const int64_t alen = (depth + unroll - 1) / unroll * unroll;
         const Chunks b = best(rest);
-        if (full / cap * (alen + fill) + b.cost < uni.cost)
+        if (full / cap * (depth + fill) + b.cost < uni.cost)
             p = ChunkPlan{full + rest * b.nch, b.len, b.nch, full, full, depth};
     }
     return p;

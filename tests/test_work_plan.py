@@ -33,3 +33,6 @@ def test_work_plans_cover_the_box(tmp_path):
     # of 103 (240 workgroups, one round of 115): 639 < 690.
     assert ("plan(512 planes, 304 tiles, cap 256, fill 12, min 16): nwg 496, "
             "A 256 tiles x 512, B 5 chunks of 103") in r.stdout, r.stdout
+    # equal chunks: 512 planes in 4 chunks of 128 (not 132 + 132 + 132 + 116)
+    assert "plan(512 planes, 64 tiles, cap 256): nwg 256, 4 chunks of 128" \
+        in r.stdout, r.stdout
