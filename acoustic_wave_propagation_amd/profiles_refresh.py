@@ -1,11 +1,15 @@
 """Rewrite the rocprofv3 summaries under profiles/ from the raw output of
 one profiling session: the databases the commands below write under $RAW.
 
-    python -m acoustic_wave_propagation_amd.profiles_refresh RAW_DIR
+    python -m acoustic_wave_propagation_amd.profiles_refresh RAW_DIR [OUT_DIR]
+    python -m acoustic_wave_propagation_amd.profiles_refresh --commands KEY...
 
 Each summary records the exact command that produced its database; the
 commands are run from /tmp with TMPDIR=/tmp, the repository at $REPO and the
-raw output directory at $RAW.
+raw output directory at $RAW.  Summaries whose databases are missing from
+RAW_DIR are skipped (a session may run only some of the commands); they are
+written to OUT_DIR (default: profiles/).  --commands prints the commands of
+the given keys (or of all), one per line, for a shell to run.
 """
 from __future__ import annotations
 
@@ -40,44 +44,97 @@ for _v in ("wave", "pml", "blocked"):
         CMDS["%s_%s" % (_v, _n)] = (
             PRE + "--pmc %s -T -d $RAW/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
             + BENCH + "--only-wave %s --calib --no-cpu --steps 1" % _v)
+# the two-step pass and the fused Jacobi passes: SQ and L2 counters
+CMDS["blocked_sq"] = (PRE + "--pmc " + SQ + " -T -d $RAW/pmc_blocked_sq -o sq"
+                      + BENCH + "--only-wave blocked --no-cpu --steps 1")
+CMDS["blocked_tcc"] = (PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_blocked_tcc -o tcc"
+                       + BENCH + "--only-wave blocked --no-cpu --steps 1")
+CMDS["others_sq"] = (PRE + "--pmc " + SQ + " -T -d $RAW/pmc_others_sq -o sq"
+                     + BENCH + "--only-others --no-cpu --steps 2 --warmup 1")
+CMDS["others_tcc"] = (PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_others_tcc -o tcc"
+                      + BENCH + "--only-others --no-cpu --steps 2 --warmup 1")
+# HBM traffic of the fused Jacobi pass and the fp64 ragged apply
+for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+    CMDS["others_%s" % _n] = (
+        PRE + "--pmc %s -T -d $RAW/pmc_others_%s -o %s" % (_c, _n, _n)
+        + BENCH + "--only-others --calib --no-cpu --steps 2 --warmup 1")
 HEADLINE_BYTES = 1098907648  # algorithmic bytes of one 512^3 R=4 fp32 apply
 WAVE_BYTES = 21575499776     # one 1024^3 R=4 fp32 wave (or PML) step
 PASS_BYTES = WAVE_BYTES + 4 * 1024 ** 3  # a two-step pass: one more field written
+JACOBI_PASS_BYTES = 1067450400  # a fused R=1 pass over 512^3: one read, one write
+F64_BYTES = 2799206128          # one R=4 fp64 apply on 1001 x 603 x 297
 
 
 def main(argv=None):
     argv = sys.argv[1:] if argv is None else argv
-    if len(argv) != 1:
+    if argv and argv[0] == "--commands":
+        for k in (argv[1:] or sorted(CMDS)):
+            print(CMDS[k])
+        return 0
+    if len(argv) not in (1, 2):
         print(__doc__, file=sys.stderr)
         return 2
     raw = argv[0]
-    prof = os.path.join(ROOT, "profiles")
-    db = lambda d, n: os.path.join(raw, d, n + "_results.db")
-    out = {
+    prof = argv[1] if len(argv) == 2 else os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+
+    class Missing(Exception):
+        pass
+
+    def db(d, n):
+        path = os.path.join(raw, d, n + "_results.db")
+        if not os.path.exists(path):
+            raise Missing(path)
+        return path
+
+    makers = {
         "star2p5d_r4_512cube_trace.md":
-            P.trace_md(db("prof_trace", "trace"), CMDS["trace"]),
+            lambda: P.trace_md(db("prof_trace", "trace"), CMDS["trace"]),
         "star2p5d_r4_512cube_traffic.md":
-            P.traffic_md(db("pmc_fetch", "fetch"), db("pmc_write", "write"),
+            lambda: P.traffic_md(db("pmc_fetch", "fetch"), db("pmc_write", "write"),
                          "star2p5d_kernel", "star2p5d_r4_f32", 1 << 30,
                          CMDS["fetch"], CMDS["write"], HEADLINE_BYTES),
         "jacobi_r1_512cube_and_f64_ragged_trace.md":
-            P.trace_md(db("prof_others", "others"), CMDS["others"]),
+            lambda: P.trace_md(db("prof_others", "others"), CMDS["others"], "fused"),
+        "blocked_r4_1024cube_counters.md":
+            lambda: P.counters_md([db("pmc_blocked_sq", "sq"), db("pmc_blocked_tcc", "tcc")],
+                          "wave2_kernel", [CMDS["blocked_sq"], CMDS["blocked_tcc"]],
+                          "blocked"),
+        "jacobi_r1_512cube_counters.md":
+            lambda: P.counters_md([db("pmc_others_sq", "sq"), db("pmc_others_tcc", "tcc")],
+                          "sweeps_fused_kernel", [CMDS["others_sq"], CMDS["others_tcc"]],
+                          "fused"),
+        "jacobi_r1_512cube_traffic.md":
+            lambda: P.traffic_md(db("pmc_others_fetch", "fetch"), db("pmc_others_write", "write"),
+                         "sweeps_fused_kernel", "jacobi_r1_f32", 1 << 30,
+                         CMDS["others_fetch"], CMDS["others_write"], JACOBI_PASS_BYTES,
+                         "fused"),
+        "apply_r4_f64_ragged_traffic.md":
+            lambda: P.traffic_md(db("pmc_others_fetch", "fetch"), db("pmc_others_write", "write"),
+                         "star2p5d_kernel", "apply_r4_f64", 1 << 30,
+                         CMDS["others_fetch"], CMDS["others_write"], F64_BYTES),
         "star2p5d_r4_512cube_counters.md":
-            P.counters_md([db("pmc_sq", "sq"), db("pmc_tcc", "tcc")],
+            lambda: P.counters_md([db("pmc_sq", "sq"), db("pmc_tcc", "tcc")],
                           "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
         "wave_pml_blocked_r4_1024cube_trace.md":
-            P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"]),
+            lambda: P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"], "blocked"),
     }
     for v in ("wave", "pml", "blocked"):
-        out["%s_r4_1024cube_traffic.md" % v] = P.traffic_md(
+        makers["%s_r4_1024cube_traffic.md" % v] = (lambda v=v: P.traffic_md(
             db("pmc_%s_fetch" % v, "fetch"), db("pmc_%s_write" % v, "write"),
             "wave2_kernel" if v == "blocked" else "star2p5d_kernel",
             "%s_r4_f32" % v, 1 << 30, CMDS["%s_fetch" % v],
-            CMDS["%s_write" % v], PASS_BYTES if v == "blocked" else WAVE_BYTES)
-    for name, text in out.items():
+            CMDS["%s_write" % v], PASS_BYTES if v == "blocked" else WAVE_BYTES,
+            "blocked" if v == "blocked" else "stream"))
+    for name, make in makers.items():
+        try:
+            text = make()
+        except Missing as e:
+            print("skipped %s (no %s)" % (name, e))
+            continue
         with open(os.path.join(prof, name), "w") as f:
             f.write(text)
-        print("wrote profiles/" + name)
+        print("wrote " + os.path.join(prof, name))
     return 0
 
 

@@ -30,11 +30,15 @@ import sqlite3
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", "star2p5d_kernel.h"),
-                  os.path.join(PKG, "csrc", "work_plan.h"),
-                  os.path.join(PKG, "csrc", "star2p5d.hip"),
-                  os.path.join(PKG, "csrc", "wave2_kernel.h"),
-                  os.path.join(PKG, "csrc", "wave2.hip")]
+_STREAM = ["star2p5d_kernel.h", "work_plan.h", "star2p5d.hip"]
+# The sources each summary's figures depend on: a summary is stale once any
+# of them changes (comments and whitespace aside).
+SOURCE_SETS = {
+    "stream": _STREAM,                                     # apply, wave, PML step
+    "blocked": _STREAM + ["wave2_kernel.h", "wave2.hip"],  # two-step pass
+    "fused": _STREAM + ["sweeps_fused_kernel.h", "sweeps_fused.hip",
+                        "pass_plan.h"],                    # fused Jacobi passes
+}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -47,12 +51,18 @@ def code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources: str = "stream") -> str:
+    """Hash of the code (comments and whitespace ignored) of one source set."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, encoding="utf-8") as f:
+    for name in SOURCE_SETS[sources]:
+        with open(os.path.join(PKG, "csrc", name), encoding="utf-8") as f:
             h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _stamp(sources: str) -> list:
+    return ["kernel_sources: " + sources + " (" + ", ".join(SOURCE_SETS[sources]) + ")",
+            "kernel_source_sha256_16: " + kernel_hash(sources), ""]
 
 
 def _db(path):
@@ -98,7 +108,7 @@ def counter_means(path, counter):
     return {n: (c, v) for n, c, v in rows}
 
 
-def trace_md(path, cmd) -> str:
+def trace_md(path, cmd, sources="stream") -> str:
     out = ["# Kernel trace summary", "",
            "Command (run from /tmp, repository at $REPO, raw output under $RAW):", "",
            "    " + cmd, "",
@@ -107,12 +117,12 @@ def trace_md(path, cmd) -> str:
     for n, c, t, a, mn, mx in kernel_stats(path):
         out.append("| %s | %d | %.1f | %.3f | %.3f | %.3f |" %
                    (n, c, t, a, mn, mx))
-    out += ["", "kernel_source_sha256_16: " + kernel_hash(), ""]
+    out += [""] + _stamp(sources)
     return "\n".join(out)
 
 
 def traffic_md(fetch, write, kernel, name, calib_bytes, cmd_fetch,
-               cmd_write, algorithmic=None) -> str:
+               cmd_write, algorithmic=None, sources="stream") -> str:
     f = counter_means(fetch, "FETCH_SIZE")
     w = counter_means(write, "WRITE_SIZE")
     if COPY_KERNEL not in f or COPY_KERNEL not in w:
@@ -143,8 +153,7 @@ def traffic_md(fetch, write, kernel, name, calib_bytes, cmd_fetch,
         out.append("")
     out += ["traffic_bytes_per_launch[%s]: %.0f" % (name, rd + wr),
             "read_bytes_per_launch[%s]: %.0f" % (name, rd),
-            "write_bytes_per_launch[%s]: %.0f" % (name, wr),
-            "kernel_source_sha256_16: " + kernel_hash(), ""]
+            "write_bytes_per_launch[%s]: %.0f" % (name, wr)] + _stamp(sources)
     return "\n".join(out)
 
 
@@ -158,7 +167,7 @@ RATIOS = [
 ]
 
 
-def counters_md(dbs, kernel, cmds) -> str:
+def counters_md(dbs, kernel, cmds, sources="stream") -> str:
     """Mean value per dispatch of every counter recorded for `kernel` in the
     given --pmc runs, plus a few derived ratios."""
     vals = {}
@@ -185,7 +194,16 @@ def counters_md(dbs, kernel, cmds) -> str:
             d = sum(vals[x][1] for x in den)
             if d > 0:
                 out.append("* %s: %.3f" % (label, vals[num][1] / d))
-    out += ["", "kernel_source_sha256_16: " + kernel_hash(), ""]
+    if "SQ_INSTS_VALU" in vals:
+        # VALU issue bound: a wave64 fp32 VALU instruction (packed FP32 off)
+        # holds a 16-lane SIMD for 4 cycles; 1024 SIMDs at 2.4 GHz
+        t = vals["SQ_INSTS_VALU"][1] * 4 / (1024 * 2.4e9)
+        out.append("* VALU issue time at 4 cycles per instruction on 1024 SIMDs "
+                   "at 2.4 GHz: %.4f ms per dispatch" % (t * 1e3))
+    out += [""]
+    for c in sorted(vals):
+        out.append("counter_mean[%s]: %.0f" % (c, vals[c][1]))
+    out += [""] + _stamp(sources)
     return "\n".join(out)
 
 
@@ -208,15 +226,17 @@ def main(argv=None):
     c.add_argument("dbs", nargs="+")
     c.add_argument("--kernel", required=True)
     c.add_argument("--cmd", action="append", default=[])
+    for sp in (t, r, c):
+        sp.add_argument("--sources", default="stream", choices=sorted(SOURCE_SETS))
     a = ap.parse_args(argv)
     if a.mode == "trace":
-        sys.stdout.write(trace_md(a.db, a.cmd))
+        sys.stdout.write(trace_md(a.db, a.cmd, a.sources))
     elif a.mode == "counters":
-        sys.stdout.write(counters_md(a.dbs, a.kernel, a.cmd))
+        sys.stdout.write(counters_md(a.dbs, a.kernel, a.cmd, a.sources))
     else:
         sys.stdout.write(traffic_md(a.fetch_db, a.write_db, a.kernel, a.name,
                                     a.calib_bytes, a.cmd_fetch, a.cmd_write,
-                                    a.algorithmic))
+                                    a.algorithmic, a.sources))
 
 
 if __name__ == "__main__":

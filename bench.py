@@ -39,13 +39,33 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
           "R=4 25-pt stencil at 512³ fp32")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "star2p5d_r4_512cube_traffic.md")
-WAVE_TRAFFIC = {v: os.path.join(ROOT, "profiles", "%s_r4_1024cube_traffic.md" % v)
+PROF = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROF, "star2p5d_r4_512cube_traffic.md")
+WAVE_TRAFFIC = {v: os.path.join(PROF, "%s_r4_1024cube_traffic.md" % v)
                 for v in ("wave", "pml", "blocked")}
+COUNTERS = {"headline": os.path.join(PROF, "star2p5d_r4_512cube_counters.md"),
+            "blocked": os.path.join(PROF, "blocked_r4_1024cube_counters.md"),
+            "jacobi": os.path.join(PROF, "jacobi_r1_512cube_counters.md")}
+JACOBI_TRAFFIC = os.path.join(PROF, "jacobi_r1_512cube_traffic.md")
+F64_TRAFFIC = os.path.join(PROF, "apply_r4_f64_ragged_traffic.md")
+OTHERS_TRACE = os.path.join(PROF, "jacobi_r1_512cube_and_f64_ragged_trace.md")
+# VALU issue rate: a wave64 fp32 VALU instruction holds a 16-lane SIMD for 4
+# cycles (packed FP32 is off); MI355X has 256 CUs x 4 SIMDs at 2.4 GHz
+VALU_CYCLES, SIMDS, CLOCK_HZ = 4, 1024, 2.4e9
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def _current(text: str) -> bool:
+    """Whether a profile summary was taken on the current kernel sources (its
+    source set's hash still matches)."""
+    from acoustic_wave_propagation_amd.profiling import SOURCE_SETS, kernel_hash
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    srcs = re.search(r"kernel_sources:\s*(\w+)", text)
+    name = srcs.group(1) if srcs else "stream"
+    return bool(m) and name in SOURCE_SETS and m.group(1) == kernel_hash(name)
 
 
 def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE, what="traffic"):
@@ -55,13 +75,52 @@ def recorded_traffic(kernel: str, path: str = TRAFFIC_FILE, what="traffic"):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
     t = re.search(r"%s_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" %
                   (what, re.escape(kernel)), text)
-    from acoustic_wave_propagation_amd.profiling import kernel_hash
-    if not m or not t or m.group(1) != kernel_hash():
+    if not t or not _current(text):
         return None
     return float(t.group(1))
+
+
+def recorded_counter(path: str, counter: str):
+    """Mean per dispatch of a counter in a committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    t = re.search(r"counter_mean\[%s\]:\s*([0-9.eE+]+)" % re.escape(counter), text)
+    if not t or not _current(text):
+        return None
+    return float(t.group(1))
+
+
+def recorded_calls(path: str, kernel_prefix: str):
+    """Calls of the kernels whose name starts with kernel_prefix in a
+    committed trace summary (current sources only); else None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if not _current(text):
+        return None
+    n = 0
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 3 and cells[1].startswith(kernel_prefix):
+            n += int(cells[2])
+    return n or None
+
+
+def valu_roofline(counters_path: str, kernel_s: float, launches: float = 1.0):
+    """VALU bound of a kernel from its committed SQ_INSTS_VALU: the issue time
+    of its VALU instructions spread over every SIMD, against the measured
+    time of `launches` dispatches (None if the counters are stale)."""
+    insts = recorded_counter(counters_path, "SQ_INSTS_VALU")
+    if insts is None:
+        return None
+    t = insts * launches * VALU_CYCLES / (SIMDS * CLOCK_HZ)
+    return dict(bound="alu", insts_per_dispatch=insts, issue_ms=round(t * 1e3, 5),
+                measured_ms=round(kernel_s * 1e3, 5), frac=round(t / kernel_s, 4),
+                derivation="SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x 2.4 GHz)")
 
 
 def host_cpu_model() -> str:
@@ -208,7 +267,8 @@ def bench_headline(torch, B, wl, args):
                       traffic_write=recorded_traffic("star2p5d_r4_f32",
                                                      what="write"),
                       read_floor=nbytes - 4 * pts, write_floor=4 * pts,
-                      kernel="star2p5d_kernel<float,4,false>"),
+                      kernel="star2p5d_kernel<float,4,false>",
+                      valu=valu_roofline(COUNTERS["headline"], mean)),
         gbs_wall=round(nbytes * args.steps / wall / 1e9, 1),
     )
     return res, host
@@ -285,19 +345,22 @@ def bench_wave(torch, B, wl, args,
                                     algorithmic_bytes_per_step=nbytes))
         if v == "blocked":
             # what a pass of two steps moves: the single step's reads plus
-            # a second written field
+            # a second written field.  achieved / frac are the pass kernel's
+            # own bytes over its own time; the per-step equivalent (20.09
+            # B/point per step, the single step's convention) is named apart.
             pass_b = nbytes + 4 * w.interior_points
-            res[v]["roofline"]["note"] = (
-                "achieved: per-step equivalent (20.09 B/point per step, "
-                "as for the single step); the pass itself moves "
-                "pass_bytes per two steps")
-            res[v]["roofline"]["pass_bytes"] = pass_b
-            res[v]["roofline"]["traffic_per"] = "pass (one launch, two steps)"
-            res[v]["roofline"]["limited_by"] = (
-                "on-chip work (VALU and LDS of the overlapped first step), "
-                "not HBM: see achieved_pass_bytes")
-            res[v]["roofline"]["achieved_pass_bytes"] = round(
-                pass_b / (2 * per) / 1e9, 1)
+            rl = res[v]["roofline"]
+            rl["achieved_step_equivalent"] = rl["achieved"]
+            rl["frac_step_equivalent"] = rl["frac"]
+            rl["achieved"] = round(pass_b / (2 * per) / 1e9, 1)
+            rl["frac"] = round(pass_b / (2 * per) / 1e9 / PEAK_HBM_GBS, 4)
+            rl["pass_bytes"] = pass_b
+            rl["traffic_per"] = "pass (one launch, two steps)"
+            rl["kernel"] = "wave2_kernel<float,4>"
+            rl["valu"] = valu_roofline(COUNTERS["blocked"], 2 * per)
+            rl["note"] = ("achieved/frac: pass bytes over pass time (one "
+                          "pass = two steps); *_step_equivalent: 20.09 "
+                          "B/point per step over the per-step time")
         if v == "regions":
             true_b = nbytes - 4 * inner
             res[v]["roofline"]["true_bytes_per_step"] = true_b
@@ -380,20 +443,40 @@ def bench_others(torch, B, wl, args):
     d = B.desc_init("f32", w.shape, w.radius, B.DIRICHLET_COPY)
     wall, durs = timed_launches(
         torch, lambda: B.stencil3d_jacobi(d, a, b, w.sweeps), runs, 1)
-    per = float(durs.mean()) / w.sweeps
+    call = float(durs.mean())
+    per = call / w.sweeps
     nbytes = star_bytes(w.interior, w.radius, 4)
+    # the call's own bytes: each fused pass reads and writes the field once
+    # (the sweep's algorithmic bytes); the pass count per call comes from
+    # the committed trace (fused-pass launches per boundary copy)
+    fused = recorded_calls(OTHERS_TRACE, "sweeps_fused_kernel")
+    copies = recorded_calls(OTHERS_TRACE, "shell_copy_kernel")
+    passes = fused / copies if fused and copies else None
+    call_b = nbytes * passes if passes else None
     res[w.name] = dict(
         value=round(w.interior_points * w.sweeps * runs / wall / 1e9, 2),
         unit="GPoints/s", ms_per_sweep=round(per * 1e3, 5),
+        ms_per_call=round(call * 1e3, 5),
         sweeps_per_run=w.sweeps, runs=runs,
-        roofline=dict(bound="hbm", achieved=round(nbytes / per / 1e9, 1),
+        roofline=dict(bound="hbm",
+                      achieved=round(call_b / call / 1e9, 1) if call_b else None,
                       peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
+                      frac=round(call_b / call / 1e9 / PEAK_HBM_GBS, 4)
+                      if call_b else None,
+                      passes_per_call=passes, bytes_per_call=call_b,
+                      achieved_sweep_equivalent=round(nbytes / per / 1e9, 1),
+                      frac_sweep_equivalent=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
                       algorithmic_bytes_per_sweep=nbytes,
-                      note="per-sweep mean incl. the one boundary copy; "
-                           "the library fuses several sweeps per pass over "
-                           "HBM (temporal blocking), so the per-sweep rate "
-                           "can exceed the one-read-one-write floor"))
+                      kernel="sweeps_fused_kernel<float,1,5>",
+                      traffic=recorded_traffic("jacobi_r1_f32", JACOBI_TRAFFIC),
+                      valu=valu_roofline(COUNTERS["jacobi"], call / passes)
+                      if passes else None,
+                      note="achieved/frac: the call's own bytes (one read and "
+                           "one write of the field per fused pass) over the "
+                           "call time, boundary copy included; "
+                           "*_sweep_equivalent: one sweep's algorithmic bytes "
+                           "over the per-sweep time, which temporal blocking "
+                           "lets exceed the floor"))
     del a, b
     if not args.no_cpu:
         import oracle
@@ -425,7 +508,9 @@ def bench_others(torch, B, wl, args):
         roofline=dict(bound="hbm", achieved=round(nbytes / per / 1e9, 1),
                       peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
-                      algorithmic_bytes=nbytes))
+                      algorithmic_bytes=nbytes,
+                      kernel="star2p5d_kernel<double,4,false>",
+                      traffic=recorded_traffic("apply_r4_f64", F64_TRAFFIC)))
     del inp, out
     torch.cuda.empty_cache()
     if not args.no_cpu:
@@ -528,8 +613,10 @@ def main():
         return
     if args.only_others:
         for k, v in bench_others(torch, B, wl, args).items():
-            log("%s: %.1f GPoints/s, %.1f GB/s"
+            log("%s: %.1f GPoints/s, %s GB/s"
                 % (k, v["value"], v["roofline"]["achieved"]))
+        if args.calib:
+            calib_copy(torch)
         return
     head, host = bench_headline(torch, B, wl, args)
     log("headline: %.1f GPoints/s, kernel %.4f ms, %.1f GB/s"
@@ -543,7 +630,7 @@ def main():
     others = None if args.no_others else bench_others(torch, B, wl, args)
     if others:
         for k, v in others.items():
-            log("%s: %.1f GPoints/s, %.1f GB/s"
+            log("%s: %.1f GPoints/s, %s GB/s"
                 % (k, v["value"], v["roofline"]["achieved"]))
     cpu = None if args.no_cpu else cpu_baseline(wl, host, args.cpu_budget)
 

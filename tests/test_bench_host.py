@@ -53,7 +53,8 @@ def test_recorded_traffic_tracks_the_kernel_source(tmp_path):
     good.write_text("traffic_bytes_per_launch[k_r4]: 1234567\n"
                     "read_bytes_per_launch[k_r4]: 1000000\n"
                     "write_bytes_per_launch[k_r4]: 234567\n"
-                    "kernel_source_sha256_16: %s\n" % kernel_hash())
+                    "kernel_sources: stream\n"
+                    "kernel_source_sha256_16: %s\n" % kernel_hash("stream"))
     assert b.recorded_traffic("k_r4", str(good)) == 1234567.0
     assert b.recorded_traffic("k_r4", str(good), what="read") == 1000000.0
     assert b.recorded_traffic("k_r4", str(good), what="write") == 234567.0
@@ -63,6 +64,41 @@ def test_recorded_traffic_tracks_the_kernel_source(tmp_path):
                      "kernel_source_sha256_16: 0000000000000000\n")
     assert b.recorded_traffic("k_r4", str(stale)) is None
     assert b.recorded_traffic("k_r4", str(tmp_path / "missing.md")) is None
+    # a summary stamped with another source set checks that set's hash
+    other = tmp_path / "o.md"
+    other.write_text("traffic_bytes_per_launch[k_r4]: 5\n"
+                     "kernel_sources: blocked\n"
+                     "kernel_source_sha256_16: %s\n" % kernel_hash("blocked"))
+    assert b.recorded_traffic("k_r4", str(other)) == 5.0
+    assert kernel_hash("blocked") != kernel_hash("stream")
+
+
+def test_recorded_counters_and_valu_bound(tmp_path):
+    """Counter means and the VALU issue bound from a counter summary; stale
+    summaries give None."""
+    b = _bench()
+    from acoustic_wave_propagation_amd.profiling import kernel_hash
+    c = tmp_path / "c.md"
+    c.write_text("counter_mean[SQ_INSTS_VALU]: 614400000\n"
+                 "kernel_sources: stream\n"
+                 "kernel_source_sha256_16: %s\n" % kernel_hash("stream"))
+    assert b.recorded_counter(str(c), "SQ_INSTS_VALU") == 614400000.0
+    assert b.recorded_counter(str(c), "SQ_WAVES") is None
+    v = b.valu_roofline(str(c), 2e-3)
+    # 614.4e6 instructions x 4 cycles / (1024 SIMDs x 2.4e9 Hz) = 1 ms
+    assert abs(v["issue_ms"] - 1.0) < 1e-9 and abs(v["frac"] - 0.5) < 1e-9
+    c.write_text("counter_mean[SQ_INSTS_VALU]: 1\n"
+                 "kernel_source_sha256_16: 0000000000000000\n")
+    assert b.valu_roofline(str(c), 1.0) is None
+    t = tmp_path / "t.md"
+    t.write_text("| kernel | calls |\n|---|---|\n"
+                 "| sweeps_fused_kernel<f32> | 40 | 1 | 1 | 1 | 1 |\n"
+                 "| shell_copy_kernel<f32> | 20 | 1 | 1 | 1 | 1 |\n"
+                 "kernel_sources: fused\n"
+                 "kernel_source_sha256_16: %s\n" % kernel_hash("fused"))
+    assert b.recorded_calls(str(t), "sweeps_fused_kernel") == 40
+    assert b.recorded_calls(str(t), "shell_copy_kernel") == 20
+    assert b.recorded_calls(str(t), "nothing") is None
 
 
 def test_kernel_hash_ignores_comments():
