@@ -22,7 +22,8 @@ HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
 EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
            "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
            "wave_step", "wave_step_pml", "wave_add_source", "wave_run",
-           "wave_run_pml", "wave_run_blocked", "wave_run_blocked_noalloc")
+           "wave_run_pml", "wave_run_blocked", "wave_run_pml_blocked",
+           "wave_run_blocked_noalloc")
 
 # largest field wave_run_blocked_noalloc accepts (ST_NOALLOC_FIELD_BYTES_MAX)
 NOALLOC_FIELD_BYTES_MAX = 32 << 20
@@ -82,6 +83,10 @@ def lib():
             "wave_run_blocked": (i32, [D, vp, vp, vp, vp, vp, vp, dp, dp, i32,
                                        i64, i64, i64,
                                        ctypes.POINTER(ctypes.c_double), vp]),
+            "wave_run_pml_blocked": (i32, [D, vp, vp, vp, vp, vp, vp, dp, dp,
+                                           i32, i64, i64, i64,
+                                           ctypes.POINTER(ctypes.c_double),
+                                           vp]),
             "wave_run_blocked_noalloc": (i32, [D, vp, vp, vp, vp, dp, dp, i32,
                                                i64, i64, i64,
                                                ctypes.POINTER(ctypes.c_double),
@@ -238,18 +243,20 @@ def wave_run_pml(d: Desc, u_prev, u, vel2, eta, dt: float, h: float,
 
 def wave_run_blocked(d: Desc, u_prev, u, work0, work1, vel2, eta, dt: float,
                      h: float, nsteps: int, src=(0, 0, 0), src_trace=None,
-                     stream=None):
+                     stream=None, pml: bool = False):
     """Time-blocked leapfrog over four buffers (two steps per pass where the
     library has the kernel); returns (older, newest): level k of the field
-    lives in (u_prev, u, work0, work1)[k % 4]."""
+    lives in (u_prev, u, work0, work1)[k % 4].  ``pml`` calls
+    ``wave_run_pml_blocked`` (the PML kernel's step)."""
     n = int(nsteps)
     tr = _trace(src_trace, n)
     ix, iy, iz = src
-    _check(lib().wave_run_blocked(
+    name = "wave_run_pml_blocked" if pml else "wave_run_blocked"
+    _check(getattr(lib(), name)(
         ctypes.byref(d), _ptr(u_prev, d, "u_prev"), _ptr(u, d, "u"),
         _ptr(work0, d, "work0"), _ptr(work1, d, "work1"), _ptr(vel2, d, "vel2"),
         _ptr(eta, d, "eta"), float(dt), float(h), n, ix, iy, iz, tr,
-        _stream(u, stream)), "wave_run_blocked")
+        _stream(u, stream)), name)
     b = (u_prev, u, work0, work1)
     return b[n % 4], b[(n + 1) % 4]
 
@@ -267,3 +274,11 @@ def wave_run_blocked_noalloc(d: Desc, u_prev, u, vel2, eta, dt: float,
         _ptr(vel2, d, "vel2"), _ptr(eta, d, "eta"), float(dt), float(h), n,
         ix, iy, iz, tr, _stream(u, stream)), "wave_run_blocked_noalloc")
     return (u_prev, u) if n % 2 == 0 else (u, u_prev)
+
+
+def wave_run_pml_blocked(d: Desc, u_prev, u, work0, work1, vel2, eta,
+                         dt: float, h: float, nsteps: int, src=(0, 0, 0),
+                         src_trace=None, stream=None):
+    """wave_run_blocked with the PML kernel's step; returns (older, newest)."""
+    return wave_run_blocked(d, u_prev, u, work0, work1, vel2, eta, dt, h,
+                            nsteps, src, src_trace, stream, pml=True)

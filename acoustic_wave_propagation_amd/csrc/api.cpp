@@ -231,7 +231,7 @@ ST_EXPORT int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u, const
 static int blocked_loop(const stencil3d_desc &d, void *u_prev, void *u, void *work0, void *work1,
                         const void *vel2, const void *eta, double wscale, int nsteps,
                         int64_t src_x, int64_t src_y, int64_t src_z, const double *src_trace,
-                        int cus, hipStream_t s) {
+                        int cus, hipStream_t s, bool pml) {
     if (nsteps <= 0) return ST_OK;
     int st = st::launch_shell_copy(d, u, work0, s);
     if (!st) st = st::launch_shell_copy(d, u, work1, s);
@@ -245,10 +245,10 @@ static int blocked_loop(const stencil3d_desc &d, void *u_prev, void *u, void *wo
             const st::Wave2Source src{src_trace != nullptr, src_x, src_y, src_z,
                                       src_trace ? src_trace[n] : 0.0,
                                       src_trace ? src_trace[n + 1] : 0.0};
-            st = st::launch_wave2(d, p, c, o1, o2, vel2, eta, wscale, src, cus, s);
+            st = st::launch_wave2(d, p, c, o1, o2, vel2, eta, wscale, src, cus, s, pml);
             n += 2;
         } else {
-            st = launch_wave(d, c, o1, p, vel2, eta, wscale, cus, s, false);
+            st = launch_wave(d, c, o1, p, vel2, eta, wscale, cus, s, pml);
             if (!st && src_trace) st = st::launch_add_source(d, o1, idx, src_trace[n], s);
             n += 1;
         }
@@ -257,17 +257,34 @@ static int blocked_loop(const stencil3d_desc &d, void *u_prev, void *u, void *wo
     return ST_OK;
 }
 
-ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
-                               void *work1, const void *vel2, const void *eta, double dt,
-                               double h, int nsteps, int64_t src_x, int64_t src_y,
-                               int64_t src_z, const double *src_trace, void *stream) {
+static int blocked_common(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
+                          void *work1, const void *vel2, const void *eta, double dt, double h,
+                          int nsteps, int64_t src_x, int64_t src_y, int64_t src_z,
+                          const double *src_trace, void *stream, bool pml) {
     int st = st::check::blocked_args(d, u_prev, u, work0, work1, vel2, eta, dt, h, nsteps, src_x,
                                      src_y, src_z, src_trace);
     if (st) return st;
     const int cus = current_cus(&st);
     if (st) return st;
     return blocked_loop(*d, u_prev, u, work0, work1, vel2, eta, (dt * dt) / (h * h), nsteps,
-                        src_x, src_y, src_z, src_trace, cus, static_cast<hipStream_t>(stream));
+                        src_x, src_y, src_z, src_trace, cus, static_cast<hipStream_t>(stream),
+                        pml);
+}
+
+ST_EXPORT int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
+                               void *work1, const void *vel2, const void *eta, double dt,
+                               double h, int nsteps, int64_t src_x, int64_t src_y,
+                               int64_t src_z, const double *src_trace, void *stream) {
+    return blocked_common(d, u_prev, u, work0, work1, vel2, eta, dt, h, nsteps, src_x, src_y,
+                          src_z, src_trace, stream, false);
+}
+
+ST_EXPORT int wave_run_pml_blocked(const stencil3d_desc *d, void *u_prev, void *u, void *work0,
+                                   void *work1, const void *vel2, const void *eta, double dt,
+                                   double h, int nsteps, int64_t src_x, int64_t src_y,
+                                   int64_t src_z, const double *src_trace, void *stream) {
+    return blocked_common(d, u_prev, u, work0, work1, vel2, eta, dt, h, nsteps, src_x, src_y,
+                          src_z, src_trace, stream, true);
 }
 
 // wave_run_blocked with the two work fields in the library's static
@@ -295,7 +312,7 @@ ST_EXPORT int wave_run_blocked_noalloc(const stencil3d_desc *d, void *u_prev, vo
     const double wscale = (dt * dt) / (h * h);
     const int bulk = nsteps / 4 * 4;
     st = blocked_loop(*d, u_prev, u, work0, work1, vel2, eta, wscale, bulk, src_x, src_y, src_z,
-                      src_trace, cus, s);
+                      src_trace, cus, s, false);
     if (st) return st;
     const int64_t idx = src_x + d->nx * (src_y + d->ny * src_z);
     return leapfrog(*d, u_prev, u, vel2, eta, wscale, bulk, nsteps, idx, src_trace, cus, s,

@@ -23,12 +23,18 @@ using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>;
 // fp64: 2 x 1 points per thread (16-byte groups), same thread layout; the
 // extended tile is 32 x 40, the output tile 24 x 32 at R = 4.
 using Wave2F64 = Wave2Cfg<2, 1, 16, 40, 3, true, true, 2, true>;
+// PML step (eta's 7-point coupling in both stages): the eta register ring
+// and the two stages' eta tiles need more registers and LDS than three waves
+// per SIMD leave, so 512 threads at two waves per SIMD over a 64 x 32
+// extended tile (fp32; output tile 56 x 24 at R = 4) or 32 x 32 (fp64).
+using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true>;
+using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true>;
 
-template <typename T, int R, class C>
+template <typename T, int R, class C, bool E7>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
              const void *vel2, const void *eta, double wscale, const Wave2Source &src, int cus,
              hipStream_t s) {
-    using S = Wave2Shape<R, C>;
+    using S = Wave2Shape<R, C, E7>;
     const int64_t ix = d.nx - 2 * R, iy = d.ny - 2 * R, iz = d.nz - 2 * R;
     const int tiles_x = (int)((ix + S::TX - 1) / S::TX);
     const int tiles_y = (int)((iy + S::TY - 1) / S::TY);
@@ -48,8 +54,20 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
     g.sz = src.on ? (int32_t)src.z : -1;
     g.s0 = (T)src.v0;
     g.s1 = (T)src.v1;
-    hipLaunchKernelGGL((wave2_kernel<T, R, C>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s, g);
+    hipLaunchKernelGGL((wave2_kernel<T, R, C, E7>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s, g);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
+}
+
+template <typename T, class C, bool E7>
+int launch_r(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
+             const void *vel2, const void *eta, double wscale, const Wave2Source &src, int cus,
+             hipStream_t s) {
+    switch (d.radius) {
+    case 1: return launch_t<T, 1, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
+    case 2: return launch_t<T, 2, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
+    case 3: return launch_t<T, 3, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
+    }
+    return launch_t<T, 4, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
 }
 
 }  // namespace
@@ -58,24 +76,17 @@ bool wave2_available(const stencil3d_desc &d) { return d.radius >= 1 && d.radius
 
 int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
                  void *out2, const void *vel2, const void *eta, double wscale,
-                 const Wave2Source &src, int cus, hipStream_t stream) {
+                 const Wave2Source &src, int cus, hipStream_t stream, bool pml) {
     if (!wave2_available(d)) return ST_ERR_ARG;
-    if (d.dtype == ST_F64) {
-        switch (d.radius) {
-        case 1: return launch_t<double, 1, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-        case 2: return launch_t<double, 2, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-        case 3: return launch_t<double, 3, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-        }
-        return launch_t<double, 4, Wave2F64>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
-                                             stream);
-    }
-    switch (d.radius) {
-    case 1: return launch_t<float, 1, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-    case 2: return launch_t<float, 2, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-    case 3: return launch_t<float, 3, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, stream);
-    }
-    return launch_t<float, 4, Wave2F32>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
-                                        stream);
+    if (d.dtype == ST_F64)
+        return pml ? launch_r<double, Wave2F64Pml, true>(d, u_prev, u, out1, out2, vel2, eta,
+                                                           wscale, src, cus, stream)
+                   : launch_r<double, Wave2F64, false>(d, u_prev, u, out1, out2, vel2, eta,
+                                                         wscale, src, cus, stream);
+    return pml ? launch_r<float, Wave2F32Pml, true>(d, u_prev, u, out1, out2, vel2, eta, wscale,
+                                                     src, cus, stream)
+               : launch_r<float, Wave2F32, false>(d, u_prev, u, out1, out2, vel2, eta, wscale,
+                                                   src, cus, stream);
 }
 
 }  // namespace st

@@ -80,7 +80,7 @@ struct Wave2Cfg {
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
 
-template <int R, class C>
+template <int R, class C, bool E7 = false>
 struct Wave2Shape {
     static constexpr int D = 1;                      // window prefetch (planes)
     static constexpr int XE = round_up(R, C::VX);    // columns added per side
@@ -94,12 +94,27 @@ struct Wave2Shape {
     static constexpr int NV = ring_fit(U, R + 1);      // vel2/eta ring slots
     static constexpr int FILL = 2 * R;               // steps before the first u^{n+2} plane
     static constexpr int PROLOGUE = FILL + 2 * R + D;
+    // PML step: eta planes q1+1 down to min(q1-1, q2+1) in registers (the
+    // ring padded to divide the unroll); plane q1+d sits in slot
+    // (k + d + EOFF) mod NE in step k
+    static constexpr int EOFF = R - 1 > 1 ? R - 1 : 1;
+    static constexpr int NE = E7 ? ring_fit(U, EOFF + 2) : 1;
 };
 
-template <typename T, int R, class C>
+// E7: two steps of the PML kernel's update (wave_step_pml): each stage adds
+// the eta-gradient coupling sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) -
+// u(p-e_a)) / (4 h^2) of its own step, with the operations of
+// star2p5d_kernel's PML step in the same order.  eta of plane q1+1 is loaded
+// in step k with the epilogue fields into a register ring of the planes
+// q1+1 .. q2+1.  Stage 1 takes eta's z neighbours from that ring and its
+// in-plane neighbours from an eta tile of plane q1 on E plus the 1-wide ring
+// around E (loaded one step ahead; two sets).  Each step also writes eta of
+// plane q2+1 on E into one of four stage-2 eta tiles, so stage 2 finds
+// planes q2-1, q2 and q2+1 in LDS (T's ring lies inside E).
+template <typename T, int R, class C, bool E7 = false>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
     wave2_kernel(Wave2Args<T> g) {
-    using S = Wave2Shape<R, C>;
+    using S = Wave2Shape<R, C, E7>;
     const StarArgs<T> &a = g.s;
     constexpr int VX = C::VX, VY = C::VY, LX = C::LX, NT = C::NT, EX = C::EX, EY = C::EY;
     constexpr int D = S::D, XE = S::XE, YE = S::YE, TX = S::TX, TY = S::TY;
@@ -119,10 +134,22 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     constexpr int NTT = (TX / VX) * (TY / VY);  // threads whose points lie in T
     constexpr int S1 = C::PSTAGE ? 2 : LB;      // stage-1 tile sets
     constexpr int T2S = C::T2S;                 // stage-2 tile sets
+    constexpr int NE = S::NE;                   // eta register ring (PML step)
+    // the vel2/eta ring of stage 2 holds vel2 only in the PML step (stage 2
+    // takes eta from the register ring)
+    constexpr int NVF = E7 ? 1 : 2;
     constexpr int VBASE = (S1 + T2S) * LTILE;
-    constexpr int SBASE = VBASE + (C::VRING ? NV * 2 * VY * NTT * VX : 0);
+    constexpr int SBASE = VBASE + (C::VRING ? NV * NVF * VY * NTT * VX : 0);
     constexpr int NU = NYU + NXU;               // halo units
     constexpr int LDUMMY = SBASE + (C::PSTAGE ? LB * NU * VX : 0);
+    // PML step: eta tiles, rows -1 .. EY of E with u's pitch and columns
+    // (2 stage-1 sets, 4 stage-2 sets), then their sink; eta ring units:
+    // the rows above and below E (LX groups each) and the group left and
+    // right of every row of E
+    constexpr int ETILE = E7 ? (EY + 2) * LP : 0;
+    constexpr int EBASE = LDUMMY + VX;
+    constexpr int EDUMMY = EBASE + 6 * ETILE;
+    constexpr int NEU = 2 * LX + 2 * EY;
     constexpr uint32_t ES = sizeof(T);
     constexpr bool DIFF = std::is_same<T, double>::value;
     static_assert(TX > 0 && TY > 0, "extended tile too small");
@@ -132,8 +159,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     static_assert(XE % VX == 0 && YE % VY == 0 && TY % VY == 0, "whole threads in T");
     static_assert(64 % LX == 0, "a wave covers whole thread rows");
     static_assert(T2S == 1 || T2S == 2, "one or two stage-2 tile sets");
+    static_assert(!E7 || (NE >= S::EOFF + 2 && U % NE == 0 && NEU <= NT && VY == 1),
+                  "PML step: eta ring, one eta unit per thread, one row per thread");
 
-    __shared__ __align__(16) T lds[LDUMMY + VX];
+    __shared__ __align__(16) T lds[E7 ? EDUMMY + VX : LDUMMY + VX];
     T *const tile2 = lds + S1 * LTILE;     // stage 2: u^{n+1} at q2
 
     const int tid = threadIdx.x;
@@ -225,19 +254,47 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     const bool wave_in_t = PAIR ? wrow0 + 64 / LX - 1 >= 2 * R
                                    : wrow0 < YE + TY && wrow0 + 64 / LX * VY > YE;
     auto vring = [&](int s, int f, int j) {
-        return lds + VBASE + (((s * 2 + f) * VY + j) * NTT + tt) * VX;
+        return lds + VBASE + (((s * NVF + f) * VY + j) * NTT + tt) * VX;
     };
+    // PML step: this thread's eta ring unit (plane q1 of the next step) and
+    // its place in the stage-1 eta tile
+    uint32_t eh_off = kOOB;
+    int eh_l = -1;
+    if (E7 && tid < NEU) {
+        if (tid < 2 * LX) {
+            const int side = tid / LX, gi = tid - side * LX;
+            eh_off = off_of(side ? ey0 + EY : ey0 - 1, ex0 + gi * VX);
+            eh_l = (side ? EY + 1 : 0) * LP + PADL + gi * VX;
+        } else {
+            // the group ending at column ex0-1, or starting at ex0+EX
+            const int xu = tid - 2 * LX, side = xu / EY, row = xu - side * EY;
+            eh_off = off_of(ey0 + row, side ? ex0 + EX : ex0 - VX);
+            eh_l = (1 + row) * LP + (side ? PADL + EX : PADL - VX);
+        }
+    }
+    T *const eh_dst = eh_l >= 0 ? lds + EBASE + eh_l : lds + EDUMMY;
+    const int eh_set_stride = eh_l >= 0 ? ETILE : 0;
 
     T w0[W0][VY][VX];  // u^n, planes q1-R .. q1+R plus D in flight
     T ws[WS][VY][VX];  // u^{n+1}, the last WS stage-1 planes
     T up[VY][VX], v2[VY][VX], et[VY][VX];  // u^{n-1}, vel2, eta at q1
     T hs[2][VX];       // halo unit in flight
+    // PML step: eta plane q1 + d in slot (k + d + EOFF) mod NE, and the eta
+    // ring unit of plane q1 in slot k mod 2
+    T ew[NE][VY][VX];
+    T ehs[2][VX];
 #pragma unroll
     for (int p = 0; p < WS; ++p)
 #pragma unroll
         for (int j = 0; j < VY; ++j)
 #pragma unroll
             for (int i = 0; i < VX; ++i) ws[p][j][i] = T(0);
+#pragma unroll
+    for (int p = 0; p < NE; ++p)
+#pragma unroll
+        for (int j = 0; j < VY; ++j)
+#pragma unroll
+            for (int i = 0; i < VX; ++i) ew[p][j][i] = T(0);
 
     auto prsrc = [&](const T *base, int q, bool need) {
         need = need && q >= 0 && q < nz;
@@ -257,6 +314,15 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
 #pragma unroll
         for (int j = 0; j < VY; ++j) bload<T, VX>(r, loff[j], w0[sl][j]);
     });
+    if constexpr (E7) {
+        static_for<0, 2>([&](auto dc) {
+            constexpr int d = decltype(dc)::value - 1;  // planes q0-1, q0
+            const rsrc_t r = prsrc(a.eta, q0 + d, true);
+#pragma unroll
+            for (int j = 0; j < VY; ++j) bload<T, VX>(r, loff[j], ew[(d + S::EOFF) % NE][j]);
+        });
+        bload<T, VX>(prsrc(a.eta, q0, true), eh_off, ehs[0]);
+    }
     {
         T hp[LB - 1][VX];
         static_for<0, LB - 1>([&](auto hc) {
@@ -280,8 +346,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
 
     // in-plane and z sums of one stage: the same operations, in the same
     // order, as star2p5d_kernel; zv(dz, j, i) is the stage input at plane
-    // offset dz of the thread's own point (j, i)
-    auto laplacian = [&](const T *tile, auto zv, T (&acc_out)[VY][VX]) {
+    // offset dz of the thread's own point (j, i).  coupling(j, i, u(x-1),
+    // u(x+1), u(y-1), u(y+1), u(z-1), u(z+1), acc) returns the sum with the
+    // PML step's eta-gradient term added (the plain step passes acc through)
+    auto laplacian = [&](const T *tile, auto zv, T (&acc_out)[VY][VX], auto coupling) {
         T xs[VY][VX + 2 * R];  // row segment, columns ex-R .. ex+VX+R-1
         T lg[VY][VX], rg[VY][VX];
 #pragma unroll
@@ -339,7 +407,13 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                         acc = fma(a.cx[kz - 1], xm + xp, acc);
                     }
                 });
-                acc_out[j][i] = acc;
+                acc_out[j][i] = coupling(
+                    j, i, xs[j][R + i - 1], xs[j][R + i + 1],
+                    j > 0 ? zv(std::integral_constant<int, 0>{}, j > 0 ? j - 1 : 0, i) : ys[R - 1][i],
+                    j + 1 < VY ? zv(std::integral_constant<int, 0>{}, j + 1 < VY ? j + 1 : 0, i)
+                               : ys[R][i],
+                    zv(std::integral_constant<int, -1>{}, j, i),
+                    zv(std::integral_constant<int, 1>{}, j, i), acc);
             }
         if constexpr (R < VX) {
 #pragma unroll
@@ -380,7 +454,17 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             constexpr int T2 = kk % T2S;                 // stage-2 tile set
             constexpr int S1SET = kk % S1;               // stage-1 tile set
             constexpr int NXT = (kk + 1) % LB;           // staging slot of step k+1
+            // PML step: eta ring slots of planes q1-1, q1, q1+1 and q2+1;
+            // stage-1 eta tile set
+            constexpr int EO = S::EOFF;
+            constexpr int EM1 = (kk + EO - 1) % NE, EC1 = (kk + EO) % NE, EP1 = (kk + EO + 1) % NE;
+            constexpr int EW2 = (kk + EO + 1 - R) % NE;
+            constexpr int ES1 = kk % 2;
             const int k = k0 + kk;
+            // stage-2 eta tile sets of planes q2+1 (written now), q2, q2-1
+            T *const e2p = lds + EBASE + (2 + (k & 3)) * ETILE;
+            T *const e2c = lds + EBASE + (2 + ((k + 3) & 3)) * ETILE;
+            T *const e2m = lds + EBASE + (2 + ((k + 2) & 3)) * ETILE;
             const int q1 = q0 + k, q2 = q1 - R;
             const bool in1 = q1 >= R && q1 < nz - R;
             T v2b[VY][VX] = {}, etb[VY][VX] = {};  // vel2, eta at q2 (stage 2)
@@ -390,19 +474,30 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             //    halo ring of step k + LB -- the same plane (D = 1)
             {
                 const bool need = in1 && k < nsteps;
-                const rsrc_t rp = prsrc(a.u_prev, q1, need), rv = prsrc(a.vel2, q1, need),
-                             re = prsrc(a.eta, q1, need);
+                const rsrc_t rp = prsrc(a.u_prev, q1, need), rv = prsrc(a.vel2, q1, need);
 #pragma unroll
                 for (int j = 0; j < VY; ++j) {
                     bload<T, VX>(rp, loff[j], up[j]);
                     bload<T, VX>(rv, loff[j], v2[j]);
-                    bload<T, VX>(re, loff[j], et[j]);
+                }
+                if constexpr (E7) {
+                    // eta of plane q1+1 (stage 1's z neighbour now, the centre
+                    // next step) and its ring units (next step's eta tile)
+                    const rsrc_t re = prsrc(a.eta, q1 + 1, k < nsteps);
+#pragma unroll
+                    for (int j = 0; j < VY; ++j) bload<T, VX>(re, loff[j], ew[EP1][j]);
+                    bload<T, VX>(re, eh_off, ehs[(kk + 1) % 2]);
+                } else {
+                    const rsrc_t re = prsrc(a.eta, q1, need);
+#pragma unroll
+                    for (int j = 0; j < VY; ++j) bload<T, VX>(re, loff[j], et[j]);
                 }
             }
             if constexpr (!C::VRING) {
-                // stage 2's vel2 and eta of plane q2 (threads with points in T)
+                // stage 2's vel2 and eta of plane q2 (threads with points in T;
+                // the PML step keeps eta in its register ring)
                 const bool need = q2 >= R && q2 < nz - R;
-                const rsrc_t rv = prsrc(a.vel2, q2, need), re = prsrc(a.eta, q2, need);
+                const rsrc_t rv = prsrc(a.vel2, q2, need), re = prsrc(a.eta, q2, need && !E7);
 #pragma unroll
                 for (int j = 0; j < VY; ++j) {
                     bload<T, VX>(rv, tthr ? loff[j] : kOOB, v2b[j]);
@@ -427,6 +522,17 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 lds_store_group<T, VX>(lds + S1SET * LTILE + (lrow0 + j) * LP + lcol, w0[CS][j]);
                 lds_store_group<T, VX>(tile2 + T2 * LTILE + (lrow0 + j) * LP + lcol, ws[WC2][j]);
             }
+            if constexpr (E7) {
+                // eta of plane q1 (own points and the ring) into stage 1's
+                // eta tile, eta of plane q2+1 (own points) into a stage-2 one
+#pragma unroll
+                for (int j = 0; j < VY; ++j) {
+                    lds_store_group<T, VX>(lds + EBASE + ES1 * ETILE + (1 + ly * VY + j) * LP + lcol,
+                                           ew[EC1][j]);
+                    lds_store_group<T, VX>(e2p + (1 + ly * VY + j) * LP + lcol, ew[EW2][j]);
+                }
+                lds_store_group<T, VX>(eh_dst + ES1 * eh_set_stride, ehs[kk % 2]);
+            }
             __syncthreads();
             if constexpr (!C::PSTAGE) {
                 // halo ring of step k + LB - 1 into its set, last read in
@@ -443,6 +549,32 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                 lds_store_group<T, VX>(h_dst + (S1SET ^ 1) * h_set_stride, hv);
             }
 
+            // eta-gradient coupling of a stage (PML step): eta of the stage's
+            // plane at the thread's points in ec, of the planes below and
+            // above in em / ep, in-plane neighbours outside the thread's
+            // points from the eta tile etl
+            auto coupling = [&](const T(&ec)[VY][VX], const T(&em)[VY][VX], const T(&ep)[VY][VX],
+                                const T *etl) {
+                return [&, etl](int j, int i, T uxm, T uxp, T uym, T uyp, T uzm, T uzp,
+                                T acc) -> T {
+                    if constexpr (!E7) {
+                        return acc;
+                    } else {
+                        const int er = 1 + ly * VY + j;
+                        const T exm = i > 0 ? ec[j][i > 0 ? i - 1 : 0] : etl[er * LP + lcol - 1];
+                        const T exp1 =
+                            i + 1 < VX ? ec[j][i + 1 < VX ? i + 1 : 0] : etl[er * LP + lcol + VX];
+                        const T eym = j > 0 ? ec[j > 0 ? j - 1 : 0][i] : etl[(er - 1) * LP + lcol + i];
+                        const T eyp =
+                            j + 1 < VY ? ec[j + 1 < VY ? j + 1 : 0][i] : etl[(er + 1) * LP + lcol + i];
+                        T gg = (exp1 - exm) * (uxp - uxm);
+                        gg = fma(eyp - eym, uyp - uym, gg);
+                        gg = fma(ep[j][i] - em[j][i], uzp - uzm, gg);
+                        return fma(a.gw, gg, acc);
+                    }
+                };
+            };
+
             // 3. stage 1: step n+1 at plane q1 on E
             {
                 T acc[VY][VX], res[VY][VX];
@@ -451,13 +583,13 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                               constexpr int dz = decltype(dzc)::value;
                               return w0[((CS + dz) % W0 + W0) % W0][j][i];
                           },
-                          acc);
+                          acc, coupling(ew[EC1], ew[EM1], ew[EP1], lds + EBASE + ES1 * ETILE));
 #pragma unroll
                 for (int j = 0; j < VY; ++j)
 #pragma unroll
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = w0[CS][j][i];
-                        const T e = et[j][i];
+                        const T e = E7 ? ew[EC1][j][i] : et[j][i];
                         const T u1 = (T(2) * ctr - (T(1) - e) * up[j][i] + v2[j][i] * acc[j][i]) /
                                      (T(1) + e);
                         res[j][i] = (in1 && rin[j] && cin[i]) ? u1 : ctr;
@@ -484,12 +616,23 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
 #pragma unroll
                     for (int j = 0; j < VY; ++j) {
                         lds_load_group<T, VX>(vring(VR, 0, j), v2b[j]);
-                        lds_load_group<T, VX>(vring(VR, 1, j), etb[j]);
+                        if constexpr (!E7) lds_load_group<T, VX>(vring(VR, 1, j), etb[j]);
                     }
 #pragma unroll
                     for (int j = 0; j < VY; ++j) {
                         lds_store_group<T, VX>(vring(VW, 0, j), v2[j]);
-                        lds_store_group<T, VX>(vring(VW, 1, j), et[j]);
+                        if constexpr (!E7) lds_store_group<T, VX>(vring(VW, 1, j), et[j]);
+                    }
+                }
+                // eta of planes q2-1, q2, q2+1 at this thread's points
+                T ec2[VY][VX], em2[VY][VX], ep2[VY][VX];
+                if constexpr (E7) {
+#pragma unroll
+                    for (int j = 0; j < VY; ++j) {
+                        const int o = (1 + ly * VY + j) * LP + lcol;
+                        lds_load_group<T, VX>(e2c + o, ec2[j]);
+                        lds_load_group<T, VX>(e2m + o, em2[j]);
+                        lds_load_group<T, VX>(e2p + o, ep2[j]);
                     }
                 }
                 laplacian(tile2 + T2 * LTILE,
@@ -497,13 +640,13 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                               constexpr int dz = decltype(dzc)::value;
                               return ws[((WC2 + dz) % WS + WS) % WS][j][i];
                           },
-                          acc);
+                          acc, coupling(ec2, em2, ep2, e2c));
 #pragma unroll
                 for (int j = 0; j < VY; ++j)
 #pragma unroll
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = ws[WC2][j][i];
-                        const T e = etb[j][i];
+                        const T e = E7 ? ec2[j][i] : etb[j][i];
                         res[j][i] = (T(2) * ctr - (T(1) - e) * w0[C2][j][i] + v2b[j][i] * acc[j][i]) /
                                     (T(1) + e);
                     }

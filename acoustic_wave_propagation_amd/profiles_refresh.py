@@ -39,7 +39,7 @@ CMDS = {
     "wave_trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_wave -o wave"
     + BENCH + "--only-wave all --no-cpu --steps 2",
 }
-for _v in ("wave", "pml", "blocked"):
+for _v in ("wave", "pml", "blocked", "pml_blocked"):
     for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         CMDS["%s_%s" % (_v, _n)] = (
             PRE + "--pmc %s -T -d $RAW/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
@@ -49,6 +49,11 @@ CMDS["blocked_sq"] = (PRE + "--pmc " + SQ + " -T -d $RAW/pmc_blocked_sq -o sq"
                       + BENCH + "--only-wave blocked --no-cpu --steps 1")
 CMDS["blocked_tcc"] = (PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_blocked_tcc -o tcc"
                        + BENCH + "--only-wave blocked --no-cpu --steps 1")
+CMDS["pml_blocked_sq"] = (PRE + "--pmc " + SQ + " -T -d $RAW/pmc_pml_blocked_sq -o sq"
+                          + BENCH + "--only-wave pml_blocked --no-cpu --steps 1")
+CMDS["pml_blocked_tcc"] = (PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d "
+                           "$RAW/pmc_pml_blocked_tcc -o tcc"
+                           + BENCH + "--only-wave pml_blocked --no-cpu --steps 1")
 CMDS["others_sq"] = (PRE + "--pmc " + SQ + " -T -d $RAW/pmc_others_sq -o sq"
                      + BENCH + "--only-others --no-cpu --steps 2 --warmup 1")
 CMDS["others_tcc"] = (PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_others_tcc -o tcc"
@@ -100,6 +105,11 @@ def main(argv=None):
             lambda: P.counters_md([db("pmc_blocked_sq", "sq"), db("pmc_blocked_tcc", "tcc")],
                           "wave2_kernel", [CMDS["blocked_sq"], CMDS["blocked_tcc"]],
                           "blocked"),
+        "pml_blocked_r4_1024cube_counters.md":
+            lambda: P.counters_md([db("pmc_pml_blocked_sq", "sq"),
+                                   db("pmc_pml_blocked_tcc", "tcc")],
+                                  "wave2_kernel", [CMDS["pml_blocked_sq"],
+                                                   CMDS["pml_blocked_tcc"]], "blocked"),
         "jacobi_r1_512cube_counters.md":
             lambda: P.counters_md([db("pmc_others_sq", "sq"), db("pmc_others_tcc", "tcc")],
                           "sweeps_fused_kernel", [CMDS["others_sq"], CMDS["others_tcc"]],
@@ -119,13 +129,14 @@ def main(argv=None):
         "wave_pml_blocked_r4_1024cube_trace.md":
             lambda: P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"], "blocked"),
     }
-    for v in ("wave", "pml", "blocked"):
-        makers["%s_r4_1024cube_traffic.md" % v] = (lambda v=v: P.traffic_md(
+    for v in ("wave", "pml", "blocked", "pml_blocked"):
+        two = v in ("blocked", "pml_blocked")
+        makers["%s_r4_1024cube_traffic.md" % v] = (lambda v=v, two=two: P.traffic_md(
             db("pmc_%s_fetch" % v, "fetch"), db("pmc_%s_write" % v, "write"),
-            "wave2_kernel" if v == "blocked" else "star2p5d_kernel",
+            "wave2_kernel" if two else "star2p5d_kernel",
             "%s_r4_f32" % v, 1 << 30, CMDS["%s_fetch" % v],
-            CMDS["%s_write" % v], PASS_BYTES if v == "blocked" else WAVE_BYTES,
-            "blocked" if v == "blocked" else "stream"))
+            CMDS["%s_write" % v], PASS_BYTES if two else WAVE_BYTES,
+            "blocked" if two else "stream"))
     for name, make in makers.items():
         try:
             text = make()

@@ -42,9 +42,10 @@ METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
 PROF = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROF, "star2p5d_r4_512cube_traffic.md")
 WAVE_TRAFFIC = {v: os.path.join(PROF, "%s_r4_1024cube_traffic.md" % v)
-                for v in ("wave", "pml", "blocked")}
+                for v in ("wave", "pml", "blocked", "pml_blocked")}
 COUNTERS = {"headline": os.path.join(PROF, "star2p5d_r4_512cube_counters.md"),
             "blocked": os.path.join(PROF, "blocked_r4_1024cube_counters.md"),
+            "pml_blocked": os.path.join(PROF, "pml_blocked_r4_1024cube_counters.md"),
             "jacobi": os.path.join(PROF, "jacobi_r1_512cube_counters.md")}
 JACOBI_TRAFFIC = os.path.join(PROF, "jacobi_r1_512cube_traffic.md")
 F64_TRAFFIC = os.path.join(PROF, "apply_r4_f64_ragged_traffic.md")
@@ -275,12 +276,13 @@ def bench_headline(torch, B, wl, args):
 
 
 def bench_wave(torch, B, wl, args,
-               variants=("wave", "pml", "regions", "blocked")):
+               variants=("wave", "pml", "regions", "blocked", "pml_blocked")):
     """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
     the pointwise step ("wave"), the PML kernel's step ("pml"), the
     pointwise step launched as data regions ("regions": pml_width = the
     sponge width, so the inner box runs without the eta stream) and the
-    time-blocked run ("blocked": two steps per pass over four buffers)."""
+    time-blocked runs ("blocked", "pml_blocked": two steps per pass over four
+    buffers)."""
     w = wl.WAVE_1024
     e = w.extra
     dev = torch.device("cuda:0")
@@ -298,8 +300,8 @@ def bench_wave(torch, B, wl, args,
     eta = up(lambda a, b: wl.eta_planes(w, a, b))
     u_prev = torch.zeros_like(vel2)
     u = torch.zeros_like(vel2)
-    work = ([torch.zeros_like(vel2) for _ in range(2)] if "blocked" in variants
-            else None)
+    work = ([torch.zeros_like(vel2) for _ in range(2)]
+            if "blocked" in variants or "pml_blocked" in variants else None)
     d = B.desc_init("f32", shp, w.radius)
     # pml_width stays 0: one launch reading eta everywhere is faster on this
     # grid than the data-region launches (thin x slabs of the sponge)
@@ -322,11 +324,12 @@ def bench_wave(torch, B, wl, args,
     res = {}
     for v in variants:
         dv = dr if v == "regions" else d
-        if v == "blocked":
+        if v in ("blocked", "pml_blocked"):
             # 20 steps = 10 passes; the fields end in (u_prev, u) again
             fn = lambda: B.wave_run_blocked(d, u_prev, u, work[0], work[1],
                                             vel2, eta, e["dt"], e["h"],
-                                            w.sweeps, src, trace)
+                                            w.sweeps, src, trace,
+                                            pml=(v == "pml_blocked"))
         else:
             fn = lambda: B.wave_run(dv, u_prev, u, vel2, eta, e["dt"], e["h"],
                                     w.sweeps, src, trace, pml=(v == "pml"))
@@ -343,7 +346,7 @@ def bench_wave(torch, B, wl, args,
                                         "%s_r4_f32" % v, WAVE_TRAFFIC[v])
                                     if v in WAVE_TRAFFIC else None,
                                     algorithmic_bytes_per_step=nbytes))
-        if v == "blocked":
+        if v in ("blocked", "pml_blocked"):
             # what a pass of two steps moves: the single step's reads plus
             # a second written field.  achieved / frac are the pass kernel's
             # own bytes over its own time; the per-step equivalent (20.09
@@ -356,8 +359,9 @@ def bench_wave(torch, B, wl, args,
             rl["frac"] = round(pass_b / (2 * per) / 1e9 / PEAK_HBM_GBS, 4)
             rl["pass_bytes"] = pass_b
             rl["traffic_per"] = "pass (one launch, two steps)"
-            rl["kernel"] = "wave2_kernel<float,4>"
-            rl["valu"] = valu_roofline(COUNTERS["blocked"], 2 * per)
+            rl["kernel"] = ("wave2_kernel<float,4,PML>" if v == "pml_blocked"
+                            else "wave2_kernel<float,4>")
+            rl["valu"] = valu_roofline(COUNTERS[v], 2 * per)
             rl["note"] = ("achieved/frac: pass bytes over pass time (one "
                           "pass = two steps); *_step_equivalent: 20.09 "
                           "B/point per step over the per-step time")
@@ -370,18 +374,22 @@ def bench_wave(torch, B, wl, args,
         log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % ({"wave": "wave", "pml": "wave, PML step",
                 "regions": "wave, data regions",
-                "blocked": "wave, time-blocked"}[v], res[v]["value"],
+                "blocked": "wave, time-blocked",
+                "pml_blocked": "wave, PML step, time-blocked"}[v],
+               res[v]["value"],
                res[v]["ms_per_step"], ach))
     del vel2, eta, u_prev, u, work
     torch.cuda.empty_cache()
     for v in variants:
-        if v in ("regions", "blocked"):  # the same update as "wave"
+        if v in ("regions", "blocked", "pml_blocked"):  # updates timed above
             continue
         res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
             wl, w, args.cpu_budget / 4, pml=(v == "pml"))
     for v in ("regions", "blocked"):
         if v in res:
             res[v]["cpu_baseline"] = res.get("wave", {}).get("cpu_baseline")
+    if "pml_blocked" in res:
+        res["pml_blocked"]["cpu_baseline"] = res.get("pml", {}).get("cpu_baseline")
     if "wave" not in res:
         return res
     out = dict(workload=w.name, **res["wave"])
@@ -391,6 +399,8 @@ def bench_wave(torch, B, wl, args,
                                "B/point)")
     if "pml" in res:
         out["pml_step"] = res["pml"]
+        if "pml_blocked" in res:
+            out["pml_step"]["time_blocked"] = res["pml_blocked"]
     if "regions" in res:
         out["data_regions"] = res["regions"]
     if "blocked" in res:
@@ -584,8 +594,8 @@ def main():
     ap.add_argument("--only-others", action="store_true",
                     help="run only the Jacobi and fp64 workloads (profiling)")
     ap.add_argument("--only-wave",
-                    choices=("wave", "pml", "regions", "blocked", "both",
-                             "all"),
+                    choices=("wave", "pml", "regions", "blocked",
+                             "pml_blocked", "both", "all"),
                     help="run only the 1032^3 leapfrog with that step "
                          "(profiling)")
     args = ap.parse_args()
@@ -606,7 +616,8 @@ def main():
     if args.only_wave:
         bench_wave(torch, B, wl, args,
                    variants={"both": ("wave", "pml"),
-                             "all": ("wave", "pml", "blocked")}.get(
+                             "all": ("wave", "pml", "blocked",
+                                     "pml_blocked")}.get(
                                  args.only_wave, (args.only_wave,)))
         if args.calib:
             calib_copy(torch)

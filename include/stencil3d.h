@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ST_ABI_VERSION 5
+#define ST_ABI_VERSION 6
 #define ST_MAX_R 4
 
 /* element types */
@@ -283,6 +283,26 @@ int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u,
                      const void *eta, double dt, double h, int nsteps,
                      int64_t src_x, int64_t src_y, int64_t src_z,
                      const double *src_trace, void *stream);
+
+/*
+ * The time-blocked run of the PML kernel's step: wave_run_blocked with
+ * wave_step_pml's update (eta's 7-point coupling beside the 25-point stencil
+ * on u, "Accelerating High-Order Stencils on GPUs", smem_eta description;
+ * the coupling formula is the reading documented at wave_step_pml) in both
+ * steps of every two-step pass, and single wave_step_pml steps for an odd
+ * last step.  Same arguments, buffer rotation, result placement, workspace
+ * handling and conditions as wave_run_blocked; the results are bit-identical
+ * to single wave_step_pml steps with their sources (up to the sign of a zero
+ * result where d->pml_width makes the single steps skip eta).  On MI355X it
+ * is slower than wave_run_pml for the 1024^3 R = 4 workload (4.27 against
+ * 3.98 ms per step): eta's register ring and tiles leave room for only two
+ * waves per SIMD on a smaller extended tile.
+ */
+int wave_run_pml_blocked(const stencil3d_desc *d, void *u_prev, void *u,
+                         void *work0, void *work1, const void *vel2,
+                         const void *eta, double dt, double h, int nsteps,
+                         int64_t src_x, int64_t src_y, int64_t src_z,
+                         const double *src_trace, void *stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

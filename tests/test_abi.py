@@ -65,7 +65,7 @@ def test_exports_nothing_else(L):
 
 def test_struct_layout_and_version(L):
     assert ctypes.sizeof(B.Desc) == 168
-    assert B.abi_version() == 5
+    assert B.abi_version() == 6
     d = B.desc_init("f32", (10, 11, 12), 4)
     assert d.struct_size == 168 and d.nx == 12 and d.ny == 11 and d.nz == 10
     assert d.pml_width == 0
@@ -222,6 +222,14 @@ def test_entry_points_reject_before_enqueue(L):
             assert b(*p) == c["ST_ERR_ALIAS"], (i, j)
     # vel2 and eta may share a buffer
     assert b(V[0], V[1], V[2], V[3], V[4], V[4], nsteps=-1) == c["ST_ERR_ARG"]
+    # the PML variant applies the same rules
+    pb = L.wave_run_pml_blocked
+    assert pb(by, *ok, 1e-3, 10.0, -1, 10, 10, 10, None, None) == c["ST_ERR_ARG"]
+    assert pb(by, V[0], V[1], None, V[3], V[4], V[5], 1e-3, 10.0, 4, 10, 10, 10,
+              None, None) == c["ST_ERR_NULL"]
+    assert pb(by, V[0], V[1], V[1], V[3], V[4], V[5], 1e-3, 10.0, 4, 10, 10, 10,
+              None, None) == c["ST_ERR_ALIAS"]
+    assert pb(by, *ok, 1e-3, 10.0, 3, 2, 10, 10, tr, None) == c["ST_ERR_BAD_INDEX"]
     # the no-allocation variant: wave_run's rules, plus the workspace limit,
     # all checked before the device is touched
     na = L.wave_run_blocked_noalloc
