@@ -590,8 +590,8 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = w0[CS][j][i];
                         const T e = E7 ? ew[EC1][j][i] : et[j][i];
-                        const T u1 = (T(2) * ctr - (T(1) - e) * up[j][i] + v2[j][i] * acc[j][i]) /
-                                     (T(1) + e);
+                        const T u1 = damp_div<T, E7>(
+                            T(2) * ctr - (T(1) - e) * up[j][i] + v2[j][i] * acc[j][i], T(1) + e);
                         res[j][i] = (in1 && rin[j] && cin[i]) ? u1 : ctr;
                     }
                 if (q1 == g.sz && sj >= 0) {
@@ -647,8 +647,9 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = ws[WC2][j][i];
                         const T e = E7 ? ec2[j][i] : etb[j][i];
-                        res[j][i] = (T(2) * ctr - (T(1) - e) * w0[C2][j][i] + v2b[j][i] * acc[j][i]) /
-                                    (T(1) + e);
+                        res[j][i] = damp_div<T, E7>(
+                            T(2) * ctr - (T(1) - e) * w0[C2][j][i] + v2b[j][i] * acc[j][i],
+                            T(1) + e);
                     }
                 if (q2 == g.sz && sj >= 0) {
 #pragma unroll
