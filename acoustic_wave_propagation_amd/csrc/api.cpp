@@ -43,15 +43,22 @@ int current_cus(int *status) {
 
 // The wave update on the interior (pml: the PML step, with the
 // eta-gradient coupling).  When the descriptor states a sponge width p
-// (eta = 0 at least p points inside every interior face) and the eta-free
-// kernel exists, the interior is launched as data regions -- an inner box
-// that does not read eta, and six slabs that do ("Accelerating High-Order
-// Stencils on GPUs": one kernel for the inner region, another for the PML
-// region).  The inner box keeps distance p from every face, p + 1 for the
-// PML step, whose coupling reads eta one point further out; there eta and
-// its differences are zero.  Every point is written by exactly one launch
-// with the same arithmetic, so the result is bit-identical to one launch
-// over the interior (for the PML step: up to the sign of a zero result).
+// (eta = 0 at least p points inside every interior face), the update
+// reads eta only in the sponge ("Accelerating High-Order Stencils on
+// GPUs": one kernel for the inner region, another for the PML region,
+// where only the latter reads eta).
+//  * Wave step: the rows within p of a y face go to two launches of their
+//    own (slabs that read eta everywhere); the launch over the other rows
+//    reads eta only on the lanes whose columns lie within p of an x face
+//    and in the planes within p of a z face.  Its workgroups then move at
+//    most 4 bytes per point of eta on a quarter of the lanes (the x-edge
+//    tiles) instead of on all of them.
+//  * PML step: an inner box that does not read eta, and six slabs that
+//    do; the inner box keeps distance p + 1 from every face (the coupling
+//    reads eta one point further out).
+// Every point is written by exactly one launch with the same arithmetic,
+// so the result is bit-identical to one launch over the interior (for the
+// PML step: up to the sign of a zero result).
 int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void *u_prev,
                 const void *vel2, const void *eta, double wscale, int cus, hipStream_t s,
                 bool pml) {
@@ -62,6 +69,23 @@ int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void
     const int64_t pw = d.pml_width < ((int64_t)1 << 30) ? d.pml_width : (int64_t)1 << 30;
     const int64_t p = pw > 0 ? pw + (pml ? 1 : 0) : 0;
     auto fits = [p](int64_t lo, int64_t hi) { return p < hi - lo && 2 * p < hi - lo; };
+    if (!pml && p > 0 && d.radius == 4) {
+        // (a width past every face reads eta everywhere: the plain launch)
+        const int pi = (int)p;
+        if (!fits(in.y0, in.y1))
+            return st::launch_star(d, in, st::Kind::WaveWide, u, u_next, u_prev, vel2, eta,
+                                   wscale, cus, s, pi);
+        const st::Box rows[3] = {
+            {in.x0, in.x1, in.y0 + p, in.y1 - p, in.z0, in.z1},  // x and z sponges only
+            {in.x0, in.x1, in.y0, in.y0 + p, in.z0, in.z1},      // y < inner
+            {in.x0, in.x1, in.y1 - p, in.y1, in.z0, in.z1},      // y > inner
+        };
+        int st = ST_OK;
+        for (int i = 0; i < 3 && st == ST_OK; ++i)
+            st = st::launch_star(d, rows[i], st::Kind::WaveWide, u, u_next, u_prev, vel2, eta,
+                                 wscale, cus, s, pi);
+        return st;
+    }
     const bool split = p > 0 && st::kind_available(d, st::Kind::WaveNoEta) &&
                        fits(in.x0, in.x1) && fits(in.y0, in.y1) && fits(in.z0, in.z1);
     if (!split)

@@ -25,8 +25,12 @@ inline Box interior_box(const stencil3d_desc &d) {
 // wave update plus the eta-gradient coupling).  The planner may replace
 // Apply by ApplyWide (row-wide tiles), Wave by WaveNarrow and WavePml by
 // WavePmlNarrow (32-column tiles) where those fit the box better; WaveNoEta
-// is the wave update for a box where eta is zero (no eta stream).
-enum class Kind { Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta, WavePml, WavePmlNarrow };
+// is the wave update for a box where eta is zero (no eta stream); WaveWide
+// the wave update on wider tiles that reads eta only in the sponge of a
+// stated width (the data-region launches).
+enum class Kind {
+    Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta, WavePml, WavePmlNarrow, WaveWide
+};
 
 // Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs
 // covering the output box, each streamed through z in chunks.  The first
@@ -50,11 +54,13 @@ Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int c
 
 // Enqueue the streaming stencil on the output box (inside the interior;
 // empty boxes enqueue nothing).  Wave variants scale the weights by wscale
-// = dt^2/h^2.  Arguments are validated by the caller.  Returns ST_OK,
-// ST_ERR_ARG (variant not instantiated) or ST_ERR_LAUNCH.
+// = dt^2/h^2.  Kind::WaveWide with pw > 0 reads eta only within pw of an
+// interior face (the caller guarantees it is zero elsewhere).  Arguments
+// are validated by the caller.  Returns ST_OK, ST_ERR_ARG (variant not
+// instantiated) or ST_ERR_LAUNCH.
 int launch_star(const stencil3d_desc &d, const Box &box, Kind kind, const void *in, void *out,
                 const void *u_prev, const void *vel2, const void *eta, double wscale, int cus,
-                hipStream_t stream);
+                hipStream_t stream, int pw = 0);
 
 // Largest number of sweeps one fused pass can do for d (1: no fused kernel
 // for this radius and element type).

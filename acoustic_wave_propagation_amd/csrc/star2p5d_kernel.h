@@ -68,6 +68,10 @@ struct StarArgs {
     // output box [bx0,bx1) x [by0,by1) x [bz0,bz1): inside the interior; the
     // tiles and z chunks cover it, and only its points are written
     int32_t bx0, bx1, by0, by1, bz0, bz1;
+    // wave step with eta: the caller guarantees eta = 0 at every interior
+    // point at least pw from all interior faces (0: no claim, eta read
+    // everywhere)
+    int32_t pw;
     T cc;             // centre weight, plain form
     T ccd;            // centre weight of the difference form
     T gw;             // weight of the eta-gradient coupling (PML step)
@@ -382,6 +386,25 @@ star2p5d_kernel(StarArgs<T> a) {
         soff[j] = (oy0 + j < a.by1 && ox < a.bx1) ? ooff[j] : kOOB;
     }
     const int nvx = max(0, min(VX, a.bx1 - ox));  // written columns (ragged x)
+    // eta of the wave step with data regions (a.pw > 0): a lane reads eta
+    // in every plane on its rows within pw of an interior face in y, and on
+    // all its rows if its columns lie within pw of an interior face in x or
+    // of an x edge of its tile; its other loads read eta only in the planes
+    // within pw of a z face.  Elsewhere eta is zero (the caller's
+    // guarantee) and the load takes the out-of-range offset: no memory
+    // traffic, and it returns that zero.  The tile-edge columns give every
+    // tile of a row the same load pattern, which keeps the tiles streaming
+    // in step (their halo rows come from each other's loads in L2); tiles
+    // that read eta on different columns drift apart and lose that reuse.
+    uint32_t eoff[VY];
+    {
+        const int lo = R + a.pw;
+        const bool xs = a.pw == 0 || ox < lo || ox + VX > nx - lo || ox - gx0 < a.pw ||
+                        gx0 + TX - (ox + VX) < a.pw;
+#pragma unroll
+        for (int j = 0; j < VY; ++j)
+            eoff[j] = (xs || oy0 + j < lo || oy0 + j >= ny - lo) ? ooff[j] : kOOB;
+    }
     const int lcol = PADL + lx * VX;
     const int lrow0 = R + ly * VY;
 
@@ -472,8 +495,11 @@ star2p5d_kernel(StarArgs<T> a) {
         }
         if constexpr (ETA && !E7) {
             const rsrc_t re = rsrc_at(a.eta, k, 0, needed);
+            const int z = z0 + dir * k;
+            const bool zs = a.pw == 0 || z < R + a.pw || z >= a.nz - R - a.pw;
 #pragma unroll
-            for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(re, ooff[jj], et[e][jj]);
+            for (int jj = 0; jj < VY; ++jj)
+                bload<T, VX, LAUX>(re, zs ? ooff[jj] : eoff[jj], et[e][jj]);
         }
     };
     auto load_eta = [&](int k, int j, bool needed, auto slot_c) {
@@ -764,6 +790,7 @@ StarArgs<T> make_args(const stencil3d_desc &d, const Box &b, const void *in, voi
     a.by1 = (int32_t)b.y1;
     a.bz0 = (int32_t)b.z0;
     a.bz1 = (int32_t)b.z1;
+    a.pw = 0;
     a.gw = (T)(wscale * 0.25);
     const double cc = d.cx[0] + d.cy[0] + d.cz[0];
     double ksum = 0.0;
