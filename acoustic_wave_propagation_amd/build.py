@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "libstencil3d.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["star2p5d.hip", "sweeps_fused.hip", "wave2.hip", "noalloc.hip",
            "validate.cpp", "api.cpp"]
+# copy kernels with the stencil's memory walk, for measuring its ceiling
+# (bench.py --ceilings); a library of their own
+WALK_SOURCE = "walk_copy.hip"
+WALK_LIB = os.path.join(PKG, "libwalkcopy.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -54,13 +58,15 @@ def build(verbose: bool = False, extra_flags=(), jobs: int | None = None) -> str
     tag = "%d" % os.getpid()
     objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".%s.o" % tag)
             for s in SOURCES]
+    walk_obj = os.path.join(OBJDIR, "walk_copy.%s.o" % tag)
     cmds = [[hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
-             os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+             os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES + [WALK_SOURCE], objs + [walk_obj])]
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     try:
         with ThreadPoolExecutor(jobs) as ex:
             results = list(ex.map(lambda c: _run(c, verbose), cmds))
-        for (rc, out), s in zip(results, SOURCES):
+        for (rc, out), s in zip(results, SOURCES + [WALK_SOURCE]):
             if rc != 0:
                 raise RuntimeError("hipcc failed on %s (%d):\n%s" % (s, rc, out))
             if verbose and out:
@@ -72,8 +78,13 @@ def build(verbose: bool = False, extra_flags=(), jobs: int | None = None) -> str
         if rc != 0:
             raise RuntimeError("link failed (%d):\n%s" % (rc, out))
         os.replace(tmp, LIB)
+        rc, out = _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", walk_obj,
+                        "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp], verbose)
+        if rc != 0:
+            raise RuntimeError("link failed (%d):\n%s" % (rc, out))
+        os.replace(tmp, WALK_LIB)
     finally:
-        for o in objs:
+        for o in objs + [walk_obj]:
             if os.path.exists(o):
                 os.remove(o)
     return LIB

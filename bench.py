@@ -16,7 +16,8 @@ stream.  `cpu_baseline` times the CPU oracle on the host cores over a
 bounded number of whole-grid applications.
 
 --calib adds a plain device copy of known size (for the counter runs that
-turn FETCH_SIZE / WRITE_SIZE into bytes); --only-headline skips everything
+turn FETCH_SIZE / WRITE_SIZE into bytes); --ceilings times copy kernels that
+walk memory like the apply (libwalkcopy.so) beside it; --only-headline skips everything
 but the timed stencil launches, --only-others runs only the Jacobi and fp64
 workloads, --only-wave {wave,pml,regions,blocked,both,all} only the 1032^3
 leapfrog with those step kinds (both: wave and pml; all: also blocked; all
@@ -234,6 +235,60 @@ from acoustic_wave_propagation_amd.traffic import apply_bytes as star_bytes  # n
 from acoustic_wave_propagation_amd.traffic import wave_bytes  # noqa: E402
 
 
+def walk_lib():
+    """libwalkcopy.so: copy kernels with the apply's memory walk."""
+    import ctypes
+    path = os.path.join(ROOT, "acoustic_wave_propagation_amd", "libwalkcopy.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libwalkcopy.so is not built (%s); run "
+                           "python -m acoustic_wave_propagation_amd.build" % path)
+    L = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    L.walk_copy_zmarch.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
+    L.walk_copy_rows.argtypes = [vp, vp, i32, i32, i32, vp]
+    return L
+
+
+def bench_ceilings(torch, inp, out, steps, warmup, full=True):
+    """Copies of the 512^3 interior of the 520^3 grid (inp -> out): with
+    the apply kernel's memory walk but without its arithmetic, and one-shot
+    row copies.  zmarch: 512-thread workgroups streaming 256 x 16 (or
+    512 x 8) tiles through 4 chunks of 128 planes, one barrier per step;
+    rows: one-shot row copies.  Stores at the rows' own place (16 bytes into
+    each row, so each row's end sectors are written in part), shifted to
+    the row start (whole 32-byte sectors), or with the rows' halo rewritten
+    from out (whole sectors).  ms are mean HIP-event launch durations;
+    stencil_frac is the apply's algorithmic bytes over that time over 8 TB/s,
+    the fraction the stencil would report at the copy's speed."""
+    L = walk_lib()
+    n, R = inp.shape[0], 4
+    stream = torch.cuda.current_stream().cuda_stream
+    ip, op = inp.data_ptr(), out.data_ptr()
+    variants = [("zmarch_256x16", lambda: L.walk_copy_zmarch(ip, op, n, R, 256, 4, 0, stream)),
+                ("zmarch_256x16_aligned",
+                 lambda: L.walk_copy_zmarch(ip, op, n, R, 256, 4, 1, stream))]
+    if full:
+        variants += [
+            ("zmarch_512x8", lambda: L.walk_copy_zmarch(ip, op, n, R, 512, 4, 0, stream)),
+            ("zmarch_512x8_aligned",
+             lambda: L.walk_copy_zmarch(ip, op, n, R, 512, 4, 1, stream)),
+            ("rows", lambda: L.walk_copy_rows(ip, op, n, R, 0, stream)),
+            ("rows_halo_rewritten", lambda: L.walk_copy_rows(ip, op, n, R, 2, stream)),
+            ("rows_aligned", lambda: L.walk_copy_rows(ip, op, n, R, 1, stream))]
+    ni = n - 2 * R
+    copy_b = 2 * 4 * ni ** 3
+    stencil_b = star_bytes((ni, ni, ni), R, 4)
+    res = {}
+    for name, fn in variants:
+        if fn() != 0:
+            raise RuntimeError("walk_copy %s refused the grid" % name)
+        _, durs = timed_launches(torch, fn, steps, warmup)
+        ms = float(durs.mean()) * 1e3
+        res[name] = dict(ms=round(ms, 4), copy_gbs=round(copy_b / ms / 1e6, 1),
+                         stencil_frac=round(stencil_b / ms / 1e6 / PEAK_HBM_GBS, 4))
+    return res
+
+
 def bench_headline(torch, B, wl, args):
     w = wl.R4_512
     dev = torch.device("cuda:0")
@@ -272,6 +327,15 @@ def bench_headline(torch, B, wl, args):
                       valu=valu_roofline(COUNTERS["headline"], mean)),
         gbs_wall=round(nbytes * args.steps / wall / 1e9, 1),
     )
+    # plain copies of the same interior (context): with the apply's walk,
+    # and one-shot row copies, the fastest way found to move those bytes
+    res["roofline"]["walk_copies"] = dict(
+        bench_ceilings(torch, inp, out, min(args.steps, 100), args.warmup),
+        note="copies of the 512^3 interior: zmarch_* with the apply's walk "
+             "(tiles streaming 4 chunks of 128 planes, a barrier per step), "
+             "rows_* one-shot; *_aligned: rows stored from the row start "
+             "(whole 32-byte sectors); stencil_frac: the apply's algorithmic "
+             "bytes over the copy's time over 8 TB/s")
     return res, host
 
 
@@ -302,9 +366,9 @@ def bench_wave(torch, B, wl, args,
     u = torch.zeros_like(vel2)
     work = ([torch.zeros_like(vel2) for _ in range(2)]
             if "blocked" in variants or "pml_blocked" in variants else None)
+    # pml_width 0: one launch reading eta everywhere (the "wave" line);
+    # the "regions" line states the sponge width (data regions)
     d = B.desc_init("f32", shp, w.radius)
-    # pml_width stays 0: one launch reading eta everywhere is faster on this
-    # grid than the data-region launches (thin x slabs of the sponge)
     src = wl.source_point(w)
     trace = wl.source_trace(w)
     runs = max(1, min(args.steps, 5))
@@ -314,13 +378,12 @@ def bench_wave(torch, B, wl, args,
     # coupling, eta's 7-point stencil) moves the same bytes: eta's
     # neighbours come from LDS and registers.
     nbytes = wave_bytes(w.interior, w.radius, 4)
-    # data regions: eta is zero from depth `sponge` on, so the inner box at
-    # that depth skips the eta stream; its true bytes lack those eta reads
+    # data regions: eta is zero from depth `sponge` on, so the wave step
+    # reads it only on the points eta_read_points counts; the true bytes
+    # lack the other eta reads
     dr = B.desc_init("f32", shp, w.radius)
     dr.pml_width = e["sponge"]
-    inner = 1
-    for n in w.interior:
-        inner *= n - 2 * e["sponge"]
+    eta_pts = eta_read_points(w.interior, e["sponge"])
     res = {}
     for v in variants:
         dv = dr if v == "regions" else d
@@ -366,7 +429,7 @@ def bench_wave(torch, B, wl, args,
                           "pass = two steps); *_step_equivalent: 20.09 "
                           "B/point per step over the per-step time")
         if v == "regions":
-            true_b = nbytes - 4 * inner
+            true_b = nbytes - 4 * (w.interior_points - eta_pts)
             res[v]["roofline"]["true_bytes_per_step"] = true_b
             res[v]["roofline"]["achieved_true_bytes"] = round(
                 true_b / per / 1e9, 1)
@@ -406,6 +469,23 @@ def bench_wave(torch, B, wl, args,
     if "blocked" in res:
         out["time_blocked"] = res["blocked"]
     return out
+
+
+def eta_read_points(interior, pw, tile_x=256, group=4):
+    """Interior points whose eta the data-region wave step loads (fp32,
+    sponge width pw): every point of the rows within pw of a y face (their
+    own launches); in the other rows every point of the planes within pw of
+    a z face, and elsewhere the 4-column groups within pw of an x face or of
+    an x edge of their 256-wide tile."""
+    iz, iy, ix = interior
+    ox = np.arange(0, ix, group)              # group starts, interior coords
+    gx0 = ox // tile_x * tile_x               # tile origins
+    cols = ((ox < pw) | (ox + group > ix - pw) | (ox - gx0 < pw) |
+            (gx0 + tile_x - (ox + group) < pw))
+    ncols = int(np.minimum(group, ix - ox)[cols].sum())
+    slabs = 2 * pw * ix * iz
+    rows = iy - 2 * pw
+    return slabs + rows * (2 * pw * ix + (iz - 2 * pw) * ncols)
 
 
 def cpu_wave_slab(wl, w, budget_s, planes=64, pml=False):
@@ -593,6 +673,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-others", action="store_true",
                     help="run only the Jacobi and fp64 workloads (profiling)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time only the copy kernels with the apply's memory "
+                         "walk (libwalkcopy.so) beside the apply, one JSON line")
     ap.add_argument("--only-wave",
                     choices=("wave", "pml", "regions", "blocked",
                              "pml_blocked", "both", "all"),
@@ -613,6 +696,20 @@ def main():
         sys.exit(1)
     B.lib()  # fail loudly if the library is missing
 
+    if args.ceilings:
+        w = wl.R4_512
+        inp = torch.from_numpy(wl.input_planes(w)).to("cuda:0")
+        out = torch.zeros_like(inp)
+        d = B.desc_init("f32", w.shape, w.radius)
+        _, durs = timed_launches(torch, lambda: B.stencil3d_apply(d, inp, out),
+                                 args.steps, args.warmup)
+        ms = float(durs.mean()) * 1e3
+        nb = star_bytes(w.interior, w.radius, 4)
+        res = dict(apply=dict(ms=round(ms, 4),
+                              stencil_frac=round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)))
+        res.update(bench_ceilings(torch, inp, out, args.steps, args.warmup))
+        print(json.dumps(dict(workload=w.name, ceilings=res)), flush=True)
+        return
     if args.only_wave:
         bench_wave(torch, B, wl, args,
                    variants={"both": ("wave", "pml"),

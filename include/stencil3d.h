@@ -83,14 +83,17 @@ extern "C" {
  * for the PML region, where only the latter reads eta).  If pml_width > 0
  * the caller guarantees that eta is exactly 0 at every interior point whose
  * distance (in points, along any axis) from the nearest interior face is
- * at least pml_width.  The wave entry points may then launch that inner box
- * without reading eta and the six slabs around it with eta (done for R = 4
- * when the inner box is not empty); the results are bit-identical to
+ * at least pml_width.  For R = 4 the wave entry points then skip eta
+ * where it is zero: the wave step reads it only near the faces (the rows
+ * within pml_width of a y face as two launches of their own; in the other
+ * rows on the columns near the x faces, in the planes near the z faces,
+ * and on the same columns of every tile, which keeps the tiles streaming
+ * in step), and the PML step launches an inner box that does not read eta
+ * and the six slabs around it.  The results are bit-identical to
  * pml_width = 0 under that guarantee, and wrong where it does not hold.
- * 0 (the default) reads eta everywhere in one launch -- on MI355X the
- * faster choice for thin sponges (a 1024^3 step with a 32-point sponge:
- * 4.0 ms in one launch, 4.8 ms as seven).  Ignored by the plain stencil.
- * 168 bytes, naturally aligned.
+ * On MI355X a 1024^3 wave step with a 32-point sponge takes 3.70 ms with
+ * pml_width = 32 and 4.0 ms with 0 (eta read everywhere in one launch).
+ * Ignored by the plain stencil.  168 bytes, naturally aligned.
  */
 typedef struct stencil3d_desc {
     uint32_t struct_size; /* = sizeof(stencil3d_desc)                    */

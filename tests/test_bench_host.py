@@ -143,3 +143,26 @@ def test_traffic_scaling(tmp_path):
                 [("star2p5d_kernel", 1.0)])
         P.traffic_md(str(tmp_path / "n.db"), w, "star2p5d_kernel", "k", gib,
                      "", "")
+
+
+def test_walk_copy_library_exports():
+    """The measurement copies (bench.py --ceilings) are built beside the
+    stencil library and export their two entry points."""
+    path = os.path.join(ROOT, "acoustic_wave_propagation_amd", "libwalkcopy.so")
+    if not os.path.exists(path):
+        pytest.skip("libwalkcopy.so not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert {"walk_copy_zmarch", "walk_copy_rows"} <= names
+
+
+def test_eta_read_points_model():
+    """The data-region byte model: pw = 32 on a 1024^3 interior reads eta on
+    the two 32-row y slabs, the 64 z-sponge planes of the other rows, and a
+    quarter of their columns elsewhere (the 32 columns at each edge of each
+    256-wide tile, which include the x sponge)."""
+    b = _bench()
+    n, pw = 1024, 32
+    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 4))
+    assert b.eta_read_points((n, n, n), pw) == want
