@@ -329,6 +329,9 @@ def bench_headline(torch, B, wl, args):
     )
     # plain copies of the same interior (context): with the apply's walk,
     # and one-shot row copies, the fastest way found to move those bytes
+    # (not in profiling runs, which time the apply alone)
+    if args.only_headline:
+        return res, host
     res["roofline"]["walk_copies"] = dict(
         bench_ceilings(torch, inp, out, min(args.steps, 100), args.warmup),
         note="copies of the 512^3 interior: zmarch_* with the apply's walk "
@@ -713,7 +716,7 @@ def main():
     if args.only_wave:
         bench_wave(torch, B, wl, args,
                    variants={"both": ("wave", "pml"),
-                             "all": ("wave", "pml", "blocked",
+                             "all": ("wave", "pml", "regions", "blocked",
                                      "pml_blocked")}.get(
                                  args.only_wave, (args.only_wave,)))
         if args.calib:

@@ -539,6 +539,44 @@ def test_wave_pml_regions(oracle_mod, torch_dev):
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype):
+    """A grid wide enough for tiles whose columns lie away from the x
+    sponge and from their own x edges (1000 interior columns; 256-wide
+    tiles in fp32, 128-wide in fp64), so those lanes really skip eta
+    outside the z-sponge planes: pml_width 12 (exact) and 13
+    (conservative) give the same bits as 0 over three steps, 6 (a false
+    claim) does not, and the result matches the oracle."""
+    import dataclasses
+    torch, _ = torch_dev
+    dt = "f32" if dtype == np.float32 else "f64"
+    base = wl.WAVE_128_RANDOM
+    w = dataclasses.replace(base, shape=(40, 44, 1008), dtype=dt,
+                            extra=dict(base.extra, sponge=12))
+    e = w.extra
+    R = w.radius
+    log("case data regions wide %s %s" % (dt, w.shape))
+    u_prev, u, vel2, eta = _wave_fields(w, torch)
+    runs = {}
+    for pml in (0, 12, 13, 6):
+        d = B.desc_init(dt, w.shape, R)
+        d.pml_width = pml
+        a, b = u_prev.clone(), u.clone()
+        older, newest = B.wave_run(d, a, b, vel2, eta, e["dt"], e["h"], 3)
+        runs[pml] = newest.cpu().numpy()
+    for pml in (12, 13):
+        assert np.array_equal(runs[pml].view(np.uint8),
+                              runs[0].view(np.uint8)), pml
+    assert not np.array_equal(runs[6], runs[0])
+    c = oracle_mod.laplacian_weights(R)
+    _, ref = oracle_mod.wave_run(u_prev.cpu().numpy(), u.cpu().numpy(),
+                                 vel2.cpu().numpy(), eta.cpu().numpy(), R, c,
+                                 e["dt"], e["h"], 3)
+    tol = 1e-4 if dtype == np.float32 else 1e-11
+    check_close(interior(runs[12], R), interior(ref, R), tol,
+                "3 free steps, wide data regions")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_wave_data_regions_ragged(oracle_mod, torch_dev, dtype):
     """The data-region launch (an eta-free inner box plus six slabs that
     read eta, for R = 4) on a ragged non-cubic grid with a 12-point sponge,
