@@ -43,66 +43,39 @@ int current_cus(int *status) {
 
 // The wave update on the interior (pml: the PML step, with the
 // eta-gradient coupling).  When the descriptor states a sponge width p
-// (eta = 0 at least p points inside every interior face), the update
-// reads eta only in the sponge ("Accelerating High-Order Stencils on
-// GPUs": one kernel for the inner region, another for the PML region,
-// where only the latter reads eta).
-//  * Wave step: the rows within p of a y face go to two launches of their
-//    own (slabs that read eta everywhere); the launch over the other rows
-//    reads eta only on the lanes whose columns lie within p of an x face
-//    and in the planes within p of a z face.  Its workgroups then move at
-//    most 4 bytes per point of eta on a quarter of the lanes (the x-edge
-//    tiles) instead of on all of them.
-//  * PML step: an inner box that does not read eta, and six slabs that
-//    do; the inner box keeps distance p + 1 from every face (the coupling
-//    reads eta one point further out).
-// Every point is written by exactly one launch with the same arithmetic,
-// so the result is bit-identical to one launch over the interior (for the
-// PML step: up to the sign of a zero result).
+// (eta = 0 at least p points inside every interior face), the update reads
+// eta only near the faces ("Accelerating High-Order Stencils on GPUs": one
+// kernel for the inner region, another for the PML region, where only the
+// latter reads eta).  The rows within p of a y face go to two launches of
+// their own (slabs that read eta everywhere); the launch over the other
+// rows reads eta on the columns within p of an x face or of an x edge of
+// the lane's tile, and elsewhere only in the planes within p of a z face
+// (the PML step's eta ring by the same rule, point by point).  Every tile
+// of that launch has the same load pattern, so its tiles stream in step.
+// Every point is written by exactly one launch with the same arithmetic
+// (eta = 0 where it is not read), so the result is bit-identical to one
+// launch over the interior.
 int launch_wave(const stencil3d_desc &d, const void *u, void *u_next, const void *u_prev,
                 const void *vel2, const void *eta, double wscale, int cus, hipStream_t s,
                 bool pml) {
     const st::Box in = st::interior_box(d);
-    const st::Kind kind = pml ? st::Kind::WavePml : st::Kind::Wave;
-    // (extents are below 2^31: a width from 2^30 up never fits, and clamping
-    // it keeps p + 1 and 2 p from overflowing)
-    const int64_t pw = d.pml_width < ((int64_t)1 << 30) ? d.pml_width : (int64_t)1 << 30;
-    const int64_t p = pw > 0 ? pw + (pml ? 1 : 0) : 0;
-    auto fits = [p](int64_t lo, int64_t hi) { return p < hi - lo && 2 * p < hi - lo; };
-    if (!pml && p > 0 && d.radius == 4) {
-        // (a width past every face reads eta everywhere: the plain launch)
-        const int pi = (int)p;
-        if (!fits(in.y0, in.y1))
-            return st::launch_star(d, in, st::Kind::WaveWide, u, u_next, u_prev, vel2, eta,
-                                   wscale, cus, s, pi);
-        const st::Box rows[3] = {
-            {in.x0, in.x1, in.y0 + p, in.y1 - p, in.z0, in.z1},  // x and z sponges only
-            {in.x0, in.x1, in.y0, in.y0 + p, in.z0, in.z1},      // y < inner
-            {in.x0, in.x1, in.y1 - p, in.y1, in.z0, in.z1},      // y > inner
-        };
-        int st = ST_OK;
-        for (int i = 0; i < 3 && st == ST_OK; ++i)
-            st = st::launch_star(d, rows[i], st::Kind::WaveWide, u, u_next, u_prev, vel2, eta,
-                                 wscale, cus, s, pi);
-        return st;
-    }
-    const bool split = p > 0 && st::kind_available(d, st::Kind::WaveNoEta) &&
-                       fits(in.x0, in.x1) && fits(in.y0, in.y1) && fits(in.z0, in.z1);
-    if (!split)
-        return st::launch_star(d, in, kind, u, u_next, u_prev, vel2, eta, wscale, cus, s);
-    const st::Box c{in.x0 + p, in.x1 - p, in.y0 + p, in.y1 - p, in.z0 + p, in.z1 - p};
-    const st::Box slabs[6] = {
-        {in.x0, in.x1, in.y0, in.y1, in.z0, c.z0},  // below the inner box in z
-        {in.x0, in.x1, in.y0, in.y1, c.z1, in.z1},  // above
-        {in.x0, in.x1, in.y0, c.y0, c.z0, c.z1},    // in its z range: y < inner
-        {in.x0, in.x1, c.y1, in.y1, c.z0, c.z1},    // y > inner
-        {in.x0, c.x0, c.y0, c.y1, c.z0, c.z1},      // inner y, z: x < inner
-        {c.x1, in.x1, c.y0, c.y1, c.z0, c.z1},      // x > inner
+    // (extents are below 2^31: clamping the width keeps 2 p from overflowing)
+    const int64_t p = d.pml_width < ((int64_t)1 << 30) ? d.pml_width : (int64_t)1 << 30;
+    if (p <= 0 || d.radius != 4)
+        return st::launch_star(d, in, pml ? st::Kind::WavePml : st::Kind::Wave, u, u_next,
+                               u_prev, vel2, eta, wscale, cus, s);
+    const st::Kind wide = pml ? st::Kind::WavePmlRegions : st::Kind::WaveRegions;
+    const int pi = (int)p;
+    if (2 * p >= in.y1 - in.y0)  // every row lies within p of a y face
+        return st::launch_star(d, in, wide, u, u_next, u_prev, vel2, eta, wscale, cus, s, pi);
+    const st::Box rows[3] = {
+        {in.x0, in.x1, in.y0 + p, in.y1 - p, in.z0, in.z1},  // x and z sponges only
+        {in.x0, in.x1, in.y0, in.y0 + p, in.z0, in.z1},      // y < inner
+        {in.x0, in.x1, in.y1 - p, in.y1, in.z0, in.z1},      // y > inner
     };
-    int st = st::launch_star(d, c, st::Kind::WaveNoEta, u, u_next, u_prev, vel2, eta, wscale,
-                             cus, s);
-    for (int i = 0; i < 6 && st == ST_OK; ++i)
-        st = st::launch_star(d, slabs[i], kind, u, u_next, u_prev, vel2, eta, wscale, cus, s);
+    int st = ST_OK;
+    for (int i = 0; i < 3 && st == ST_OK; ++i)
+        st = st::launch_star(d, rows[i], wide, u, u_next, u_prev, vel2, eta, wscale, cus, s, pi);
     return st;
 }
 

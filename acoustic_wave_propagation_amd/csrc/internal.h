@@ -24,12 +24,12 @@ inline Box interior_box(const stencil3d_desc &d) {
 // wave update of (u_prev, in = u, vel2, eta).  WavePml: the PML step (the
 // wave update plus the eta-gradient coupling).  The planner may replace
 // Apply by ApplyWide (row-wide tiles), Wave by WaveNarrow and WavePml by
-// WavePmlNarrow (32-column tiles) where those fit the box better; WaveNoEta
-// is the wave update for a box where eta is zero (no eta stream); WaveWide
-// the wave update on wider tiles that reads eta only in the sponge of a
-// stated width (the data-region launches).
+// WavePmlNarrow (32-column tiles) where those fit the box better.
+// WaveRegions and WavePmlRegions: the wave update and the PML step on wider
+// tiles, reading eta only near the faces for a stated sponge width (the
+// data-region launches).
 enum class Kind {
-    Apply, ApplyWide, Wave, WaveNarrow, WaveNoEta, WavePml, WavePmlNarrow, WaveWide
+    Apply, ApplyWide, Wave, WaveNarrow, WavePml, WavePmlNarrow, WaveRegions, WavePmlRegions
 };
 
 // Launch geometry of the 2.5D kernel: XY tiles of tile_x * tile_y outputs
@@ -54,8 +54,9 @@ Geometry plan_geometry(const stencil3d_desc &d, const Box &box, Kind kind, int c
 
 // Enqueue the streaming stencil on the output box (inside the interior;
 // empty boxes enqueue nothing).  Wave variants scale the weights by wscale
-// = dt^2/h^2.  Kind::WaveWide with pw > 0 reads eta only within pw of an
-// interior face (the caller guarantees it is zero elsewhere).  Arguments
+// = dt^2/h^2.  Kind::WaveRegions and WavePmlRegions with pw > 0 read eta only
+// within pw of an interior face (the caller guarantees it is zero
+// elsewhere).  Arguments
 // are validated by the caller.  Returns ST_OK, ST_ERR_ARG (variant not
 // instantiated) or ST_ERR_LAUNCH.
 int launch_star(const stencil3d_desc &d, const Box &box, Kind kind, const void *in, void *out,

@@ -44,16 +44,18 @@ using F32Wave = TileCfg<4, 2, 32, 16, 1, 0, true, 2, false, true, true, false, f
 using F64Apply = TileCfg<2, 2, 64, 8, 1, 0, true, 2, false, true, true, true>;
 using F64Wave = TileCfg<2, 2, 32, 16, 1, 0, true, 2, false, true, true, false, false, 1, false, true>;
 
-// Wide tiles for the wave step's data regions (Kind::WaveWide, with a
-// sponge width): 4 x 2 (fp32) or 2 x 2 (fp64) per thread, 64 x 8 threads ->
-// 256 x 16 or 128 x 16 tiles.  Every tile reads eta on the columns within
-// the sponge width of its x edges (a quarter of a 256-wide tile for a
-// 32-point sponge, half of a 128-wide one): 1032^3 step with pml_width 32,
-// 3.70 against 3.92 ms with the 128 x 32 tiles, which are the faster ones
-// when eta is read everywhere (4.00 against 4.11 ms).
-using F32WaveWide =
+// Tiles of the wave step's data regions (Kind::WaveRegions, with a sponge
+// width): 4 x 2 (fp32) or 2 x 2 (fp64) per thread, 64 x 8 threads -> 256 x
+// 16 or 128 x 16 tiles.  Every tile reads eta on the columns within the
+// sponge width of its x edges (a quarter of a 256-wide tile for a 32-point
+// sponge, half of a 128-wide one): 1032^3 step with pml_width 32, 3.70
+// against 3.92 ms with the 128 x 32 tiles, which are the faster ones when
+// eta is read everywhere (4.00 against 4.11 ms).  The PML step's data
+// regions (Kind::WavePmlRegions) keep its primary tiles: on 256 x 16 its
+// eta masks and rings spill registers.
+using F32WaveRegions =
     TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, false, false, 1, false, true>;
-using F64WaveWide =
+using F64WaveRegions =
     TileCfg<2, 2, 64, 8, 1, 0, true, 2, false, true, true, false, false, 1, false, true>;
 
 // Narrow tiles for the thin x slabs of the wave step's sponge (32 columns):
@@ -77,18 +79,18 @@ using F64WavePmlNarrow =
 template <typename T, int R, Kind K>
 struct KindCfg {
     static constexpr bool f64 = std::is_same<T, double>::value;
-    static constexpr bool pml = K == Kind::WavePml || K == Kind::WavePmlNarrow;
+    static constexpr bool pml =
+        K == Kind::WavePml || K == Kind::WavePmlNarrow || K == Kind::WavePmlRegions;
     static constexpr bool narrow = K == Kind::WaveNarrow || K == Kind::WavePmlNarrow;
-    static constexpr bool wide = K == Kind::WaveWide;
-    static constexpr bool wave = K == Kind::Wave || K == Kind::WaveNarrow ||
-                                 K == Kind::WaveNoEta || wide || pml;
-    static constexpr bool eta = K != Kind::WaveNoEta;
+    static constexpr bool regions = K == Kind::WaveRegions || K == Kind::WavePmlRegions;
+    static constexpr bool wide = K == Kind::WaveRegions;
+    static constexpr bool wave = K == Kind::Wave || K == Kind::WaveNarrow || regions || pml;
     using Apply = typename std::conditional<f64, F64Apply,
                   typename std::conditional<R == 1, F32ApplyR1, F32Apply>::type>::type;
     using Cfg = typename std::conditional<
         K == Kind::ApplyWide && R == 1 && !f64, F32ApplyR1Wide,
         typename std::conditional<
-        wide, typename std::conditional<f64, F64WaveWide, F32WaveWide>::type,
+        wide, typename std::conditional<f64, F64WaveRegions, F32WaveRegions>::type,
         typename std::conditional<
             narrow && !(pml && f64),
             typename std::conditional<f64, F64WaveNarrow, F32WaveNarrow>::type,
@@ -101,21 +103,21 @@ struct KindCfg {
 };
 
 // Variants that exist for radius R (the others fall back to the primary
-// ones): the row-wide apply for fp32 R = 1, the narrow and eta-free wave
-// kernels for R = 4, the radius of the acoustic model with a sponge.
+// ones): the row-wide apply for fp32 R = 1, the narrow and wide wave and
+// PML kernels for R = 4, the radius of the acoustic model with a sponge.
 template <typename T, int R>
 constexpr bool kind_exists(Kind k) {
     return k == Kind::Apply || k == Kind::Wave || k == Kind::WavePml ||
            (k == Kind::ApplyWide && R == 1 && std::is_same<T, float>::value) ||
-           ((k == Kind::WaveNarrow || k == Kind::WaveNoEta || k == Kind::WavePmlNarrow ||
-             k == Kind::WaveWide) &&
+           ((k == Kind::WaveNarrow || k == Kind::WavePmlNarrow || k == Kind::WaveRegions ||
+             k == Kind::WavePmlRegions) &&
             R == 4);
 }
 
 template <typename T, int R, Kind K>
 int launch_kind(const StarArgs<T> &a, int nwg, hipStream_t stream) {
     using KC = KindCfg<T, R, K>;
-    hipLaunchKernelGGL((star2p5d_kernel<T, R, KC::wave, typename KC::Cfg, KC::eta, KC::pml>),
+    hipLaunchKernelGGL((star2p5d_kernel<T, R, KC::wave, typename KC::Cfg, KC::pml, KC::regions>),
                        dim3(nwg), dim3(KC::Cfg::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }
@@ -126,7 +128,7 @@ int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, voi
                  hipStream_t stream, int pw) {
     StarArgs<T> a = make_args<T, R>(d, g.box, in, out, u_prev, vel2, eta, wscale, g.tiles_x,
                                     g.tiles_y, g.chunk_len, g.nwg);
-    a.pw = g.kind == Kind::WaveWide ? pw : 0;
+    a.pw = (g.kind == Kind::WaveRegions || g.kind == Kind::WavePmlRegions) ? pw : 0;
     a.ga_nwg = g.a_nwg;
     a.ga_tiles = g.a_tiles;
     a.ga_len = g.a_len;
@@ -140,13 +142,13 @@ int launch_typed(const stencil3d_desc &d, const Geometry &g, const void *in, voi
         if constexpr (kind_exists<T, R>(Kind::WaveNarrow))
             return launch_kind<T, R, Kind::WaveNarrow>(a, g.nwg, stream);
         break;
-    case Kind::WaveNoEta:
-        if constexpr (kind_exists<T, R>(Kind::WaveNoEta))
-            return launch_kind<T, R, Kind::WaveNoEta>(a, g.nwg, stream);
+    case Kind::WaveRegions:
+        if constexpr (kind_exists<T, R>(Kind::WaveRegions))
+            return launch_kind<T, R, Kind::WaveRegions>(a, g.nwg, stream);
         break;
-    case Kind::WaveWide:
-        if constexpr (kind_exists<T, R>(Kind::WaveWide))
-            return launch_kind<T, R, Kind::WaveWide>(a, g.nwg, stream);
+    case Kind::WavePmlRegions:
+        if constexpr (kind_exists<T, R>(Kind::WavePmlRegions))
+            return launch_kind<T, R, Kind::WavePmlRegions>(a, g.nwg, stream);
         break;
     case Kind::WavePml: return launch_kind<T, R, Kind::WavePml>(a, g.nwg, stream);
     case Kind::WavePmlNarrow:
@@ -191,8 +193,8 @@ Shape shape_k(Kind k) {
     case Kind::ApplyWide: return shape_of<T, R, Kind::ApplyWide>();
     case Kind::Wave: return shape_of<T, R, Kind::Wave>();
     case Kind::WaveNarrow: return shape_of<T, R, Kind::WaveNarrow>();
-    case Kind::WaveNoEta: return shape_of<T, R, Kind::WaveNoEta>();
-    case Kind::WaveWide: return shape_of<T, R, Kind::WaveWide>();
+    case Kind::WaveRegions: return shape_of<T, R, Kind::WaveRegions>();
+    case Kind::WavePmlRegions: return shape_of<T, R, Kind::WavePmlRegions>();
     case Kind::WavePml: return shape_of<T, R, Kind::WavePml>();
     case Kind::WavePmlNarrow: return shape_of<T, R, Kind::WavePmlNarrow>();
     default: return shape_of<T, R, Kind::Apply>();

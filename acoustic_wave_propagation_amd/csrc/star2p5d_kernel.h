@@ -298,19 +298,17 @@ struct Rings {
     static constexpr int U = clcm(clcm(U0, NE), HE);   // z-loop unroll
 };
 
-// WAVE: fused wave epilogue.  ETA (wave only): read eta; without it the
-// kernel evaluates the same update with eta = 0 (no eta stream, and the
-// factors 1 - eta and 1 / (1 + eta) fold away exactly), for boxes where the
-// caller guarantees eta = 0.  E7 (wave with eta): the PML step, which adds
-// the eta-gradient coupling sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) -
+// WAVE: fused wave epilogue.  E7 (wave): the PML step, which adds the
+// eta-gradient coupling sum_a (eta(p+e_a) - eta(p-e_a)) (u(p+e_a) -
 // u(p-e_a)) / (4 h^2) to the Laplacian -- eta's 7-point stencil of halo 1
 // ("Accelerating High-Order Stencils on GPUs", smem_eta description).  As
 // in smem_eta, each plane of eta is staged in LDS with its 1-wide ring; its
-// z neighbours stay in a 3-plane register ring, as u's do.
-template <typename T, int R, bool WAVE, class C, bool ETA = true, bool E7 = false>
+// z neighbours stay in a 3-plane register ring, as u's do.  SP (wave): eta
+// read only near the faces for the sponge width a.pw (data regions).
+template <typename T, int R, bool WAVE, class C, bool E7 = false, bool SP = false>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
 star2p5d_kernel(StarArgs<T> a) {
-    static_assert(!E7 || (WAVE && ETA), "the eta stencil belongs to the wave update with eta");
+    static_assert(!E7 || WAVE, "the eta stencil belongs to the wave update");
     constexpr int VX = C::VX, VY = C::VY, LX = C::LX;
     constexpr int NT = C::NT, TX = C::TX, TY = C::TY;
     using RG = Rings<R, WAVE, C, E7>;
@@ -386,25 +384,38 @@ star2p5d_kernel(StarArgs<T> a) {
         soff[j] = (oy0 + j < a.by1 && ox < a.bx1) ? ooff[j] : kOOB;
     }
     const int nvx = max(0, min(VX, a.bx1 - ox));  // written columns (ragged x)
-    // eta of the wave step with data regions (a.pw > 0): a lane reads eta
-    // in every plane on its rows within pw of an interior face in y, and on
-    // all its rows if its columns lie within pw of an interior face in x or
-    // of an x edge of its tile; its other loads read eta only in the planes
-    // within pw of a z face.  Elsewhere eta is zero (the caller's
-    // guarantee) and the load takes the out-of-range offset: no memory
+    // eta with data regions (a.pw > 0; eta is zero at every point at least
+    // pw from all interior faces): a lane reads eta in every plane on its
+    // rows within pw of an interior face in y, and on all its rows if its
+    // columns lie within pw of an interior face in x or of an x edge of its
+    // tile; its other loads read eta only in the planes within pw of a z
+    // face.  Elsewhere the load takes the out-of-range offset: no memory
     // traffic, and it returns that zero.  The tile-edge columns give every
     // tile of a row the same load pattern, which keeps the tiles streaming
     // in step (their halo rows come from each other's loads in L2); tiles
     // that read eta on different columns drift apart and lose that reuse.
-    uint32_t eoff[VY];
-    {
-        const int lo = R + a.pw;
-        const bool xs = a.pw == 0 || ox < lo || ox + VX > nx - lo || ox - gx0 < a.pw ||
-                        gx0 + TX - (ox + VX) < a.pw;
+    // The PML step's eta ring follows the same rule point by point (its
+    // units left and right of the tile always lie in the tile-edge band).
+    // Bit j of emask: row j reads eta in every plane; bit VY + q: the eta
+    // ring unit q does (set for every point without SP).
+    const int elo = R + a.pw;  // first x (y, z) at least pw inside the interior
+    auto eta_cols = [&](int x) {  // a group at x lies in the x band
+        return !SP || x < elo || x + VX > nx - elo || x - gx0 < a.pw ||
+               gx0 + TX - (x + VX) < a.pw;
+    };
+    auto eta_row = [&](int y) { return y < elo || y >= ny - elo; };
+    auto eta_plane = [&](int k, int j) {
+        const int z = z0 + dir * (k + j);
+        return !SP || z < elo || z >= a.nz - elo;
+    };
+    uint32_t emask = 0;
 #pragma unroll
-        for (int j = 0; j < VY; ++j)
-            eoff[j] = (xs || oy0 + j < lo || oy0 + j >= ny - lo) ? ooff[j] : kOOB;
-    }
+    for (int j = 0; j < VY; ++j) emask |= (eta_cols(ox) || eta_row(oy0 + j)) ? 1u << j : 0u;
+    // eta offset of row j (or ring unit j - VY) in a plane where zs says
+    // whether the plane lies near a z face
+    auto eta_off = [&](uint32_t off, int j, bool zs) {
+        return (!SP || zs || ((emask >> j) & 1u)) ? off : kOOB;
+    };
     const int lcol = PADL + lx * VX;
     const int lrow0 = R + ly * VY;
 
@@ -446,6 +457,7 @@ star2p5d_kernel(StarArgs<T> a) {
             const int side = u / GX, g = u - side * GX;
             const int gy = side ? gy0 + TY : gy0 - 1;
             eh_off[q] = ((uint32_t)gy * (uint32_t)nx + (uint32_t)(gx0 + g * VX)) * ES;
+            emask |= (eta_cols(gx0 + g * VX) || eta_row(gy)) ? 1u << (VY + q) : 0u;
             eh_l[q] = (side ? TY + 1 : 0) * LP + PADL + g * VX;
         } else if (u < NYE + NXE) {
             // the group ending at gx0-1 (it may start in the previous row,
@@ -454,6 +466,7 @@ star2p5d_kernel(StarArgs<T> a) {
             const int xu = u - NYE, side = xu / TY, row = xu - side * TY;
             const int gx = side ? gx0 + TX : gx0 - VX;
             eh_off[q] = ((uint32_t)(gy0 + row) * (uint32_t)nx + (uint32_t)gx) * ES;
+            emask |= 1u << (VY + q);
             eh_l[q] = (1 + row) * LP + (side ? PADL + TX : PADL - VX);
         } else {
             eh_off[q] = kOOB;
@@ -493,26 +506,28 @@ star2p5d_kernel(StarArgs<T> a) {
             bload<T, VX, LAUX>(rp, ooff[jj], up[e][jj]);
             bload<T, VX, LAUX>(rv, ooff[jj], v2[e][jj]);
         }
-        if constexpr (ETA && !E7) {
+        if constexpr (!E7) {
             const rsrc_t re = rsrc_at(a.eta, k, 0, needed);
-            const int z = z0 + dir * k;
-            const bool zs = a.pw == 0 || z < R + a.pw || z >= a.nz - R - a.pw;
+            const bool zs = eta_plane(k, 0);
 #pragma unroll
             for (int jj = 0; jj < VY; ++jj)
-                bload<T, VX, LAUX>(re, zs ? ooff[jj] : eoff[jj], et[e][jj]);
+                bload<T, VX, LAUX>(re, eta_off(ooff[jj], jj, zs), et[e][jj]);
         }
     };
     auto load_eta = [&](int k, int j, bool needed, auto slot_c) {
         constexpr int s = decltype(slot_c)::value;
         const rsrc_t r = rsrc_at(a.eta, k, j, needed);
+        const bool zs = eta_plane(k, j);
 #pragma unroll
-        for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(r, ooff[jj], ew[s][jj]);
+        for (int jj = 0; jj < VY; ++jj) bload<T, VX, LAUX>(r, eta_off(ooff[jj], jj, zs), ew[s][jj]);
     };
     auto load_eta_halo = [&](int k, bool needed, auto slot_c) {
         constexpr int h = decltype(slot_c)::value;
         const rsrc_t r = rsrc_at(a.eta, k, 0, needed);
+        const bool zs = eta_plane(k, 0);
 #pragma unroll
-        for (int q = 0; q < KHE; ++q) bload<T, VX, LAUX>(r, eh_off[q], ehs[h][q]);
+        for (int q = 0; q < KHE; ++q)
+            bload<T, VX, LAUX>(r, eta_off(eh_off[q], VY + q, zs), ehs[h][q]);
     };
 
     // prologue: window planes at step offsets -R .. R+D-1 into slots
@@ -681,7 +696,7 @@ star2p5d_kernel(StarArgs<T> a) {
                     if constexpr (WAVE) {
                         // the weights carry dt^2/h^2: acc = dt^2 * Lap(u)
                         // (PML step: plus dt^2 times the coupling)
-                        const T e = E7 ? ew[EC7][j][i] : ETA ? et[EC][j][i] : T(0);
+                        const T e = E7 ? ew[EC7][j][i] : et[EC][j][i];
                         acc = damp_div<T, E7>(
                             T(2) * ctr - (T(1) - e) * up[EC][j][i] + v2[EC][j][i] * acc,
                             T(1) + e);

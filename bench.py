@@ -19,9 +19,9 @@ bounded number of whole-grid applications.
 turn FETCH_SIZE / WRITE_SIZE into bytes); --ceilings times copy kernels that
 walk memory like the apply (libwalkcopy.so) beside it; --only-headline skips everything
 but the timed stencil launches, --only-others runs only the Jacobi and fp64
-workloads, --only-wave {wave,pml,regions,blocked,both,all} only the 1032^3
-leapfrog with those step kinds (both: wave and pml; all: also blocked; all
-for profiler runs).
+workloads, --only-wave {wave,pml,regions,pml_regions,blocked,both,all} only
+the 1032^3 leapfrog with those step kinds (both: wave and pml; all: every
+kind; for profiler runs).
 """
 from __future__ import annotations
 
@@ -343,11 +343,12 @@ def bench_headline(torch, B, wl, args):
 
 
 def bench_wave(torch, B, wl, args,
-               variants=("wave", "pml", "regions", "blocked", "pml_blocked")):
+               variants=("wave", "pml", "regions", "pml_regions", "blocked",
+                         "pml_blocked")):
     """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
-    the pointwise step ("wave"), the PML kernel's step ("pml"), the
-    pointwise step launched as data regions ("regions": pml_width = the
-    sponge width, so the inner box runs without the eta stream) and the
+    the pointwise step ("wave"), the PML kernel's step ("pml"), both
+    launched as data regions ("regions", "pml_regions": pml_width = the
+    sponge width, so eta is read only near the faces) and the
     time-blocked runs ("blocked", "pml_blocked": two steps per pass over four
     buffers)."""
     w = wl.WAVE_1024
@@ -386,10 +387,13 @@ def bench_wave(torch, B, wl, args,
     # lack the other eta reads
     dr = B.desc_init("f32", shp, w.radius)
     dr.pml_width = e["sponge"]
-    eta_pts = eta_read_points(w.interior, e["sponge"])
+    # (the PML step's data regions run on its own 128-wide tiles)
+    eta_pts = {"regions": eta_read_points(w.interior, e["sponge"]),
+               "pml_regions": eta_read_points(w.interior, e["sponge"],
+                                              tile_x=128)}
     res = {}
     for v in variants:
-        dv = dr if v == "regions" else d
+        dv = dr if v in ("regions", "pml_regions") else d
         if v in ("blocked", "pml_blocked"):
             # 20 steps = 10 passes; the fields end in (u_prev, u) again
             fn = lambda: B.wave_run_blocked(d, u_prev, u, work[0], work[1],
@@ -398,7 +402,8 @@ def bench_wave(torch, B, wl, args,
                                             pml=(v == "pml_blocked"))
         else:
             fn = lambda: B.wave_run(dv, u_prev, u, vel2, eta, e["dt"], e["h"],
-                                    w.sweeps, src, trace, pml=(v == "pml"))
+                                    w.sweeps, src, trace,
+                                    pml=(v in ("pml", "pml_regions")))
         wall, durs = timed_launches(torch, fn, runs, 1)
         per = float(durs.mean()) / w.sweeps
         ach = nbytes / per / 1e9
@@ -431,8 +436,8 @@ def bench_wave(torch, B, wl, args,
             rl["note"] = ("achieved/frac: pass bytes over pass time (one "
                           "pass = two steps); *_step_equivalent: 20.09 "
                           "B/point per step over the per-step time")
-        if v == "regions":
-            true_b = nbytes - 4 * (w.interior_points - eta_pts)
+        if v in ("regions", "pml_regions"):
+            true_b = nbytes - 4 * (w.interior_points - eta_pts[v])
             res[v]["roofline"]["true_bytes_per_step"] = true_b
             res[v]["roofline"]["achieved_true_bytes"] = round(
                 true_b / per / 1e9, 1)
@@ -440,6 +445,7 @@ def bench_wave(torch, B, wl, args,
         log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % ({"wave": "wave", "pml": "wave, PML step",
                 "regions": "wave, data regions",
+                "pml_regions": "wave, PML step, data regions",
                 "blocked": "wave, time-blocked",
                 "pml_blocked": "wave, PML step, time-blocked"}[v],
                res[v]["value"],
@@ -447,15 +453,17 @@ def bench_wave(torch, B, wl, args,
     del vel2, eta, u_prev, u, work
     torch.cuda.empty_cache()
     for v in variants:
-        if v in ("regions", "blocked", "pml_blocked"):  # updates timed above
+        if v in ("regions", "pml_regions", "blocked",
+                 "pml_blocked"):  # updates timed above
             continue
         res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
             wl, w, args.cpu_budget / 4, pml=(v == "pml"))
     for v in ("regions", "blocked"):
         if v in res:
             res[v]["cpu_baseline"] = res.get("wave", {}).get("cpu_baseline")
-    if "pml_blocked" in res:
-        res["pml_blocked"]["cpu_baseline"] = res.get("pml", {}).get("cpu_baseline")
+    for v in ("pml_regions", "pml_blocked"):
+        if v in res:
+            res[v]["cpu_baseline"] = res.get("pml", {}).get("cpu_baseline")
     if "wave" not in res:
         return res
     out = dict(workload=w.name, **res["wave"])
@@ -465,6 +473,8 @@ def bench_wave(torch, B, wl, args,
                                "B/point)")
     if "pml" in res:
         out["pml_step"] = res["pml"]
+        if "pml_regions" in res:
+            out["pml_step"]["data_regions"] = res["pml_regions"]
         if "pml_blocked" in res:
             out["pml_step"]["time_blocked"] = res["pml_blocked"]
     if "regions" in res:
@@ -479,7 +489,8 @@ def eta_read_points(interior, pw, tile_x=256, group=4):
     sponge width pw): every point of the rows within pw of a y face (their
     own launches); in the other rows every point of the planes within pw of
     a z face, and elsewhere the 4-column groups within pw of an x face or of
-    an x edge of their 256-wide tile."""
+    an x edge of their tile_x-wide tile (256 for the wave step, 128 for the
+    PML step)."""
     iz, iy, ix = interior
     ox = np.arange(0, ix, group)              # group starts, interior coords
     gx0 = ox // tile_x * tile_x               # tile origins
@@ -680,8 +691,8 @@ def main():
                     help="time only the copy kernels with the apply's memory "
                          "walk (libwalkcopy.so) beside the apply, one JSON line")
     ap.add_argument("--only-wave",
-                    choices=("wave", "pml", "regions", "blocked",
-                             "pml_blocked", "both", "all"),
+                    choices=("wave", "pml", "regions", "pml_regions",
+                             "blocked", "pml_blocked", "both", "all"),
                     help="run only the 1032^3 leapfrog with that step "
                          "(profiling)")
     args = ap.parse_args()
@@ -716,8 +727,8 @@ def main():
     if args.only_wave:
         bench_wave(torch, B, wl, args,
                    variants={"both": ("wave", "pml"),
-                             "all": ("wave", "pml", "regions", "blocked",
-                                     "pml_blocked")}.get(
+                             "all": ("wave", "pml", "regions", "pml_regions",
+                                     "blocked", "pml_blocked")}.get(
                                  args.only_wave, (args.only_wave,)))
         if args.calib:
             calib_copy(torch)

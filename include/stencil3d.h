@@ -83,14 +83,13 @@ extern "C" {
  * for the PML region, where only the latter reads eta).  If pml_width > 0
  * the caller guarantees that eta is exactly 0 at every interior point whose
  * distance (in points, along any axis) from the nearest interior face is
- * at least pml_width.  For R = 4 the wave entry points then skip eta
- * where it is zero: the wave step reads it only near the faces (the rows
- * within pml_width of a y face as two launches of their own; in the other
- * rows on the columns near the x faces, in the planes near the z faces,
- * and on the same columns of every tile, which keeps the tiles streaming
- * in step), and the PML step launches an inner box that does not read eta
- * and the six slabs around it.  The results are bit-identical to
- * pml_width = 0 under that guarantee, and wrong where it does not hold.
+ * at least pml_width.  For R = 4 the wave and PML entry points then read
+ * eta only near the faces: the rows within pml_width of a y face as two
+ * launches of their own; in the other rows on the columns near the x
+ * faces, in the planes near the z faces, and on the same columns of every
+ * tile (which keeps the tiles streaming in step).  The results are
+ * bit-identical to pml_width = 0 under that guarantee, and wrong where it
+ * does not hold.
  * On MI355X a 1024^3 wave step with a 32-point sponge takes 3.70 ms with
  * pml_width = 32 and 4.0 ms with 0 (eta read everywhere in one launch).
  * Ignored by the plain stencil.  168 bytes, naturally aligned.
@@ -187,8 +186,8 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
  * eta dimensionless; all five arrays share d's extents and element type.
  * u_next may be the same buffer as u_prev (each point reads u_prev only at
  * itself), but must not overlap u, vel2 or eta.  dt, h finite, h > 0.
- * With d->pml_width > 0 (R = 4), eta is read only where it may be non-zero:
- * seven launches (inner box and sponge slabs) instead of one.
+ * With d->pml_width > 0 (R = 4), eta is read only where it may be non-zero
+ * (three launches: two y slabs and the rows between them).
  */
 int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u,
               void *u_next, const void *vel2, const void *eta, double dt,
@@ -210,9 +209,9 @@ int wave_step(const stencil3d_desc *d, const void *u_prev, const void *u,
  * eta is read at the interior points and their face neighbours (which may
  * lie in the halo).  Where eta is the same on a point's six face neighbours
  * G = 0 and the result is wave_step's.  Same arrays, layout, aliasing and
- * argument rules as wave_step.  With d->pml_width = p > 0 (R = 4) the
- * inner box at distance >= p+1 from every interior face, where G = 0, runs
- * the eta-free kernel (same bits, up to the sign of a zero result).
+ * argument rules as wave_step.  With d->pml_width > 0 (R = 4) eta is read
+ * only where it may be non-zero, in the launches of wave_step (same bits:
+ * an eta value not read enters as the zero it is guaranteed to be).
  */
 int wave_step_pml(const stencil3d_desc *d, const void *u_prev,
                   const void *u, void *u_next, const void *vel2,
@@ -273,9 +272,8 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
  * conditions: outside the interior u_prev and u must hold the same values
  * (zero, as a leapfrog from zero halos keeps them), since a pass takes
  * level k+1's non-interior points to be level k's; and d->pml_width is
- * ignored by
- * the two-step passes (eta is read on the whole interior; the eta-free
- * inner box of wave_step gives the same values up to the sign of a zero).
+ * ignored by the two-step passes (eta is read on the whole interior, which
+ * gives the same bits where the pml_width claim holds).
  * Same arguments as wave_run otherwise.  Errors: those of wave_run, plus
  * ST_ERR_NULL / ST_ERR_ALIGN for work0 or work1 and ST_ERR_ALIAS where any
  * two of the four u buffers, vel2 and eta overlap (vel2 and eta may be the

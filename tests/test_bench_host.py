@@ -166,3 +166,6 @@ def test_eta_read_points_model():
     n, pw = 1024, 32
     want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 4))
     assert b.eta_read_points((n, n, n), pw) == want
+    # the PML step's 128-wide tiles: the 32 columns at each edge are half
+    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 2))
+    assert b.eta_read_points((n, n, n), pw, tile_x=128) == want

@@ -205,8 +205,8 @@ def test_mixed_chunking_and_source_in_the_overlap(torch_dev):
 
 def test_no_source_and_pml_width(torch_dev):
     """Without a source trace; with pml_width set the single steps of
-    wave_run split the interior into data regions (eta-free inner box) while
-    the passes read eta everywhere: equal up to the sign of zero."""
+    wave_run launch data regions (eta read only near the faces) while the
+    passes read eta everywhere: equal."""
     torch, _ = torch_dev
     shape = (60, 70, 90)
     up, uc, v2, _ = _fields(shape, 1500)

@@ -538,14 +538,16 @@ def test_wave_pml_regions(oracle_mod, torch_dev):
     check_close(interior(runs[0], R), interior(ref, R), 1e-4, "3 free steps")
 
 
+@pytest.mark.parametrize("pml_step", [False, True], ids=["wave", "pml"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
-def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype):
+def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype, pml_step):
     """A grid wide enough for tiles whose columns lie away from the x
-    sponge and from their own x edges (1000 interior columns; 256-wide
-    tiles in fp32, 128-wide in fp64), so those lanes really skip eta
-    outside the z-sponge planes: pml_width 12 (exact) and 13
-    (conservative) give the same bits as 0 over three steps, 6 (a false
-    claim) does not, and the result matches the oracle."""
+    sponge and from their own x edges (1000 interior columns; wave step
+    256-wide tiles in fp32, 128-wide in fp64; PML step 128 and 64), so
+    those lanes really skip eta outside the z-sponge planes: pml_width 12
+    (exact) and 13 (conservative) give the same bits as 0 over three
+    steps, 6 (a false claim) does not, and the result matches the oracle
+    (the PML step's: eta's gradient coupling included)."""
     import dataclasses
     torch, _ = torch_dev
     dt = "f32" if dtype == np.float32 else "f64"
@@ -554,14 +556,15 @@ def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype):
                             extra=dict(base.extra, sponge=12))
     e = w.extra
     R = w.radius
-    log("case data regions wide %s %s" % (dt, w.shape))
+    log("case data regions wide %s %s pml=%s" % (dt, w.shape, pml_step))
     u_prev, u, vel2, eta = _wave_fields(w, torch)
     runs = {}
     for pml in (0, 12, 13, 6):
         d = B.desc_init(dt, w.shape, R)
         d.pml_width = pml
         a, b = u_prev.clone(), u.clone()
-        older, newest = B.wave_run(d, a, b, vel2, eta, e["dt"], e["h"], 3)
+        older, newest = B.wave_run(d, a, b, vel2, eta, e["dt"], e["h"], 3,
+                                   pml=pml_step)
         runs[pml] = newest.cpu().numpy()
     for pml in (12, 13):
         assert np.array_equal(runs[pml].view(np.uint8),
@@ -570,7 +573,7 @@ def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype):
     c = oracle_mod.laplacian_weights(R)
     _, ref = oracle_mod.wave_run(u_prev.cpu().numpy(), u.cpu().numpy(),
                                  vel2.cpu().numpy(), eta.cpu().numpy(), R, c,
-                                 e["dt"], e["h"], 3)
+                                 e["dt"], e["h"], 3, pml=pml_step)
     tol = 1e-4 if dtype == np.float32 else 1e-11
     check_close(interior(runs[12], R), interior(ref, R), tol,
                 "3 free steps, wide data regions")
@@ -578,12 +581,12 @@ def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype):
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_wave_data_regions_ragged(oracle_mod, torch_dev, dtype):
-    """The data-region launch (an eta-free inner box plus six slabs that
-    read eta, for R = 4) on a ragged non-cubic grid with a 12-point sponge,
-    through wave_run: pml_width 12 (exact) and 30 (conservative) split the
-    interior and give the same bits as 0; 40 cannot split (the inner box
-    would be empty in y) and is the single launch; 1 is a false claim and
-    must change the result.  Also checked against the oracle."""
+    """The data-region launches (two y slabs and the rows between them, eta
+    read only near the faces, for R = 4) on a ragged non-cubic grid with a
+    12-point sponge, through wave_run: pml_width 12 (exact) and 30
+    (conservative) give the same bits as 0; at 40 the slabs would overlap
+    and one launch reads eta near the faces; 1 is a false claim and must
+    change the result.  Also checked against the oracle."""
     import dataclasses
     torch, _ = torch_dev
     dt = "f32" if dtype == np.float32 else "f64"

@@ -168,10 +168,10 @@ def test_pml_sponge_steps_teacher_forced(oracle_mod, torch_dev):
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_pml_data_regions_and_run(oracle_mod, torch_dev, dtype):
     """wave_run_pml on a ragged grid with a 12-point sponge: pml_width 12
-    (exact: inner box at depth >= 13, where eta and its differences vanish)
-    and 30 (conservative) run the eta-free inner box and give the same bits
-    as 0; 40 cannot split (single launch); 1 is a false claim and changes
-    the result.  Three free steps against the oracle's loop."""
+    (exact) and 30 (conservative) read eta only near the faces and give the
+    same bits as 0; at 40 the y slabs would overlap (one launch, eta still
+    read only near the faces); 1 is a false claim and changes the result.
+    Three free steps against the oracle's loop."""
     dt = _name(dtype)
     base = wl.WAVE_128_RANDOM
     w = dataclasses.replace(base, shape=(82, 75, 141), dtype=dt,

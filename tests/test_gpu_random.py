@@ -148,8 +148,8 @@ def _sponge(shape, R, width, emax=0.1):
 @pytest.mark.parametrize("seed", range(8))
 def test_random_wave_data_regions(oracle_mod, torch_dev, seed):
     """R = 4 wave steps with pml_width on random ragged shapes: the
-    data-region launches (eta-free inner box, sponge slabs, narrow x slabs
-    where they are thin) give the same bits as one launch and match the
+    data-region launches (two y slabs and the rows between them, eta read
+    only near the faces) give the same bits as one launch and match the
     oracle."""
     g = np.random.default_rng(900 + seed)
     R = 4
