@@ -579,6 +579,53 @@ def test_wave_data_regions_wide(oracle_mod, torch_dev, dtype, pml_step):
                 "3 free steps, wide data regions")
 
 
+def test_data_regions_1024_random(oracle_mod, torch_dev):
+    """The data-region launches in the configuration the benchmark times
+    (1032^3, the workload's vel2 and 32-point sponge as eta, pml_width 32)
+    on random u_prev and u (seeded, drawn on the device), so the field is
+    non-zero inside the sponge: one wave step and one PML step each give
+    the same bits as one launch reading eta everywhere, over the whole
+    array (halos untouched), and match the oracle on a slab that crosses
+    the z sponge's inner edge."""
+    torch, _ = torch_dev
+    w = wl.WAVE_1024
+    e, R = w.extra, w.radius
+    log("case data regions 1024 random %s" % (w.shape,))
+    vel2 = upload_planes(lambda a, b: wl.vel2_planes(w, a, b), w.shape,
+                         w.np_dtype)
+    eta = upload_planes(lambda a, b: wl.eta_planes(w, a, b), w.shape,
+                        w.np_dtype)
+    g = torch.Generator(device=vel2.device).manual_seed(781)
+    up = torch.empty_like(vel2).uniform_(-1, 1, generator=g)
+    uc = torch.empty_like(vel2).uniform_(-1, 1, generator=g)
+    # z planes R + 26 .. R + 38: the sponge's inner edge at depth 32
+    z0, z1 = R + 26, R + 38
+    sl = slice(z0 - R, z1 + R)
+    sub = [t[sl].cpu().numpy() for t in (up, uc, vel2, eta)]
+    c = list(B.desc_init("f32", w.shape, R).cx[:R + 1])
+    s = np.float32(SENTINEL)
+    for step, ref_fn, name in ((B.wave_step, oracle_mod.wave_step, "wave"),
+                               (B.wave_step_pml, oracle_mod.wave_step_pml, "pml")):
+        log("  %s step, pml_width 0 and %d" % (name, e["sponge"]))
+        outs = []
+        for pw in (0, e["sponge"]):
+            d = B.desc_init("f32", w.shape, R)
+            d.pml_width = pw
+            out = sentinel_like(w.shape, w.np_dtype)
+            step(d, up, uc, out, vel2, eta, e["dt"], e["h"])
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), "%s: data regions differ" % name
+        ref = ref_fn(*sub, R, c, e["dt"], e["h"])
+        got = outs[1][z0:z1].cpu().numpy()
+        check_close(got[:, R:-R, R:-R], ref[R:-R, R:-R, R:-R], F32_TOL,
+                    "%s data regions 1024 slab z %d..%d" % (name, z0, z1))
+        assert np.all(outs[1][:R].cpu().numpy() == s)
+        del outs, out
+    del vel2, eta, up, uc
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_wave_data_regions_ragged(oracle_mod, torch_dev, dtype):
     """The data-region launches (two y slabs and the rows between them, eta
