@@ -27,8 +27,14 @@ using Wave2F64 = Wave2Cfg<2, 1, 16, 40, 3, true, true, 2, true>;
 // and the two stages' eta tiles need more registers and LDS than three waves
 // per SIMD leave, so 512 threads at two waves per SIMD over a 64 x 32
 // extended tile (fp32; output tile 56 x 24 at R = 4) or 32 x 32 (fp64).
-using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true>;
-using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true>;
+// Tiles numbered down bands of 6 tile columns.  The order decides which
+// tiles share an XCD's L2 at a time; measured on the 1032^3 run (ms per
+// step, same box, bands of 0 (rows) / 4 / 5 / 6 / 7 / 8 / 10 tile
+// columns): PML pass 4.09-4.14 / 4.12 / 4.34 / 3.94 / 4.12 / 4.15 / 4.15;
+// the plain pass 3.40-3.41 / 3.52 / 4.32 / 3.66-3.68 / 3.82 / 3.50 / 3.56,
+// so it keeps the row order.  Bit-identical in every order.
+using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true, 6>;
+using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true, 6>;
 
 template <typename T, int R, class C, bool E7>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,

@@ -79,6 +79,25 @@ inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t min_len, int6
     return p;
 }
 
+// Tile index -> tile index in x-fastest order, numbering the tiles down
+// vertical bands of bw tile columns (x fastest within a band, whose width is
+// bw except for a narrower last band), so that a run of consecutive indices
+// covers a compact block of the tile grid rather than a strip of rows.
+// Workgroups that run together on one XCD stream consecutive indices
+// (xcd_remap), so the overlap of their tiles (rows and columns that
+// neighbouring tiles both read) is read while it sits in that XCD's L2.
+// bw <= 0 or bw >= tiles_x: the identity.  A bijection on
+// [0, tiles_x * tiles_y).
+__attribute__((always_inline)) constexpr int band_order(int t, int tiles_x, int tiles_y, int bw) {
+    if (bw <= 0 || bw >= tiles_x) return t;
+    const int per = bw * tiles_y;  // tiles of a whole band
+    const int b = t / per, local = t - b * per;
+    const int x0 = b * bw;
+    const int w = tiles_x - x0 < bw ? tiles_x - x0 : bw;
+    const int row = local / w;
+    return row * tiles_x + x0 + (local - row * w);
+}
+
 // What one workgroup streams.
 struct WgWork {
     int tile;   // tile index, x fastest

@@ -69,6 +69,38 @@ int main() {
                 break;
             }
     }
+    // band_order: a bijection on the tile grid for every band width, the
+    // identity for widths <= 0 or >= tiles_x, and a run of bw * k
+    // consecutive indices inside a whole band is a bw x k block
+    long bands = 0;
+    for (int tx = 1; tx <= 24; ++tx)
+        for (int ty = 1; ty <= 24; ++ty)
+            for (int bw = -1; bw <= tx + 1; ++bw) {
+                const int n = tx * ty;
+                std::vector<int> hit(n, 0);
+                for (int t = 0; t < n; ++t) {
+                    const int m = st::band_order(t, tx, ty, bw);
+                    if (m < 0 || m >= n) {
+                        fail("band_order range", tx, ty, bw, 0);
+                        break;
+                    }
+                    hit[m]++;
+                    if ((bw <= 0 || bw >= tx) && m != t) fail("band_order identity", tx, ty, bw, 0);
+                    if (bw > 0 && bw < tx && t < (tx / bw) * bw * ty) {
+                        // whole band: column and row from the index
+                        const int b = t / (bw * ty), l = t % (bw * ty);
+                        if (m % tx != b * bw + l % bw || m / tx != l / bw)
+                            fail("band_order block", tx, ty, bw, 0);
+                    }
+                }
+                for (int h : hit)
+                    if (h != 1) {
+                        fail("band_order bijection", tx, ty, bw, 0);
+                        break;
+                    }
+                ++bands;
+            }
+    std::printf("band orders checked: %ld\n", bands);
     const long depths[] = {1, 2, 3, 5, 8, 13, 16, 17, 31, 64, 100, 127, 255, 512, 1016, 1024};
     const long tiles[] = {1, 2, 7, 8, 9, 63, 255, 256, 257, 300, 304, 511, 513, 700};
     const long caps[] = {80, 256, 1024};
