@@ -16,9 +16,10 @@ namespace {
 // tile 56 x 32.  The halo units wait in private LDS slots (PSTAGE), which
 // leaves room for the vel2/eta ring and two stage-2 tile sets; thread rows
 // are paired for conflict-free LDS access where the shape allows (PAIR,
-// R = 4: 80-float rows, 146 KB).  Measured on the 1032^3 run (ms per step):
-// 64 x 32 with R+1 full stage-1 tile sets 3.585, 64 x 40 as shipped
-// 3.29-3.40 (box to box), 64 x 48 with one stage-2 set 3.352.
+// R = 4: 80-float rows, 146 KB).  Measured on the 1032^3 run (ms per step,
+// before the per-round tile order of launch_t): 64 x 32 with R+1 full
+// stage-1 tile sets 3.585, 64 x 40 as shipped 3.29-3.40 (box to box), 64 x 48
+// with one stage-2 set 3.352; the shipped shape with that order: 3.03-3.08.
 using Wave2F32 = Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>;
 // fp64: 2 x 1 points per thread (16-byte groups), same thread layout; the
 // extended tile is 32 x 40, the output tile 24 x 32 at R = 4.
@@ -27,14 +28,8 @@ using Wave2F64 = Wave2Cfg<2, 1, 16, 40, 3, true, true, 2, true>;
 // and the two stages' eta tiles need more registers and LDS than three waves
 // per SIMD leave, so 512 threads at two waves per SIMD over a 64 x 32
 // extended tile (fp32; output tile 56 x 24 at R = 4) or 32 x 32 (fp64).
-// Tiles numbered down bands of 6 tile columns.  The order decides which
-// tiles share an XCD's L2 at a time; measured on the 1032^3 run (ms per
-// step, same box, bands of 0 (rows) / 4 / 5 / 6 / 7 / 8 / 10 tile
-// columns): PML pass 4.09-4.14 / 4.12 / 4.34 / 3.94 / 4.12 / 4.15 / 4.15;
-// the plain pass 3.40-3.41 / 3.52 / 4.32 / 3.66-3.68 / 3.82 / 3.50 / 3.56,
-// so it keeps the row order.  Bit-identical in every order.
-using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true, 6>;
-using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true, 6>;
+using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true>;
+using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true>;
 
 template <typename T, int R, class C, bool E7>
 int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
@@ -60,6 +55,15 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
     g.sz = src.on ? (int32_t)src.z : -1;
     g.s0 = (T)src.v0;
     g.s1 = (T)src.v1;
+    // one workgroup per compute unit: the workgroups of a round run
+    // together, and each XCD takes a contiguous range of every round's
+    // tiles (rows of tiles, x fastest), so the 32 tiles an XCD streams at
+    // once lie next to each other and next to the other XCDs' tiles of the
+    // round.  Against a remap over the whole group (each XCD's tiles
+    // contiguous over all rounds, the tiles of one round scattered in
+    // strips), 1032^3 run, ms per step: plain pass 3.39 -> 3.08, PML pass
+    // 3.97-4.14 -> 3.94.
+    g.round = cus > 0 ? cus : 256;
     hipLaunchKernelGGL((wave2_kernel<T, R, C, E7>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s, g);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }

@@ -48,6 +48,7 @@ struct Wave2Args {
     T *out2;               // u^{n+2}
     int32_t sx, sy, sz;    // source point (allocated coordinates); sz = -1: no source
     T s0, s1;              // source values of steps n+1 and n+2
+    int32_t round;         // workgroups per round for xcd_remap_rounds (0: whole groups)
 };
 
 // VX x VY points per thread, LX x LY threads covering the extended tile,
@@ -71,16 +72,12 @@ struct Wave2Args {
 // with the R rows below it (whole waves, which skip stage 2), and the halo
 // rows above with those below.  Shapes the pairing does not tile keep the
 // plain row order.
-//
-// BAND: tiles numbered down vertical bands of this many tile columns
-// (band_order in work_plan.h; 0: x-fastest rows), which decides the tiles
-// that run at the same time on one XCD.
 template <int VX_, int VY_, int LX_, int LY_, int MINW_, bool VRING_ = true,
-          bool PSTAGE_ = false, int T2S_ = 2, bool PAIR_ = false, int BAND_ = 0>
+          bool PSTAGE_ = false, int T2S_ = 2, bool PAIR_ = false>
 struct Wave2Cfg {
     static constexpr int VX = VX_, VY = VY_, LX = LX_, LY = LY_, MINW = MINW_;
     static constexpr bool VRING = VRING_, PSTAGE = PSTAGE_, PAIR = PAIR_;
-    static constexpr int T2S = T2S_, BAND = BAND_;
+    static constexpr int T2S = T2S_;
     static constexpr int NT = LX * LY, EX = LX * VX, EY = LY * VY;
 };
 
@@ -173,9 +170,8 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     const int nx = a.nx, ny = a.ny, nz = a.nz;
     const int ntile = a.tiles_x * a.tiles_y;
     const WgWork w = wg_work((int)blockIdx.x, a.nwg, ntile, a.ga_nwg, a.ga_tiles, a.ga_len,
-                             a.chunk_len, true, true);
-    const int tile = band_order(w.tile, a.tiles_x, a.tiles_y, C::BAND);
-    const int tyi = tile / a.tiles_x, txi = tile - tyi * a.tiles_x;
+                             a.chunk_len, true, true, g.round);
+    const int tyi = w.tile / a.tiles_x, txi = w.tile - tyi * a.tiles_x;
     const int gx0 = R + txi * TX, gy0 = R + tyi * TY;  // output tile origin
     const int zs = R + w.zoff;
     const int ze = min(zs + w.len, nz - R);

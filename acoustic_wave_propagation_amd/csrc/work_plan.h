@@ -22,6 +22,18 @@ __attribute__((always_inline)) constexpr int xcd_remap(int b, int n) {
     return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
 }
 
+// xcd_remap applied to each run of `round` consecutive ids on its own (the
+// workgroups that run at the same time when each of `round` compute units
+// holds one), so that within every round each XCD owns a contiguous range
+// of that round's logical ids.  round <= 0 or round >= n: xcd_remap over
+// all of [0, n).  A bijection on [0, n) that keeps every round in place.
+__attribute__((always_inline)) constexpr int xcd_remap_rounds(int b, int n, int round) {
+    if (round <= 0 || round >= n) return xcd_remap(b, n);
+    const int r0 = b / round * round;
+    const int m = n - r0 < round ? n - r0 : round;
+    return r0 + xcd_remap(b - r0, m);
+}
+
 // Chunking of one launch.  Two groups of workgroups: group A (ids below
 // a_nwg) streams tiles [0, a_tiles) in chunks of a_len planes; group B (the
 // other nwg - a_nwg ids) streams the remaining tiles, each in `nchunks`
@@ -79,25 +91,6 @@ inline ChunkPlan plan_chunks(int64_t depth, int64_t tiles, int64_t min_len, int6
     return p;
 }
 
-// Tile index -> tile index in x-fastest order, numbering the tiles down
-// vertical bands of bw tile columns (x fastest within a band, whose width is
-// bw except for a narrower last band), so that a run of consecutive indices
-// covers a compact block of the tile grid rather than a strip of rows.
-// Workgroups that run together on one XCD stream consecutive indices
-// (xcd_remap), so the overlap of their tiles (rows and columns that
-// neighbouring tiles both read) is read while it sits in that XCD's L2.
-// bw <= 0 or bw >= tiles_x: the identity.  A bijection on
-// [0, tiles_x * tiles_y).
-__attribute__((always_inline)) constexpr int band_order(int t, int tiles_x, int tiles_y, int bw) {
-    if (bw <= 0 || bw >= tiles_x) return t;
-    const int per = bw * tiles_y;  // tiles of a whole band
-    const int b = t / per, local = t - b * per;
-    const int x0 = b * bw;
-    const int w = tiles_x - x0 < bw ? tiles_x - x0 : bw;
-    const int row = local / w;
-    return row * tiles_x + x0 + (local - row * w);
-}
-
 // What one workgroup streams.
 struct WgWork {
     int tile;   // tile index, x fastest
@@ -110,19 +103,22 @@ struct WgWork {
 // The tile and chunk of workgroup `block` of a launch of `nwg` workgroups
 // over `ntile` tiles, chunked as a ChunkPlan says.  Each group is remapped
 // on its own (remap), so every XCD sweeps a contiguous band of its group's
-// tiles.  Chunk-major order (cmaj) numbers the tiles fastest, so workgroups
-// that run together stream the same planes; otherwise the chunks of one
-// tile are neighbours.
+// tiles; with round > 0 each round of `round` workgroups of a group is
+// remapped on its own (xcd_remap_rounds), so the band is contiguous within
+// every round.  Chunk-major order (cmaj) numbers the tiles fastest, so
+// workgroups that run together stream the same planes; otherwise the
+// chunks of one tile are neighbours.
 __attribute__((always_inline)) constexpr WgWork wg_work(int block, int nwg, int ntile,
                                                         int a_nwg, int a_tiles, int a_len,
-                                                        int chunk_len, bool remap, bool cmaj) {
+                                                        int chunk_len, bool remap, bool cmaj,
+                                                        int round = 0) {
     const bool ga = block < a_nwg;
     const int gid = ga ? block : block - a_nwg;
     const int gnwg = ga ? a_nwg : nwg - a_nwg;
     const int gt0 = ga ? 0 : a_tiles;
     const int gtiles = ga ? a_tiles : ntile - a_tiles;
     const int glen = ga ? a_len : chunk_len;
-    const int wg = remap ? xcd_remap(gid, gnwg) : gid;
+    const int wg = remap ? xcd_remap_rounds(gid, gnwg, round) : gid;
     int chunk = 0, t = 0;
     if (cmaj) {
         chunk = wg / gtiles;

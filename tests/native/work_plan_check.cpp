@@ -3,6 +3,7 @@
 // kernels' workgroup map every (tile, plane) of the box is streamed by
 // exactly one workgroup, for every combination of remapping and order.
 #include <cstdio>
+#include <initializer_list>
 #include <vector>
 
 #include "work_plan.h"
@@ -69,38 +70,38 @@ int main() {
                 break;
             }
     }
-    // band_order: a bijection on the tile grid for every band width, the
-    // identity for widths <= 0 or >= tiles_x, and a run of bw * k
-    // consecutive indices inside a whole band is a bw x k block
-    long bands = 0;
-    for (int tx = 1; tx <= 24; ++tx)
-        for (int ty = 1; ty <= 24; ++ty)
-            for (int bw = -1; bw <= tx + 1; ++bw) {
-                const int n = tx * ty;
-                std::vector<int> hit(n, 0);
-                for (int t = 0; t < n; ++t) {
-                    const int m = st::band_order(t, tx, ty, bw);
-                    if (m < 0 || m >= n) {
-                        fail("band_order range", tx, ty, bw, 0);
-                        break;
-                    }
-                    hit[m]++;
-                    if ((bw <= 0 || bw >= tx) && m != t) fail("band_order identity", tx, ty, bw, 0);
-                    if (bw > 0 && bw < tx && t < (tx / bw) * bw * ty) {
-                        // whole band: column and row from the index
-                        const int b = t / (bw * ty), l = t % (bw * ty);
-                        if (m % tx != b * bw + l % bw || m / tx != l / bw)
-                            fail("band_order block", tx, ty, bw, 0);
-                    }
+    // xcd_remap_rounds: a bijection on [0, n) that keeps every round of
+    // `round` ids in place and, within a whole round, gives each XCD a
+    // contiguous range of it
+    long rounds = 0;
+    for (int n = 1; n <= 700; n += 3)
+        for (int round : {0, 1, 8, 16, 24, 64, 80, 256}) {
+            std::vector<int> hit(n, 0);
+            for (int b = 0; b < n; ++b) {
+                const int l = st::xcd_remap_rounds(b, n, round);
+                if (l < 0 || l >= n) {
+                    fail("xcd_remap_rounds range", n, round, 0, 0);
+                    break;
                 }
-                for (int h : hit)
-                    if (h != 1) {
-                        fail("band_order bijection", tx, ty, bw, 0);
-                        break;
-                    }
-                ++bands;
+                hit[l]++;
+                if (round > 0 && round < n) {
+                    const int r0 = b / round * round;
+                    if (l < r0 || l >= r0 + round) fail("xcd_remap_rounds round", n, round, b, 0);
+                    const int m = n - r0 < round ? n - r0 : round;
+                    if (l != r0 + st::xcd_remap(b - r0, m))
+                        fail("xcd_remap_rounds per round", n, round, b, 0);
+                } else if (l != st::xcd_remap(b, n)) {
+                    fail("xcd_remap_rounds whole", n, round, b, 0);
+                }
             }
-    std::printf("band orders checked: %ld\n", bands);
+            for (int h : hit)
+                if (h != 1) {
+                    fail("xcd_remap_rounds bijection", n, round, 0, 0);
+                    break;
+                }
+            ++rounds;
+        }
+    std::printf("round remaps checked: %ld\n", rounds);
     const long depths[] = {1, 2, 3, 5, 8, 13, 16, 17, 31, 64, 100, 127, 255, 512, 1016, 1024};
     const long tiles[] = {1, 2, 7, 8, 9, 63, 255, 256, 257, 300, 304, 511, 513, 700};
     const long caps[] = {80, 256, 1024};
