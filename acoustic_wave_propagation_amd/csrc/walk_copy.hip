@@ -27,10 +27,12 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int LX, int LY>
+// (store modes are template arguments so that each variant has a kernel
+// name of its own in profiler output)
+template <int LX, int LY, int SHIFT>
 __global__ void __launch_bounds__(LX *LY)
     zmarch_kernel(const float *__restrict__ in, float *__restrict__ out, int n, int R,
-                  int chunk, int nch, int shift) {
+                  int chunk, int nch) {
     constexpr int VY = 2, TX = 4 * LX, TY = LY * VY;
     const int ni = n - 2 * R;
     const int tx = ni / TX, ntile = tx * (ni / TY);
@@ -41,7 +43,7 @@ __global__ void __launch_bounds__(LX *LY)
     const int oy = R + (tile / tx) * TY + VY * ly;
     const int z0 = R + ck * chunk;
     const int64_t pl = (int64_t)n * n;
-    const int sh = shift ? R : 0;
+    const int sh = SHIFT ? R : 0;
     f4 cur[VY], nxt[VY];
 #pragma unroll
     for (int j = 0; j < VY; ++j)
@@ -61,8 +63,9 @@ __global__ void __launch_bounds__(LX *LY)
     }
 }
 
+template <int MODE>
 __global__ void __launch_bounds__(256)
-    rows_kernel(const float *__restrict__ in, float *__restrict__ out, int n, int R, int mode) {
+    rows_kernel(const float *__restrict__ in, float *__restrict__ out, int n, int R) {
     const int ni = n - 2 * R;
     const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
     const int l = threadIdx.x & 127;
@@ -71,9 +74,9 @@ __global__ void __launch_bounds__(256)
     const int64_t base = (z * n + y) * n;
     for (int x = R + 4 * l; x < n - R; x += 512) {
         const f4 v = __builtin_nontemporal_load((const f4 *)(in + base + x));
-        __builtin_nontemporal_store(v, (f4 *)(out + base + x - (mode == 1 ? R : 0)));
+        __builtin_nontemporal_store(v, (f4 *)(out + base + x - (MODE == 1 ? R : 0)));
     }
-    if (mode == 2 && l < R) {
+    if (MODE == 2 && l < R) {
         // the row's halo, rewritten in place with its own values
         volatile float *vo = out;
         vo[base + l] = vo[base + l];
@@ -95,12 +98,19 @@ WC_EXPORT int walk_copy_zmarch(const float *in, float *out, int n, int R, int ti
     if (R != 4 || n % 4 != 0 || chunks < 1 || ni % tw || ni % th || ni % chunks) return -1;
     const int nwg = (ni / tw) * (ni / th) * chunks;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (tw == 512)
-        hipLaunchKernelGGL((zmarch_kernel<128, 4>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
-                           ni / chunks, chunks, shift);
+    const int len = ni / chunks;
+    if (tw == 512 && shift)
+        hipLaunchKernelGGL((zmarch_kernel<128, 4, 1>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
+                           len, chunks);
+    else if (tw == 512)
+        hipLaunchKernelGGL((zmarch_kernel<128, 4, 0>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
+                           len, chunks);
+    else if (shift)
+        hipLaunchKernelGGL((zmarch_kernel<64, 8, 1>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
+                           len, chunks);
     else
-        hipLaunchKernelGGL((zmarch_kernel<64, 8>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
-                           ni / chunks, chunks, shift);
+        hipLaunchKernelGGL((zmarch_kernel<64, 8, 0>), dim3(nwg), dim3(512), 0, s, in, out, n, R,
+                           len, chunks);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
@@ -109,7 +119,13 @@ WC_EXPORT int walk_copy_rows(const float *in, float *out, int n, int R, int mode
     const int ni = n - 2 * R;
     if (R != 4 || n % 4 != 0 || mode < 0 || mode > 2 || ni < 1) return -1;
     const int64_t rows = (int64_t)ni * ni;
-    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), in, out, n, R, mode);
+    const dim3 grid((unsigned)((rows + 1) / 2)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == 0)
+        hipLaunchKernelGGL(rows_kernel<0>, grid, block, 0, s, in, out, n, R);
+    else if (mode == 1)
+        hipLaunchKernelGGL(rows_kernel<1>, grid, block, 0, s, in, out, n, R);
+    else
+        hipLaunchKernelGGL(rows_kernel<2>, grid, block, 0, s, in, out, n, R);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }

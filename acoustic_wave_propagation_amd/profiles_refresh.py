@@ -39,6 +39,25 @@ CMDS = {
     "wave_trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_wave -o wave"
     + BENCH + "--only-wave all --no-cpu --steps 2",
 }
+# request latency and concurrency of the apply beside copies that walk
+# memory the same way (bench.py --ceilings); full kernel names (no -T), so
+# the copies' store variants stay apart
+LAT_TCP = ("TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_WRITE_REQ_LATENCY_sum "
+           "TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum GRBM_GUI_ACTIVE")
+LAT_EA = ("TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_LEVEL_sum "
+          "TCC_EA0_WRREQ_sum GRBM_GUI_ACTIVE")
+CMDS["lat_tcp"] = (PRE + "--pmc " + LAT_TCP + " -d $RAW/pmc_lat_tcp -o lat"
+                   + BENCH + "--ceilings --steps 20 --warmup 2")
+CMDS["lat_ea"] = (PRE + "--pmc " + LAT_EA + " -d $RAW/pmc_lat_ea -o lat"
+                  + BENCH + "--ceilings --steps 20 --warmup 2")
+LAT_KERNELS = [
+    ("R=4 apply (star2p5d_kernel, 256 x 16 tiles)", "%star2p5d_kernel<float, 4, false%"),
+    ("z-march copy, 256 x 16 tiles", "%zmarch_kernel<64, 8, 0>%"),
+    ("z-march copy, 256 x 16 tiles, row-aligned stores", "%zmarch_kernel<64, 8, 1>%"),
+    ("z-march copy, 512 x 8 tiles", "%zmarch_kernel<128, 4, 0>%"),
+    ("one-shot row copy", "%rows_kernel<0>%"),
+    ("one-shot row copy, row-aligned stores", "%rows_kernel<1>%"),
+]
 for _v in ("wave", "pml", "blocked", "pml_blocked"):
     for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         CMDS["%s_%s" % (_v, _n)] = (
@@ -128,6 +147,9 @@ def main(argv=None):
                           "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
         "wave_pml_blocked_r4_1024cube_trace.md":
             lambda: P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"], "blocked"),
+        "apply_and_walk_copies_r4_512cube_latency.md":
+            lambda: P.latency_md([db("pmc_lat_tcp", "lat"), db("pmc_lat_ea", "lat")],
+                                 LAT_KERNELS, [CMDS["lat_tcp"], CMDS["lat_ea"]]),
     }
     for v in ("wave", "pml", "blocked", "pml_blocked"):
         two = v in ("blocked", "pml_blocked")

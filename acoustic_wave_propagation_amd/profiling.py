@@ -38,6 +38,7 @@ SOURCE_SETS = {
     "blocked": _STREAM + ["wave2_kernel.h", "wave2.hip"],  # two-step pass
     "fused": _STREAM + ["sweeps_fused_kernel.h", "sweeps_fused.hip",
                         "pass_plan.h"],                    # fused Jacobi passes
+    "walk": _STREAM + ["walk_copy.hip"],                   # the apply beside its copies
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -203,6 +204,70 @@ def counters_md(dbs, kernel, cmds, sources="stream") -> str:
     out += [""]
     for c in sorted(vals):
         out.append("counter_mean[%s]: %.0f" % (c, vals[c][1]))
+    out += [""] + _stamp(sources)
+    return "\n".join(out)
+
+
+def _dispatch_means(db, like):
+    """{counter: mean over dispatches of the per-dispatch sum over hardware
+    instances} for the kernels whose full name matches `like`."""
+    rows = _db(db).execute(
+        "select counter_name, avg(total) from (select dispatch_id, "
+        "counter_name, sum(counter_value) as total from pmc_events where "
+        "name like ? group by dispatch_id, counter_name) group by counter_name",
+        (like,)).fetchall()
+    return {c: v for c, v in rows}
+
+
+def latency_md(dbs, kernels, cmds, cus=256, xccs=8, sources="walk") -> str:
+    """Request latencies and requests in flight of several kernels from --pmc
+    runs of TCP_TCC_{READ,WRITE}_REQ{,_LATENCY}_sum, TCC_EA0_{RD,WR}REQ{,
+    _LEVEL}_sum and GRBM_GUI_ACTIVE.  kernels: (label, SQL LIKE pattern on
+    the full kernel name).  Latency per request = latency (or level) sum /
+    requests, in cycles; requests in flight = the same sums / elapsed cycles
+    (GRBM_GUI_ACTIVE summed over the XCCs / xccs), by Little's law: per
+    compute unit for the vector L1 -> L2 requests, chip-wide for the L2 ->
+    memory (EA) requests."""
+    out = ["# Memory request latency and concurrency", "", "Runs:", ""]
+    out += ["    " + c for c in cmds]
+    out += ["",
+            "| kernel | cycles | L1->L2 read latency | L1->L2 write latency | "
+            "L1->L2 reads in flight per CU | writes in flight per CU | "
+            "L2->memory read latency | reads in flight (chip) | "
+            "L2->memory write latency | writes in flight (chip) |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    keys = []
+    for label, like in kernels:
+        v = {}
+        for db in dbs:
+            v.update(_dispatch_means(db, like))
+        need = ("GRBM_GUI_ACTIVE", "TCP_TCC_READ_REQ_sum", "TCP_TCC_WRITE_REQ_sum",
+                "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_WRITE_REQ_LATENCY_sum",
+                "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_RDREQ_LEVEL_sum",
+                "TCC_EA0_WRREQ_LEVEL_sum")
+        if not all(k in v and v[k] for k in need):
+            raise RuntimeError("counters of %s missing from the runs" % label)
+        cyc = v["GRBM_GUI_ACTIVE"] / xccs
+        r = dict(
+            cycles=cyc,
+            rd_lat=v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"],
+            wr_lat=v["TCP_TCC_WRITE_REQ_LATENCY_sum"] / v["TCP_TCC_WRITE_REQ_sum"],
+            rd_fl=v["TCP_TCC_READ_REQ_LATENCY_sum"] / cyc / cus,
+            wr_fl=v["TCP_TCC_WRITE_REQ_LATENCY_sum"] / cyc / cus,
+            ea_rd_lat=v["TCC_EA0_RDREQ_LEVEL_sum"] / v["TCC_EA0_RDREQ_sum"],
+            ea_rd_fl=v["TCC_EA0_RDREQ_LEVEL_sum"] / cyc,
+            ea_wr_lat=v["TCC_EA0_WRREQ_LEVEL_sum"] / v["TCC_EA0_WRREQ_sum"],
+            ea_wr_fl=v["TCC_EA0_WRREQ_LEVEL_sum"] / cyc)
+        out.append("| %s | %.0f | %.0f | %.0f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f |" % (
+            label, r["cycles"], r["rd_lat"], r["wr_lat"], r["rd_fl"], r["wr_fl"],
+            r["ea_rd_lat"], r["ea_rd_fl"], r["ea_wr_lat"], r["ea_wr_fl"]))
+        keys.append((label, r))
+    out += ["", "Latencies in cycles per request; cycles: GRBM_GUI_ACTIVE per XCC "
+            "per dispatch.", ""]
+    for label, r in keys:
+        for k in ("rd_lat", "wr_lat", "rd_fl", "wr_fl", "ea_rd_lat", "ea_rd_fl",
+                  "ea_wr_lat", "ea_wr_fl"):
+            out.append("%s[%s]: %.2f" % (k, label, r[k]))
     out += [""] + _stamp(sources)
     return "\n".join(out)
 
