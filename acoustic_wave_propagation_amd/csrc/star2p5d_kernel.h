@@ -134,17 +134,18 @@ constexpr int pair_pitch(int need, int vx) {
 }
 
 // num / d for the damping denominator d = 1 + eta of the wave update (d in
-// [1, 2) for the sponge's eta in [0, 1)).  With RCP (the PML step's
-// kernels, fp32) it multiplies by the hardware reciprocal (v_rcp_f32:
-// within 1 ulp, exact for d = 1) instead of the ten-instruction IEEE
-// division: the PML two-step pass, which does the most arithmetic per point,
-// runs 5% faster with it (4.07 against 4.27 ms per 1032^3 step), while the
-// plain two-step pass runs 2% slower (3.49 against 3.42), so the plain
-// update keeps IEEE division.  A single-step kernel and the two-step pass of
-// the same update use the same form, so they round alike.
-template <typename T, bool RCP>
+// [1, 2) for the sponge's eta in [0, 1)).  In fp32 it multiplies by the
+// hardware reciprocal (v_rcp_f32: within 1 ulp, exact for d = 1, so
+// wherever eta = 0 the result is the IEEE quotient's) instead of the
+// ten-instruction IEEE division; fp64 divides.  Every wave kernel, single
+// step and two-step pass, plain update and PML step, uses this form, so
+// they round alike.  Measured on the 1032^3 run (ms per step, IEEE
+// division against the reciprocal): plain two-step pass 3.05 -> 2.95, PML
+// two-step pass 4.27 -> 4.07 (before its tile order), single steps
+// unchanged (4.00 / 3.99).
+template <typename T>
 __device__ __forceinline__ T damp_div(T num, T d) {
-    if constexpr (RCP && std::is_same<T, float>::value)
+    if constexpr (std::is_same<T, float>::value)
         return num * __builtin_amdgcn_rcpf(d);
     else
         return num / d;
@@ -697,7 +698,7 @@ star2p5d_kernel(StarArgs<T> a) {
                         // the weights carry dt^2/h^2: acc = dt^2 * Lap(u)
                         // (PML step: plus dt^2 times the coupling)
                         const T e = E7 ? ew[EC7][j][i] : et[EC][j][i];
-                        acc = damp_div<T, E7>(
+                        acc = damp_div<T>(
                             T(2) * ctr - (T(1) - e) * up[EC][j][i] + v2[EC][j][i] * acc,
                             T(1) + e);
                     }

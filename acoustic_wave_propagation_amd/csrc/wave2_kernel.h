@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = w0[CS][j][i];
                         const T e = E7 ? ew[EC1][j][i] : et[j][i];
-                        const T u1 = damp_div<T, E7>(
+                        const T u1 = damp_div<T>(
                             T(2) * ctr - (T(1) - e) * up[j][i] + v2[j][i] * acc[j][i], T(1) + e);
                         res[j][i] = (in1 && rin[j] && cin[i]) ? u1 : ctr;
                     }
@@ -648,7 +648,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     for (int i = 0; i < VX; ++i) {
                         const T ctr = ws[WC2][j][i];
                         const T e = E7 ? ec2[j][i] : etb[j][i];
-                        res[j][i] = damp_div<T, E7>(
+                        res[j][i] = damp_div<T>(
                             T(2) * ctr - (T(1) - e) * w0[C2][j][i] + v2b[j][i] * acc[j][i],
                             T(1) + e);
                     }

@@ -184,6 +184,8 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
  * star_d is the stencil of d with d's weights (the Laplacian with unit
  * spacing from stencil3d_desc_init).  vel2 is in m^2/s^2, dt in s, h in m,
  * eta dimensionless; all five arrays share d's extents and element type.
+ * In fp32 the division is a multiplication by the hardware reciprocal of
+ * 1 + eta (within 1 ulp; exact where eta = 0); fp64 divides.
  * u_next may be the same buffer as u_prev (each point reads u_prev only at
  * itself), but must not overlap u, vel2 or eta.  dt, h finite, h > 0.
  * With d->pml_width > 0 (R = 4), eta is read only where it may be non-zero
