@@ -50,6 +50,11 @@ CMDS["lat_tcp"] = (PRE + "--pmc " + LAT_TCP + " -d $RAW/pmc_lat_tcp -o lat"
                    + BENCH + "--ceilings --steps 20 --warmup 2")
 CMDS["lat_ea"] = (PRE + "--pmc " + LAT_EA + " -d $RAW/pmc_lat_ea -o lat"
                   + BENCH + "--ceilings --steps 20 --warmup 2")
+# the same counters on the single wave step (one launch, eta everywhere)
+CMDS["lat_wave_tcp"] = (PRE + "--pmc " + LAT_TCP + " -d $RAW/pmc_lat_wave_tcp -o lat"
+                        + BENCH + "--only-wave wave --no-cpu --steps 1")
+CMDS["lat_wave_ea"] = (PRE + "--pmc " + LAT_EA + " -d $RAW/pmc_lat_wave_ea -o lat"
+                       + BENCH + "--only-wave wave --no-cpu --steps 1")
 LAT_KERNELS = [
     ("R=4 apply (star2p5d_kernel, 256 x 16 tiles)", "%star2p5d_kernel<float, 4, false%"),
     ("z-march copy, 256 x 16 tiles", "%zmarch_kernel<64, 8, 0>%"),
@@ -147,6 +152,11 @@ def main(argv=None):
                           "star2p5d_kernel", [CMDS["sq"], CMDS["tcc"]]),
         "wave_pml_blocked_r4_1024cube_trace.md":
             lambda: P.trace_md(db("prof_wave", "wave"), CMDS["wave_trace"], "blocked"),
+        "wave_r4_1024cube_latency.md":
+            lambda: P.latency_md([db("pmc_lat_wave_tcp", "lat"), db("pmc_lat_wave_ea", "lat")],
+                                 [("R=4 wave step (star2p5d_kernel, 128 x 32 tiles)",
+                                   "%star2p5d_kernel<float, 4, true%")],
+                                 [CMDS["lat_wave_tcp"], CMDS["lat_wave_ea"]], sources="stream"),
         "apply_and_walk_copies_r4_512cube_latency.md":
             lambda: P.latency_md([db("pmc_lat_tcp", "lat"), db("pmc_lat_ea", "lat")],
                                  LAT_KERNELS, [CMDS["lat_tcp"], CMDS["lat_ea"]]),
