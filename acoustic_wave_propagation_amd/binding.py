@@ -21,6 +21,7 @@ HALO_UNTOUCHED, DIRICHLET_COPY = 0, 1
 # every entry point declared in include/stencil3d.h
 EXPORTS = ("stencil3d_abi_version", "stencil3d_strerror", "stencil3d_desc_init",
            "stencil3d_desc_validate", "stencil3d_apply", "stencil3d_jacobi",
+           "stencil3d_jacobi_plan",
            "wave_step", "wave_step_pml", "wave_add_source", "wave_run",
            "wave_run_pml", "wave_run_blocked", "wave_run_pml_blocked",
            "wave_run_blocked_noalloc")
@@ -73,6 +74,8 @@ def lib():
             "stencil3d_desc_validate": (i32, [D]),
             "stencil3d_apply": (i32, [D, vp, vp, vp]),
             "stencil3d_jacobi": (i32, [D, vp, vp, i32, vp]),
+            "stencil3d_jacobi_plan": (i32, [D, i32, ctypes.POINTER(i64),
+                                            ctypes.POINTER(ctypes.c_int), i32]),
             "wave_step": (i32, [D, vp, vp, vp, vp, vp, dp, dp, vp]),
             "wave_step_pml": (i32, [D, vp, vp, vp, vp, vp, dp, dp, vp]),
             "wave_add_source": (i32, [D, vp, i64, i64, i64, dp, vp]),
@@ -180,6 +183,16 @@ def stencil3d_jacobi(d: Desc, buf0, buf1, sweeps: int, stream=None):
                                   _ptr(buf1, d, "buf1"), int(sweeps),
                                   _stream(buf0, stream)), "stencil3d_jacobi")
     return buf0 if sweeps % 2 == 0 else buf1
+
+
+def stencil3d_jacobi_plan(d: Desc, sweeps: int, max_passes: int = 64):
+    """(number of passes, sweeps fused by each of the first max_passes
+    passes) that stencil3d_jacobi makes for d and sweeps."""
+    n = ctypes.c_int64(0)
+    ns = (ctypes.c_int * max(1, int(max_passes)))()
+    _check(lib().stencil3d_jacobi_plan(ctypes.byref(d), int(sweeps), ctypes.byref(n),
+                                       ns, int(max_passes)), "stencil3d_jacobi_plan")
+    return n.value, list(ns[:min(n.value, int(max_passes))])
 
 
 def _step(name, d: Desc, u_prev, u, u_next, vel2, eta, dt, h, stream):

@@ -142,6 +142,22 @@ ST_EXPORT int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1, 
     return ST_OK;
 }
 
+ST_EXPORT int stencil3d_jacobi_plan(const stencil3d_desc *d, int sweeps, int64_t *passes,
+                                   int *ns, int max) {
+    int st = st::check::desc(d);
+    if (st) return st;
+    if (!passes || (max > 0 && !ns)) return ST_ERR_NULL;
+    if (sweeps < 0 || max < 0) return ST_ERR_ARG;
+    // the plan stencil3d_jacobi follows (the boundary mode does not enter it)
+    const st::PassPlan plan =
+        st::plan_passes(sweeps, st::fused_max_sweeps(*d), st::fused_pass_costs(*d));
+    *passes = plan.bulk + plan.ntail;
+    int64_t k = 0;
+    for (; k < plan.bulk && k < max; ++k) ns[k] = plan.bulk_ns;
+    for (int t = 0; t < plan.ntail && k < max; ++t, ++k) ns[k] = plan.tail[t];
+    return ST_OK;
+}
+
 static int step_common(const stencil3d_desc *d, const void *u_prev, const void *u, void *u_next,
                        const void *vel2, const void *eta, double dt, double h, void *stream,
                        bool pml) {

@@ -50,7 +50,6 @@ COUNTERS = {"headline": os.path.join(PROF, "star2p5d_r4_512cube_counters.md"),
             "jacobi": os.path.join(PROF, "jacobi_r1_512cube_counters.md")}
 JACOBI_TRAFFIC = os.path.join(PROF, "jacobi_r1_512cube_traffic.md")
 F64_TRAFFIC = os.path.join(PROF, "apply_r4_f64_ragged_traffic.md")
-OTHERS_TRACE = os.path.join(PROF, "jacobi_r1_512cube_and_f64_ragged_trace.md")
 # VALU issue rate: a wave64 fp32 VALU instruction holds a 16-lane SIMD for 4
 # cycles (packed FP32 is off); MI355X has 256 CUs x 4 SIMDs at 2.4 GHz
 VALU_CYCLES, SIMDS, CLOCK_HZ = 4, 1024, 2.4e9
@@ -94,22 +93,6 @@ def recorded_counter(path: str, counter: str):
     if not t or not _current(text):
         return None
     return float(t.group(1))
-
-
-def recorded_calls(path: str, kernel_prefix: str):
-    """Calls of the kernels whose name starts with kernel_prefix in a
-    committed trace summary (current sources only); else None."""
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    if not _current(text):
-        return None
-    n = 0
-    for line in text.splitlines():
-        cells = [c.strip() for c in line.split("|")]
-        if len(cells) > 3 and cells[1].startswith(kernel_prefix):
-            n += int(cells[2])
-    return n or None
 
 
 def valu_roofline(counters_path: str, kernel_s: float, launches: float = 1.0):
@@ -550,12 +533,9 @@ def bench_others(torch, B, wl, args):
     call = float(durs.mean())
     per = call / w.sweeps
     nbytes = star_bytes(w.interior, w.radius, 4)
-    # the call's own bytes: each fused pass reads and writes the field once
-    # (the sweep's algorithmic bytes); the pass count per call comes from
-    # the committed trace (fused-pass launches per boundary copy)
-    fused = recorded_calls(OTHERS_TRACE, "sweeps_fused_kernel")
-    copies = recorded_calls(OTHERS_TRACE, "shell_copy_kernel")
-    passes = fused / copies if fused and copies else None
+    # the call's own bytes: each pass reads and writes the field once (the
+    # sweep's algorithmic bytes); the passes are the library's own plan
+    passes, plan_ns = B.stencil3d_jacobi_plan(d, w.sweeps)
     call_b = nbytes * passes if passes else None
     res[w.name] = dict(
         value=round(w.interior_points * w.sweeps * runs / wall / 1e9, 2),
@@ -567,11 +547,12 @@ def bench_others(torch, B, wl, args):
                       peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=round(call_b / call / 1e9 / PEAK_HBM_GBS, 4)
                       if call_b else None,
-                      passes_per_call=passes, bytes_per_call=call_b,
+                      passes_per_call=passes, sweeps_per_pass=plan_ns,
+                      bytes_per_call=call_b,
                       achieved_sweep_equivalent=round(nbytes / per / 1e9, 1),
                       frac_sweep_equivalent=round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4),
                       algorithmic_bytes_per_sweep=nbytes,
-                      kernel="sweeps_fused_kernel<float,1,5>",
+                      kernel="sweeps_fused_kernel<float,1,%d>" % max(plan_ns),
                       traffic=recorded_traffic("jacobi_r1_f32", JACOBI_TRAFFIC),
                       valu=valu_roofline(COUNTERS["jacobi"], call / passes)
                       if passes else None,

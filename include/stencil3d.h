@@ -172,6 +172,18 @@ int stencil3d_jacobi(const stencil3d_desc *d, void *buf0, void *buf1,
                      int sweeps, void *stream);
 
 /*
+ * The passes stencil3d_jacobi makes for d and `sweeps`, without running
+ * them (host only: no device call, no allocation): *passes = the number of
+ * passes over memory, each one kernel launch after the boundary copy;
+ * ns[0 .. min(*passes, max) - 1] = the sweeps each pass fuses, in launch
+ * order (ns may be NULL when max is 0).  Errors: those of
+ * stencil3d_desc_validate, ST_ERR_NULL (passes, or ns with max > 0),
+ * ST_ERR_ARG (sweeps or max negative).
+ */
+int stencil3d_jacobi_plan(const stencil3d_desc *d, int sweeps, int64_t *passes,
+                          int *ns, int max);
+
+/*
  * One time step of the acoustic isotropic wave equation with a damping
  * sponge (the acoustic isotropic model with an absorbing eta layer of
  * "Accelerating High-Order Stencils on GPUs", smem_u / smem_eta

@@ -49,6 +49,17 @@ static int cpu_checks(void) {
     EXPECT(wave_run_blocked(&d, (void *)64, (void *)1000000, (void *)2000000, (void *)2000000,
                             (void *)3000000, (void *)4000000, 1e-3, 10.0, 2, 10, 10, 10, NULL,
                             NULL) == ST_ERR_ALIAS);
+    {
+        /* the Jacobi pass plan, a host-only query: R = 1 fp32, 10 sweeps
+           as two passes of five */
+        stencil3d_desc j;
+        int64_t passes = -1;
+        int ns[4] = {0, 0, 0, 0};
+        EXPECT(stencil3d_desc_init(&j, ST_F32, 40, 40, 40, 1, ST_BC_DIRICHLET_COPY) == ST_OK);
+        EXPECT(stencil3d_jacobi_plan(&j, 10, &passes, ns, 4) == ST_OK);
+        EXPECT(passes == 2 && ns[0] == 5 && ns[1] == 5 && ns[2] == 0);
+        EXPECT(stencil3d_jacobi_plan(&j, 10, NULL, NULL, 0) == ST_ERR_NULL);
+    }
     printf("cpu checks ok\n");
     return 0;
 }

@@ -284,3 +284,39 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         mod.lib()
     with pytest.raises(RuntimeError, match="not built"):
         mod.desc_init("f32", (9, 9, 9), 1)
+
+
+def test_jacobi_plan(L):
+    """stencil3d_jacobi_plan reports the passes stencil3d_jacobi makes (host
+    only): every plan covers the sweeps with passes of at most the fused
+    kernel's size, in a count of the sweeps' parity; R = 1 fp32 runs 10
+    sweeps as two passes of five, radii without a fused kernel one sweep per
+    pass."""
+    c = _codes()
+    d32 = B.desc_init("f32", (40, 40, 40), 1)
+    assert B.stencil3d_jacobi_plan(d32, 10) == (2, [5, 5])
+    assert B.stencil3d_jacobi_plan(d32, 0) == (0, [])
+    assert B.stencil3d_jacobi_plan(d32, 1) == (1, [1])
+    for dt, maxns in (("f32", 6), ("f64", 4)):
+        d = B.desc_init(dt, (40, 40, 40), 1)
+        for sweeps in (2, 3, 7, 10, 21, 100, 257, 1000):
+            n, ns = B.stencil3d_jacobi_plan(d, sweeps, max_passes=sweeps)
+            assert n == len(ns) and sum(ns) == sweeps, (dt, sweeps, ns)
+            assert n % 2 == sweeps % 2 and all(1 <= k <= maxns for k in ns)
+    d4 = B.desc_init("f32", (40, 40, 40), 4)
+    assert B.stencil3d_jacobi_plan(d4, 10) == (10, [1] * 10)
+    # the count alone (no list), and the list cut at max
+    n = ctypes.c_int64(-1)
+    assert L.stencil3d_jacobi_plan(ctypes.byref(d32), 10, ctypes.byref(n), None, 0) == 0
+    assert n.value == 2
+    assert B.stencil3d_jacobi_plan(d32, 1000, max_passes=3)[1] == \
+        B.stencil3d_jacobi_plan(d32, 1000, max_passes=1000)[1][:3]
+    # errors
+    assert L.stencil3d_jacobi_plan(ctypes.byref(d32), 10, None, None, 0) == c["ST_ERR_NULL"]
+    assert L.stencil3d_jacobi_plan(ctypes.byref(d32), 10, ctypes.byref(n), None, 4) == \
+        c["ST_ERR_NULL"]
+    assert L.stencil3d_jacobi_plan(ctypes.byref(d32), -1, ctypes.byref(n), None, 0) == \
+        c["ST_ERR_ARG"]
+    bad = _desc(radius=0)
+    assert L.stencil3d_jacobi_plan(ctypes.byref(bad), 10, ctypes.byref(n), None, 0) == \
+        c["ST_ERR_RADIUS"]

@@ -90,15 +90,6 @@ def test_recorded_counters_and_valu_bound(tmp_path):
     c.write_text("counter_mean[SQ_INSTS_VALU]: 1\n"
                  "kernel_source_sha256_16: 0000000000000000\n")
     assert b.valu_roofline(str(c), 1.0) is None
-    t = tmp_path / "t.md"
-    t.write_text("| kernel | calls |\n|---|---|\n"
-                 "| sweeps_fused_kernel<f32> | 40 | 1 | 1 | 1 | 1 |\n"
-                 "| shell_copy_kernel<f32> | 20 | 1 | 1 | 1 | 1 |\n"
-                 "kernel_sources: fused\n"
-                 "kernel_source_sha256_16: %s\n" % kernel_hash("fused"))
-    assert b.recorded_calls(str(t), "sweeps_fused_kernel") == 40
-    assert b.recorded_calls(str(t), "shell_copy_kernel") == 20
-    assert b.recorded_calls(str(t), "nothing") is None
 
 
 def test_kernel_hash_ignores_comments():
