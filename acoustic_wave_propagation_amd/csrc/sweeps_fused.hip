@@ -13,21 +13,33 @@ namespace st {
 namespace {
 
 // R = 1 only: the extended tile grows by NS*R points per side, so larger
-// radii would spend most of the work on the overlap.  Output tiles are
-// 128 x 16 (fp32) and 64 x 16 (fp64) for every NS; the extended tile adds
-// whole 16-byte groups in x and NS rows in y on each side.  4 x 2 (fp32) or
-// 2 x 2 (fp64) points per thread keep the input window and the NS-1
-// intermediate rings within two waves per SIMD.  Up to 5 sweeps two sets of
-// (dense) LDS tiles fit (one barrier per z step); 6 sweeps use one set.
-// Kernel time per pass on a 512^3 interior, fp32 (rocprofv3 trace of
-// Jacobi calls): NS = 3..6: 0.322, 0.389, 0.460, 0.570 ms (one single
-// sweep: 0.211); fp64 NS = 2..4: 0.547, 0.694, 0.865 (one sweep: ~0.49).
+// radii would spend most of the work on the overlap.  The extended tile
+// adds whole 16-byte groups in x and NS rows in y on each side; 4 x 2
+// (fp32) or 2 x 2 (fp64) points per thread.
+//  * fp32, NS = 3..5: 128 x 32 output tiles, one set of (dense) LDS tiles
+//    (two barriers per z step), 646-756 threads at three or four waves per
+//    SIMD (NS = 5: 168 VGPRs, 8 bytes spilled).  The taller tile cuts the
+//    overlap the stages recompute (NS = 5: extended / output area 1.48
+//    against 1.83 at 128 x 16).  Per 512^3 call, ms (two passes and the
+//    boundary copy), 128 x 16 with two LDS sets -> 128 x 32: 10 sweeps
+//    (5 + 5) 0.930 -> 0.750, 8 (4 + 4) 0.794 -> 0.653, 6 (3 + 3) 0.653 ->
+//    0.592; 128 x 48 at NS = 3: 0.629.  Taller NS = 4 and 5 tiles need four
+//    waves per SIMD and spill.
+//  * fp32, NS = 2 and 6: 128 x 16 output tiles (NS = 6 needs 194 VGPRs, two
+//    waves per SIMD: no taller tile fits), two LDS sets at NS = 2, one at 6.
+//  * fp64, NS = 2..4: 64 x 16 output tiles, two LDS sets.
+// Time per pass on a 512^3 grid, fp32 (from 10-sweep calls and others of
+// a known plan, less the 0.018 ms boundary copy): NS = 3, 4, 5, 6: 0.287,
+// 0.317, 0.366, 0.559 ms (one single sweep: 0.224); fp64 NS = 2..4: 0.547,
+// 0.694, 0.865 (one sweep: ~0.49).
 template <typename T, int NS>
 struct FusedShipped;
 template <int NS>
 struct FusedShipped<float, NS> {
     static constexpr int XE = (NS + 3) / 4 * 4;
-    using Cfg = FusedCfg<4, 2, (128 + 2 * XE) / 4, (16 + 2 * NS) / 2, 1, NS <= 5 ? 2 : 1>;
+    static constexpr int TY = NS >= 3 && NS <= 5 ? 32 : 16;  // output tile rows
+    using Cfg = FusedCfg<4, 2, (128 + 2 * XE) / 4, (TY + 2 * NS) / 2, 1,
+                         (TY > 16 || NS > 5) ? 1 : 2>;
 };
 template <int NS>
 struct FusedShipped<double, NS> {
@@ -105,9 +117,10 @@ int fused_max_sweeps(const stencil3d_desc &d) {
 
 const double *fused_pass_costs(const stencil3d_desc &d) {
     // time of a pass of ns sweeps relative to one single sweep (index ns),
-    // measured on 512^3 grids (fp32 ns = 2: an older measurement; no call
-    // plan isolates it, and at 0.71 per sweep it is the dearest fused pass)
-    static const double f32[] = {0.0, 1.0, 1.42, 1.525, 1.842, 2.176, 2.696};
+    // measured on 512^3 grids (fp32 ns = 2: an older measurement, 0.30 ms,
+    // scaled to the current single sweep; no call plan isolates it, and at
+    // 0.67 per sweep it is the dearest fused pass)
+    static const double f32[] = {0.0, 1.0, 1.34, 1.281, 1.416, 1.634, 2.496};
     static const double f64[] = {0.0, 1.0, 1.12, 1.42, 1.77};
     return d.dtype == ST_F64 ? f64 : f32;
 }

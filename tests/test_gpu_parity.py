@@ -403,9 +403,9 @@ def test_jacobi_zero_one_sweeps(oracle_mod, torch_dev):
 def test_jacobi_fused_passes_match_single_sweeps(oracle_mod, torch_dev, dtype):
     """stencil3d_jacobi runs several sweeps per pass over HBM (R = 1); the
     result must equal one stencil3d_apply per sweep bit for bit, for sweep
-    counts that give every pass size and both parities, on a grid with
-    ragged tiles in x, y and z.  The first count is also checked against the
-    oracle."""
+    counts that give every pass size the plans choose (fp32 3..6, fp64 2..4;
+    stencil3d_jacobi_plan) and both parities, on a grid with ragged tiles in
+    x, y and z.  The first count is also checked against the oracle."""
     torch, _ = torch_dev
     shape = (53, 45, 263)  # (nz, ny, nx): 3 tiles in x, ragged in x and y
     dt = "f32" if dtype == np.float32 else "f64"
@@ -417,8 +417,10 @@ def test_jacobi_fused_passes_match_single_sweeps(oracle_mod, torch_dev, dtype):
         nxt = sentinel_like(shape, dtype)
         B.stencil3d_apply(d, chain[-1], nxt)
         chain.append(nxt)
-    for sweeps in (2, 3, 4, 5, 6, 7, 9, 10, 13):
+    used = set()
+    for sweeps in (2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 13):
         log("case jacobi fused %s sweeps=%d" % (dt, sweeps))
+        used |= set(B.stencil3d_jacobi_plan(d, sweeps)[1])
         b0, b1 = upload(u), sentinel_like(shape, dtype)
         res = B.stencil3d_jacobi(d, b0, b1, sweeps)
         assert res is (b0 if sweeps % 2 == 0 else b1)
@@ -430,6 +432,7 @@ def test_jacobi_fused_passes_match_single_sweeps(oracle_mod, torch_dev, dtype):
         if sweeps == 2:
             ref = oracle_mod.jacobi(u, sweeps, 1, c)
             check_close(got, ref, 2 * _tol(dtype), "jacobi fused 2 sweeps")
+    assert used >= ({3, 4, 5, 6} if dtype == np.float32 else {2, 3, 4}), used
 
 
 @pytest.mark.parametrize("nsteps", [0, 1, 3])
@@ -762,11 +765,11 @@ def test_graph_capture_replays(torch_dev):
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_jacobi_fused_mixed_chunking(torch_dev, dtype):
     """A grid with more fused-pass tiles than one round of workgroups (300
-    fp32 / 600 fp64 tiles on 256 compute units): whole columns for the full
-    rounds, chunks for the rest.  Ten sweeps (passes 5 + 5, or 4 + 4 + 2 in
-    fp64) are bit-identical to ten single applies."""
+    fp32 / 1200 fp64 tiles on 256 compute units): whole columns for the full
+    rounds, chunks for the rest.  Ten sweeps (passes 5 + 5 in fp32, 3 + 3 +
+    2 + 2 in fp64) are bit-identical to ten single applies."""
     torch, _ = torch_dev
-    shape = (102, 962, 642)
+    shape = (102, 962, 1282)
     name = "f32" if dtype == np.float32 else "f64"
     log("case jacobi mixed chunking %s %s" % (name, shape))
     u = wl.uniform_planes(shape, 97, -1, 1, dtype=dtype)
