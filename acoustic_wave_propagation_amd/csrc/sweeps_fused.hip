@@ -27,11 +27,17 @@ namespace {
 //    waves per SIMD and spill.
 //  * fp32, NS = 2 and 6: 128 x 16 output tiles (NS = 6 needs 194 VGPRs, two
 //    waves per SIMD: no taller tile fits), two LDS sets at NS = 2, one at 6.
-//  * fp64, NS = 2..4: 64 x 16 output tiles, two LDS sets.
-// Time per pass on a 512^3 grid, fp32 (from 10-sweep calls and others of
-// a known plan, less the 0.018 ms boundary copy): NS = 3, 4, 5, 6: 0.287,
-// 0.317, 0.366, 0.559 ms (one single sweep: 0.224); fp64 NS = 2..4: 0.547,
-// 0.694, 0.865 (one sweep: ~0.49).
+//  * fp64, NS = 2..4: 64 x 32 output tiles, one LDS set, 612-720 threads
+//    (NS = 4: 148 VGPRs, three waves per SIMD).  Per 512^3 call against 64
+//    x 16 tiles with two LDS sets, ms: 10 sweeps (3 + 3 + 2 + 2) 2.34 ->
+//    1.93, 8 (4 + 4) 1.62 -> 1.22, 6 (3 + 3) 1.33 -> 1.04, 4 (2 + 2) 1.04
+//    -> 0.92.
+// Time per pass on a 512^3 grid (from calls of a known plan, less the
+// boundary copy, 0.018 ms fp32 and 0.024 ms fp64): fp32 NS = 3, 4, 5, 6:
+// 0.287, 0.317, 0.366, 0.559 ms (one single sweep: 0.224); fp64 NS = 2, 3,
+// 4: 0.450, 0.506, 0.599 (one single sweep: 0.502).  The fp64 two-sweep
+// pass varies from box to box (0.45-0.57 ms on three boxes; the others
+// within 1%); the table takes the first box's figures.
 template <typename T, int NS>
 struct FusedShipped;
 template <int NS>
@@ -44,7 +50,7 @@ struct FusedShipped<float, NS> {
 template <int NS>
 struct FusedShipped<double, NS> {
     static constexpr int XE = (NS + 1) / 2 * 2;
-    using Cfg = FusedCfg<2, 2, (64 + 2 * XE) / 2, (16 + 2 * NS) / 2>;
+    using Cfg = FusedCfg<2, 2, (64 + 2 * XE) / 2, (32 + 2 * NS) / 2, 1, 1>;
 };
 
 struct FusedPlan {
@@ -121,7 +127,7 @@ const double *fused_pass_costs(const stencil3d_desc &d) {
     // scaled to the current single sweep; no call plan isolates it, and at
     // 0.67 per sweep it is the dearest fused pass)
     static const double f32[] = {0.0, 1.0, 1.34, 1.281, 1.416, 1.634, 2.496};
-    static const double f64[] = {0.0, 1.0, 1.12, 1.42, 1.77};
+    static const double f64[] = {0.0, 1.0, 0.896, 1.006, 1.192};
     return d.dtype == ST_F64 ? f64 : f32;
 }
 

@@ -765,7 +765,7 @@ def test_graph_capture_replays(torch_dev):
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_jacobi_fused_mixed_chunking(torch_dev, dtype):
     """A grid with more fused-pass tiles than one round of workgroups (300
-    fp32 / 1200 fp64 tiles on 256 compute units): whole columns for the full
+    fp32 / 600 fp64 tiles on 256 compute units): whole columns for the full
     rounds, chunks for the rest.  Ten sweeps (passes 5 + 5 in fp32, 3 + 3 +
     2 + 2 in fp64) are bit-identical to ten single applies."""
     torch, _ = torch_dev
