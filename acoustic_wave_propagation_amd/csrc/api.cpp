@@ -48,10 +48,12 @@ int current_cus(int *status) {
 // kernel for the inner region, another for the PML region, where only the
 // latter reads eta).  The rows within p of a y face go to two launches of
 // their own (slabs that read eta everywhere); the launch over the other
-// rows reads eta on the columns within p of an x face or of an x edge of
-// the lane's tile, and elsewhere only in the planes within p of a z face
-// (the PML step's eta ring by the same rule, point by point).  Every tile
-// of that launch has the same load pattern, so its tiles stream in step.
+// rows reads eta on the columns within p of an x face or of a multiple of
+// two tile widths (p columns of every tile: the left ones of even tiles,
+// the right ones of odd tiles), and elsewhere only in the planes within p
+// of a z face (the PML step's eta ring by the same rule, point by point).
+// Every tile of that launch moves the same bytes per plane, so its tiles
+// stream in step.
 // Every point is written by exactly one launch with the same arithmetic
 // (eta = 0 where it is not read), so the result is bit-identical to one
 // launch over the interior.

@@ -46,13 +46,14 @@ using F64Wave = TileCfg<2, 2, 32, 16, 1, 0, true, 2, false, true, true, false, f
 
 // Tiles of the wave step's data regions (Kind::WaveRegions, with a sponge
 // width): 4 x 2 (fp32) or 2 x 2 (fp64) per thread, 64 x 8 threads -> 256 x
-// 16 or 128 x 16 tiles.  Every tile reads eta on the columns within the
-// sponge width of its x edges (a quarter of a 256-wide tile for a 32-point
-// sponge, half of a 128-wide one): 1032^3 step with pml_width 32, 3.70
-// against 3.92 ms with the 128 x 32 tiles, which are the faster ones when
-// eta is read everywhere (4.00 against 4.11 ms).  The PML step's data
-// regions (Kind::WavePmlRegions) keep its primary tiles: on 256 x 16 its
-// eta masks and rings spill registers.
+// 16 or 128 x 16 tiles.  Every tile reads eta on as many columns as the
+// sponge width (an eighth of a 256-wide tile for a 32-point sponge, a
+// quarter of a 128-wide one): 1032^3 step with pml_width 32, 3.53 ms (3.70
+// when each tile read the sponge width at both of its x edges, 3.92 with
+// the 128 x 32 tiles, which are the faster ones when eta is read
+// everywhere: 4.00 against 4.11 ms).  The PML step's data regions
+// (Kind::WavePmlRegions) keep its primary tiles: on 256 x 16 its eta masks
+// and rings spill registers.
 using F32WaveRegions =
     TileCfg<4, 2, 64, 8, 1, 0, true, 2, false, true, true, false, false, 1, false, true>;
 using F64WaveRegions =

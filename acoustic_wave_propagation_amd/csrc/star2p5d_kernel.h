@@ -388,21 +388,24 @@ star2p5d_kernel(StarArgs<T> a) {
     // eta with data regions (a.pw > 0; eta is zero at every point at least
     // pw from all interior faces): a lane reads eta in every plane on its
     // rows within pw of an interior face in y, and on all its rows if its
-    // columns lie within pw of an interior face in x or of an x edge of its
-    // tile; its other loads read eta only in the planes within pw of a z
-    // face.  Elsewhere the load takes the out-of-range offset: no memory
-    // traffic, and it returns that zero.  The tile-edge columns give every
-    // tile of a row the same load pattern, which keeps the tiles streaming
-    // in step (their halo rows come from each other's loads in L2); tiles
-    // that read eta on different columns drift apart and lose that reuse.
-    // The PML step's eta ring follows the same rule point by point (its
-    // units left and right of the tile always lie in the tile-edge band).
+    // columns lie within pw of an interior face in x or in the band of
+    // columns within pw of a multiple of two tile widths (interior x); its
+    // other loads read eta only in the planes within pw of a z face.
+    // Elsewhere the load takes the out-of-range offset: no memory traffic,
+    // and it returns that zero.  The band gives every tile the same number
+    // of eta columns (even tiles their left pw columns, odd tiles their
+    // right pw, which include the x sponges where the row of tiles is
+    // whole), so the tiles move the same bytes per plane and stream in step
+    // (their halo rows come from each other's loads in L2); tiles that read
+    // eta on more columns than others drift apart and lose that reuse.  The
+    // PML step's eta ring follows the same rule point by point, and its
+    // units left and right of the tile are always read.
     // Bit j of emask: row j reads eta in every plane; bit VY + q: the eta
     // ring unit q does (set for every point without SP).
     const int elo = R + a.pw;  // first x (y, z) at least pw inside the interior
     auto eta_cols = [&](int x) {  // a group at x lies in the x band
-        return !SP || x < elo || x + VX > nx - elo || x - gx0 < a.pw ||
-               gx0 + TX - (x + VX) < a.pw;
+        const int m = (x - R) % (2 * TX);  // interior x modulo two tiles (x >= R)
+        return !SP || x < elo || x + VX > nx - elo || m < a.pw || m + VX > 2 * TX - a.pw;
     };
     auto eta_row = [&](int y) { return y < elo || y >= ny - elo; };
     auto eta_plane = [&](int k, int j) {

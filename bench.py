@@ -472,13 +472,13 @@ def eta_read_points(interior, pw, tile_x=256, group=4):
     sponge width pw): every point of the rows within pw of a y face (their
     own launches); in the other rows every point of the planes within pw of
     a z face, and elsewhere the 4-column groups within pw of an x face or of
-    an x edge of their tile_x-wide tile (256 for the wave step, 128 for the
-    PML step)."""
+    a multiple of two tile widths (tile_x: 256 for the wave step, 128 for
+    the PML step; each tile reads pw of its columns)."""
     iz, iy, ix = interior
     ox = np.arange(0, ix, group)              # group starts, interior coords
-    gx0 = ox // tile_x * tile_x               # tile origins
-    cols = ((ox < pw) | (ox + group > ix - pw) | (ox - gx0 < pw) |
-            (gx0 + tile_x - (ox + group) < pw))
+    m = ox % (2 * tile_x)                     # position in the two-tile band period
+    cols = ((ox < pw) | (ox + group > ix - pw) | (m < pw) |
+            (m + group > 2 * tile_x - pw))
     ncols = int(np.minimum(group, ix - ox)[cols].sum())
     slabs = 2 * pw * ix * iz
     rows = iy - 2 * pw

@@ -86,12 +86,13 @@ extern "C" {
  * at least pml_width.  For R = 4 the wave and PML entry points then read
  * eta only near the faces: the rows within pml_width of a y face as two
  * launches of their own; in the other rows on the columns near the x
- * faces, in the planes near the z faces, and on the same columns of every
+ * faces, in the planes near the z faces, and on as many columns of every
  * tile (which keeps the tiles streaming in step).  The results are
  * bit-identical to pml_width = 0 under that guarantee, and wrong where it
  * does not hold.
- * On MI355X a 1024^3 wave step with a 32-point sponge takes 3.70 ms with
- * pml_width = 32 and 4.0 ms with 0 (eta read everywhere in one launch).
+ * On MI355X a 1024^3 wave step with a 32-point sponge takes 3.53 ms with
+ * pml_width = 32 and 4.0 ms with 0 (eta read everywhere in one launch);
+ * the PML step 3.73 and 3.98 ms.
  * Ignored by the plain stencil.  168 bytes, naturally aligned.
  */
 typedef struct stencil3d_desc {

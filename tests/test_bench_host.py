@@ -150,13 +150,19 @@ def test_walk_copy_library_exports():
 
 def test_eta_read_points_model():
     """The data-region byte model: pw = 32 on a 1024^3 interior reads eta on
-    the two 32-row y slabs, the 64 z-sponge planes of the other rows, and a
-    quarter of their columns elsewhere (the 32 columns at each edge of each
-    256-wide tile, which include the x sponge)."""
+    the two 32-row y slabs, the 64 z-sponge planes of the other rows, and
+    elsewhere 32 columns of each tile (the left 32 of even tiles, the right
+    32 of odd ones, which include the x sponges): an eighth of the columns
+    on 256-wide tiles, a quarter on the PML step's 128-wide ones."""
     b = _bench()
     n, pw = 1024, 32
-    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 4))
+    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 8))
     assert b.eta_read_points((n, n, n), pw) == want
-    # the PML step's 128-wide tiles: the 32 columns at each edge are half
-    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 2))
+    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 4))
     assert b.eta_read_points((n, n, n), pw, tile_x=128) == want
+    # a ragged row of 1000 columns: bands [0, 32) and [480, 544), and the x
+    # face rule reads [968, 1000), where the last tile's band would lie past
+    # the row: 128 columns
+    iz, iy, ix = 100, 100, 1000
+    want = 2 * pw * ix * iz + (iy - 2 * pw) * (2 * pw * ix + (iz - 2 * pw) * 128)
+    assert b.eta_read_points((iz, iy, ix), pw) == want
