@@ -136,6 +136,51 @@ def test_traffic_scaling(tmp_path):
                      "", "")
 
 
+def test_latency_summary(tmp_path):
+    """Request latency = latency (or level) sum / requests; in flight = the
+    same sum / elapsed cycles (GRBM_GUI_ACTIVE summed over the XCCs, divided
+    by their number), per CU for L1 -> L2.  Counters of one dispatch are
+    summed over hardware instances, then averaged over dispatches."""
+    from acoustic_wave_propagation_amd import profiling as P
+    db = str(tmp_path / "lat.db")
+    con = sqlite3.connect(db)
+    con.execute("create table pmc_events (dispatch_id integer, name text, "
+                "counter_name text, counter_value real)")
+    k = "void st::star2p5d_kernel<float, 4, false, X>(st::StarArgs<float>)"
+    rows = []
+    for disp, scale in ((0, 1.0), (1, 3.0)):   # dispatch means: 2x dispatch 0
+        rows += [(disp, k, "GRBM_GUI_ACTIVE", 500.0 * scale),   # two XCCs
+                 (disp, k, "GRBM_GUI_ACTIVE", 500.0 * scale),
+                 (disp, k, "TCP_TCC_READ_REQ_sum", 100.0 * scale),
+                 (disp, k, "TCP_TCC_READ_REQ_LATENCY_sum", 40000.0 * scale),
+                 (disp, k, "TCP_TCC_READ_REQ_LATENCY_sum", 10000.0 * scale),
+                 (disp, k, "TCP_TCC_WRITE_REQ_sum", 50.0 * scale),
+                 (disp, k, "TCP_TCC_WRITE_REQ_LATENCY_sum", 20000.0 * scale),
+                 (disp, k, "TCC_EA0_RDREQ_sum", 80.0 * scale),
+                 (disp, k, "TCC_EA0_RDREQ_LEVEL_sum", 160000.0 * scale),
+                 (disp, k, "TCC_EA0_WRREQ_sum", 40.0 * scale),
+                 (disp, k, "TCC_EA0_WRREQ_LEVEL_sum", 20000.0 * scale)]
+    rows.append((2, "other_kernel", "GRBM_GUI_ACTIVE", 1e9))
+    con.executemany("insert into pmc_events values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    text = P.latency_md([db], [("apply", "%star2p5d_kernel<float, 4, false%")],
+                        ["cmd"], cus=2, xccs=2)
+    v = dict(l.split(": ", 1) for l in text.splitlines() if "[apply]: " in l)
+    # dispatch means: cycles 2000 / 2 XCCs = 1000; reads 200 with latency
+    # sum 100000 -> 500 cycles each, 100000 / 1000 / 2 CUs = 50 in flight
+    assert float(v["rd_lat[apply]"]) == 500.0
+    assert float(v["rd_fl[apply]"]) == 50.0
+    assert float(v["wr_lat[apply]"]) == 400.0
+    assert float(v["wr_fl[apply]"]) == 20.0
+    assert float(v["ea_rd_lat[apply]"]) == 2000.0
+    assert float(v["ea_rd_fl[apply]"]) == 320.0
+    assert float(v["ea_wr_lat[apply]"]) == 500.0
+    assert float(v["ea_wr_fl[apply]"]) == 40.0
+    with pytest.raises(RuntimeError):
+        P.latency_md([db], [("none", "%nothing%")], ["cmd"])
+
+
 def test_walk_copy_library_exports():
     """The measurement copies (bench.py --ceilings) are built beside the
     stencil library and export their two entry points."""
