@@ -763,6 +763,34 @@ def test_graph_capture_replays(torch_dev):
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_jacobi_fused_degenerate_grids(torch_dev, dtype):
+    """Fused passes on grids far smaller than their tiles: one interior
+    point, one interior row or column, one interior plane, thin slabs.  The
+    boundary stays fixed and the result equals single applies bit for bit,
+    for sweep counts that run passes of every size the plans choose."""
+    torch, _ = torch_dev
+    dt = "f32" if dtype == np.float32 else "f64"
+    shapes = [(3, 3, 3), (3, 5, 40), (40, 3, 6), (5, 40, 3), (4, 5, 6), (20, 3, 300),
+              (9, 70, 9), (3, 200, 150)]
+    for k, shape in enumerate(shapes):
+        u = wl.uniform_planes(shape, 600 + k, -1, 1, dtype=dtype)
+        d = B.desc_init(dt, shape, 1, B.DIRICHLET_COPY)
+        chain = [upload(u)]
+        for _ in range(12):
+            nxt = sentinel_like(shape, dtype)
+            B.stencil3d_apply(d, chain[-1], nxt)
+            chain.append(nxt)
+        for sweeps in (3, 4, 5, 7, 8, 10, 12):
+            log("case jacobi degenerate %s %s sweeps=%d" % (dt, shape, sweeps))
+            b0, b1 = upload(u), sentinel_like(shape, dtype)
+            res = B.stencil3d_jacobi(d, b0, b1, sweeps)
+            got, want = res.cpu().numpy(), chain[sweeps].cpu().numpy()
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), \
+                "%s %s sweeps=%d: %d points differ" % (dt, shape, sweeps,
+                                                      int((got != want).sum()))
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_jacobi_fused_mixed_chunking(torch_dev, dtype):
     """A grid with more fused-pass tiles than one round of workgroups (300
     fp32 / 600 fp64 tiles on 256 compute units): whole columns for the full
