@@ -178,13 +178,15 @@ __device__ __forceinline__ void zsteps(int n, F &&step) {
 
 // ---- buffer addressing -----------------------------------------------------
 // Every plane is addressed through a buffer resource (V#) whose base is the
-// plane start (uniform, scalar registers) and whose num_records ends at the
-// allocation end (capped below 2^31).  Lanes carry 32-bit byte offsets that
-// stay fixed over the whole z sweep, so a load or store costs no vector
-// address arithmetic.  The hardware range check makes any access at or past
-// num_records return zeros (loads) or do nothing (stores): lanes whose data
-// is not needed use the offset kOOB, and loads that run past the end of the
-// last row of the array read zeros instead of faulting.
+// plane start (uniform, scalar registers) and whose num_records ends 16
+// bytes past the plane (a 16-byte group on the plane's last row may
+// straddle its end), or at the plane's end on the array's last plane.
+// Lanes carry 32-bit byte offsets that stay fixed over the whole z sweep,
+// so a load or store costs no vector address arithmetic.  The hardware
+// range check makes any access at or past num_records return zeros (loads)
+// or do nothing (stores): lanes whose data is not needed use the offset
+// kOOB, and loads past the plane (rows of a ragged tile beyond the array)
+// read zeros that only points outside the interior use.
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -193,13 +195,20 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 family: 32-bit raw data
 constexpr uint32_t kOOB = 0x80000000u;        // >= every num_records we build
 constexpr int kAuxNT = 2;                     // cache policy: nontemporal
 
-// A plane that is not needed gets num_records = 0: its accesses are still
-// issued (so the instruction stream, and the wait counts the compiler
-// derives from it, do not depend on the chunk length) but touch no memory.
-__device__ __forceinline__ rsrc_t plane_rsrc(const void *base, int64_t bytes_left, bool needed) {
-    int64_t n = bytes_left < 0x7fffffff ? bytes_left : 0x7fffffff;
-    n = (needed && n > 0) ? n : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)n, kRsrcWord3);
+// Plane z of an array of nz planes of pzb bytes each (pzb < 2^31, which
+// validation guarantees; z in [0, nz) wherever needed is true).  A plane
+// that is not needed gets num_records = 0: its accesses are still issued
+// (so the instruction stream, and the wait counts the compiler derives from
+// it, do not depend on the chunk length) but touch no memory.  32-bit
+// arithmetic apart from the base address, so the resources of every
+// unrolled step stay cheap in scalar registers.
+__device__ __forceinline__ rsrc_t plane_rsrc(const void *base, int z, int nz, uint32_t pzb,
+                                             bool needed) {
+    const uint32_t mid = pzb + 16u < 0x7fffffffu ? pzb + 16u : 0x7fffffffu;
+    const uint32_t n = !needed ? 0u : (z < nz - 1 ? mid : pzb);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(base)) + (uint64_t)(uint32_t)z * pzb, 0,
+        (int)n, kRsrcWord3);
 }
 
 // N consecutive elements at byte offset off (any element-aligned offset).
@@ -368,8 +377,7 @@ star2p5d_kernel(StarArgs<T> a) {
     // sums are symmetric in +-k, so the result does not depend on direction.
     const int dir = (C::ALT && (chunk & 1)) ? -1 : 1;
     const int z0 = dir > 0 ? zs : ze - 1;       // plane of step 0
-    const int64_t pzb = a.pz * (int64_t)ES;     // plane bytes
-    const int64_t totb = pzb * a.nz;            // allocation bytes
+    const uint32_t pzb = (uint32_t)(a.pz * (int64_t)ES);  // plane bytes (< 2^31)
     // some columns of this tile lie outside the box (ragged x edge)
     const bool xpart = gx0 + TX > a.bx1;
 
@@ -487,7 +495,7 @@ star2p5d_kernel(StarArgs<T> a) {
     // resource of the plane at step offset j from step k (empty if unneeded)
     auto rsrc_at = [&](const T *base, int k, int j, bool needed) {
         const int z = z0 + dir * (k + j);
-        return plane_rsrc((const char *)base + (int64_t)z * pzb, totb - (int64_t)z * pzb, needed);
+        return plane_rsrc(base, z, a.nz, pzb, needed);
     };
     // window slot s holds the plane at step offset s - R of the block start
     auto load_window = [&](int k, int j, bool needed, auto slot_c) {

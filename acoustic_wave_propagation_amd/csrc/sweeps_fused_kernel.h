@@ -108,8 +108,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
     const int n = ze - zs;                    // output planes of this chunk
     const int nsteps = n + FILL;
     const int q0 = zs - (NS - 1) * R;         // plane of stage 1 at step 0
-    const int64_t pzb = a.pz * (int64_t)ES;
-    const int64_t totb = pzb * nz;
+    const uint32_t pzb = (uint32_t)(a.pz * (int64_t)ES);  // plane bytes (< 2^31)
     const bool xpart = gx0 + TX > nx - R;     // ragged x edge inside this tile
 
     // ---- this thread's points: columns ex..ex+VX-1 on rows ey..ey+VY-1 -----
@@ -161,7 +160,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
     // input plane q; only planes this chunk's outputs depend on are read
     auto in_rsrc = [&](int q) {
         const bool need = q >= 0 && q < nz && q >= zs - NS * R && q < ze + NS * R;
-        return plane_rsrc((const char *)a.in + (int64_t)q * pzb, totb - (int64_t)q * pzb, need);
+        return plane_rsrc(a.in, q, nz, pzb, need);
     };
     // prologue: window slot i holds the plane at step offset i - R
     static_for<0, 2 * R + D>([&](auto sc) {
@@ -297,8 +296,7 @@ __global__ void __launch_bounds__(C::NT) sweeps_fused_kernel(StarArgs<T> a) {
                 } else {
                     // 4. last sweep: store T's interior points of plane q
                     const bool st = k >= FILL && k < nsteps;
-                    const rsrc_t ro = plane_rsrc((const char *)a.out + (int64_t)q * pzb,
-                                                 totb - (int64_t)q * pzb, st);
+                    const rsrc_t ro = plane_rsrc(a.out, q, nz, pzb, st);
                     if (!xpart) {
 #pragma unroll
                         for (int j = 0; j < VY; ++j) bstore<T, VX, SAUX>(ro, soff[j], res[j]);

@@ -178,8 +178,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     const int n = ze - zs;                    // output planes of this chunk
     const int nsteps = n + S::FILL;
     const int q0 = zs - R;                    // stage-1 plane of step 0
-    const int64_t pzb = a.pz * (int64_t)ES;
-    const int64_t totb = pzb * nz;
+    const uint32_t pzb = (uint32_t)(a.pz * (int64_t)ES);  // plane bytes (< 2^31)
     const bool xpart = gx0 + TX > nx - R;     // ragged x edge inside this tile
 
     // ---- this thread's points: columns ex..ex+VX-1 on rows ey..ey+VY-1 -----
@@ -298,8 +297,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
             for (int i = 0; i < VX; ++i) ew[p][j][i] = T(0);
 
     auto prsrc = [&](const T *base, int q, bool need) {
-        need = need && q >= 0 && q < nz;
-        return plane_rsrc((const char *)base + (int64_t)q * pzb, totb - (int64_t)q * pzb, need);
+        return plane_rsrc(base, q, nz, pzb, need && q >= 0 && q < nz);
     };
     // u^n planes this chunk depends on
     auto u_need = [&](int q) { return q >= zs - 2 * R && q < ze + 2 * R; };
