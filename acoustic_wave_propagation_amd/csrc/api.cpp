@@ -236,6 +236,21 @@ ST_EXPORT int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u, const
                       stream, true);
 }
 
+// Two steps in one pass (launch_wave2).  With a sponge width p (plain step,
+// R = 4) the pass reads eta only where it may be nonzero, in one launch:
+// split into launch_wave's three row launches it measured slower (1032^3,
+// ms per step: one launch reading eta everywhere 2.930, three launches
+// 2.906, one launch 2.866), since the pass is bound by on-chip work more
+// than by its bytes and the two y-slab launches fill the chip poorly.
+static int launch_pass(const stencil3d_desc &d, const void *u_prev, const void *u, void *o1,
+                       void *o2, const void *vel2, const void *eta, double wscale,
+                       const st::Wave2Source &src, int cus, hipStream_t s, bool pml) {
+    // (extents are below 2^31: clamping keeps the width in an int)
+    const int64_t p = d.pml_width < ((int64_t)1 << 30) ? d.pml_width : (int64_t)1 << 30;
+    const int pw = (pml || d.radius != 4) ? 0 : (int)p;
+    return st::launch_wave2(d, pw, u_prev, u, o1, o2, vel2, eta, wscale, src, cus, s, pml);
+}
+
 // Time-blocked leapfrog over four buffers: u^k lives in b[k mod 4], so two
 // steps at a time read (u^{k-1}, u^k) and write (u^{k+1}, u^{k+2}) into
 // the other two buffers, which no tile of the pass reads.  A pass reads
@@ -260,7 +275,7 @@ static int blocked_loop(const stencil3d_desc &d, void *u_prev, void *u, void *wo
             const st::Wave2Source src{src_trace != nullptr, src_x, src_y, src_z,
                                       src_trace ? src_trace[n] : 0.0,
                                       src_trace ? src_trace[n + 1] : 0.0};
-            st = st::launch_wave2(d, p, c, o1, o2, vel2, eta, wscale, src, cus, s, pml);
+            st = launch_pass(d, p, c, o1, o2, vel2, eta, wscale, src, cus, s, pml);
             n += 2;
         } else {
             st = launch_wave(d, c, o1, p, vel2, eta, wscale, cus, s, pml);

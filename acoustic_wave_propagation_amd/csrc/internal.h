@@ -92,12 +92,14 @@ bool wave2_available(const stencil3d_desc &d);
 
 // Two leapfrog steps in one pass: out1 = u^{n+1} and out2 = u^{n+2} on the
 // interior from u_prev = u^{n-1} and u = u^n (weights scaled by wscale =
-// dt^2/h^2, eta read on the whole interior; pml: the PML step's update, with
-// the eta-gradient coupling).  Non-interior points of the outputs are not
-// written; u^{n+1}'s non-interior values are taken as u's.  out1 and out2
-// must not overlap each other or any input.  Returns ST_OK, ST_ERR_ARG (no
-// such pass for d) or ST_ERR_LAUNCH.
-int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
+// dt^2/h^2; pml: the PML step's update, with the eta-gradient coupling).
+// pw > 0 (plain step, R = 4) states that eta is 0 at every interior point
+// at least pw from all interior faces, and eta is read only where it may
+// not be; otherwise eta is read on the whole interior.  Non-interior points
+// of the outputs are not written; u^{n+1}'s non-interior values are taken
+// as u's.  out1 and out2 must not overlap each other or any input.  Returns
+// ST_OK, ST_ERR_ARG (no such pass for d) or ST_ERR_LAUNCH.
+int launch_wave2(const stencil3d_desc &d, int pw, const void *u_prev, const void *u, void *out1,
                  void *out2, const void *vel2, const void *eta, double wscale,
                  const Wave2Source &src, int cus, hipStream_t stream, bool pml);
 

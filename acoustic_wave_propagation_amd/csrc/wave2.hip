@@ -31,10 +31,10 @@ using Wave2F64 = Wave2Cfg<2, 1, 16, 40, 3, true, true, 2, true>;
 using Wave2F32Pml = Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true>;
 using Wave2F64Pml = Wave2Cfg<2, 1, 16, 32, 2, true, true, 2, true>;
 
-template <typename T, int R, class C, bool E7>
-int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
-             const void *vel2, const void *eta, double wscale, const Wave2Source &src, int cus,
-             hipStream_t s) {
+template <typename T, int R, class C, bool E7, bool SP>
+int launch_t(const stencil3d_desc &d, int pw, const void *u_prev, const void *u, void *out1,
+             void *out2, const void *vel2, const void *eta, double wscale,
+             const Wave2Source &src, int cus, hipStream_t s) {
     using S = Wave2Shape<R, C, E7>;
     const int64_t ix = d.nx - 2 * R, iy = d.ny - 2 * R, iz = d.nz - 2 * R;
     const int tiles_x = (int)((ix + S::TX - 1) / S::TX);
@@ -46,6 +46,7 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
     Wave2Args<T> g;
     g.s = make_args<T, R>(d, interior_box(d), u, out1, u_prev, vel2, eta, wscale, tiles_x, tiles_y,
                           (int)p.chunk_len, (int)p.nwg);
+    g.s.pw = SP ? pw : 0;
     g.s.ga_nwg = (int)p.a_nwg;
     g.s.ga_tiles = (int)p.a_tiles;
     g.s.ga_len = (int)p.a_len;
@@ -64,38 +65,52 @@ int launch_t(const stencil3d_desc &d, const void *u_prev, const void *u, void *o
     // strips), 1032^3 run, ms per step: plain pass 3.39 -> 3.08, PML pass
     // 3.97-4.14 -> 3.94.
     g.round = cus > 0 ? cus : 256;
-    hipLaunchKernelGGL((wave2_kernel<T, R, C, E7>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s, g);
+    hipLaunchKernelGGL((wave2_kernel<T, R, C, E7, SP>), dim3((unsigned)p.nwg), dim3(C::NT), 0, s,
+                       g);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_ERR_LAUNCH;
 }
 
+// Data regions (pw > 0) for the plain step at R = 4 only, as for the
+// single step.
 template <typename T, class C, bool E7>
-int launch_r(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1, void *out2,
-             const void *vel2, const void *eta, double wscale, const Wave2Source &src, int cus,
-             hipStream_t s) {
+int launch_r(const stencil3d_desc &d, int pw, const void *u_prev, const void *u, void *out1,
+             void *out2, const void *vel2, const void *eta, double wscale,
+             const Wave2Source &src, int cus, hipStream_t s) {
     switch (d.radius) {
-    case 1: return launch_t<T, 1, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
-    case 2: return launch_t<T, 2, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
-    case 3: return launch_t<T, 3, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
+    case 1:
+        return launch_t<T, 1, C, E7, false>(d, 0, u_prev, u, out1, out2, vel2, eta, wscale, src,
+                                            cus, s);
+    case 2:
+        return launch_t<T, 2, C, E7, false>(d, 0, u_prev, u, out1, out2, vel2, eta, wscale, src,
+                                            cus, s);
+    case 3:
+        return launch_t<T, 3, C, E7, false>(d, 0, u_prev, u, out1, out2, vel2, eta, wscale, src,
+                                            cus, s);
     }
-    return launch_t<T, 4, C, E7>(d, u_prev, u, out1, out2, vel2, eta, wscale, src, cus, s);
+    if constexpr (!E7)
+        if (pw > 0)
+            return launch_t<T, 4, C, false, true>(d, pw, u_prev, u, out1, out2, vel2, eta, wscale,
+                                                  src, cus, s);
+    return launch_t<T, 4, C, E7, false>(d, 0, u_prev, u, out1, out2, vel2, eta, wscale, src, cus,
+                                        s);
 }
 
 }  // namespace
 
 bool wave2_available(const stencil3d_desc &d) { return d.radius >= 1 && d.radius <= 4; }
 
-int launch_wave2(const stencil3d_desc &d, const void *u_prev, const void *u, void *out1,
+int launch_wave2(const stencil3d_desc &d, int pw, const void *u_prev, const void *u, void *out1,
                  void *out2, const void *vel2, const void *eta, double wscale,
                  const Wave2Source &src, int cus, hipStream_t stream, bool pml) {
-    if (!wave2_available(d)) return ST_ERR_ARG;
+    if (!wave2_available(d) || pw < 0) return ST_ERR_ARG;
     if (d.dtype == ST_F64)
-        return pml ? launch_r<double, Wave2F64Pml, true>(d, u_prev, u, out1, out2, vel2, eta,
+        return pml ? launch_r<double, Wave2F64Pml, true>(d, pw, u_prev, u, out1, out2, vel2, eta,
                                                            wscale, src, cus, stream)
-                   : launch_r<double, Wave2F64, false>(d, u_prev, u, out1, out2, vel2, eta,
+                   : launch_r<double, Wave2F64, false>(d, pw, u_prev, u, out1, out2, vel2, eta,
                                                          wscale, src, cus, stream);
-    return pml ? launch_r<float, Wave2F32Pml, true>(d, u_prev, u, out1, out2, vel2, eta, wscale,
-                                                     src, cus, stream)
-               : launch_r<float, Wave2F32, false>(d, u_prev, u, out1, out2, vel2, eta, wscale,
+    return pml ? launch_r<float, Wave2F32Pml, true>(d, pw, u_prev, u, out1, out2, vel2, eta,
+                                                     wscale, src, cus, stream)
+               : launch_r<float, Wave2F32, false>(d, pw, u_prev, u, out1, out2, vel2, eta, wscale,
                                                    src, cus, stream);
 }
 

@@ -112,7 +112,17 @@ struct Wave2Shape {
 // around E (loaded one step ahead; two sets).  Each step also writes eta of
 // plane q2+1 on E into one of four stage-2 eta tiles, so stage 2 finds
 // planes q2-1, q2 and q2+1 in LDS (T's ring lies inside E).
-template <typename T, int R, class C, bool E7 = false>
+//
+// SP (data regions, plain step): the caller guarantees eta = 0 at every
+// interior point at least pw from all interior faces; stage 1 then loads
+// eta of its points by the rule of star2p5d_kernel's data regions, applied
+// to E's points: in every plane on rows within pw of a y face and on
+// columns within pw of an x face or of a multiple of two output-tile widths
+// (with E's XE extra columns per side, pw + XE of E's columns in every tile
+// away from the x faces), elsewhere only in the planes within pw of a z
+// face.  A load that is skipped returns the zero it would have read.
+// Stage 2 takes eta from the ring stage 1 fills.
+template <typename T, int R, class C, bool E7 = false, bool SP = false>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MINW)))
     wave2_kernel(Wave2Args<T> g) {
     using S = Wave2Shape<R, C, E7>;
@@ -160,6 +170,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
     static_assert(XE % VX == 0 && YE % VY == 0 && TY % VY == 0, "whole threads in T");
     static_assert(64 % LX == 0, "a wave covers whole thread rows");
     static_assert(T2S == 1 || T2S == 2, "one or two stage-2 tile sets");
+    static_assert(!(SP && E7), "data regions: the plain step's pass only");
     static_assert(!E7 || (NE >= S::EOFF + 2 && U % NE == 0 && NEU <= NT && VY == 1),
                   "PML step: eta ring, one eta unit per thread, one row per thread");
 
@@ -208,6 +219,17 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
         rin[j] = y >= R && y < ny - R;
         loff[j] = off_of(y, ex);
         soff[j] = (tcol && ty >= YE && ty < YE + TY && rin[j] && ex < nx - R) ? loff[j] : kOOB;
+    }
+    // SP: bit j of emask says whether row j reads eta in planes away from
+    // the z faces
+    uint32_t emask = 0;
+    const int elo = R + a.pw;  // first x (y, z) at least pw inside the interior
+    if constexpr (SP) {
+        const int m = (ex - R) % (2 * TX);  // interior x modulo two output tiles (if ex >= elo)
+        const bool cols = ex < elo || ex + VX > nx - elo || m < a.pw || m + VX > 2 * TX - a.pw;
+#pragma unroll
+        for (int j = 0; j < VY; ++j)
+            emask |= (cols || ey + j < elo || ey + j >= ny - elo) ? 1u << j : 0u;
     }
     bool cin[VX];
 #pragma unroll
@@ -488,8 +510,10 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::M
                     bload<T, VX>(re, eh_off, ehs[(kk + 1) % 2]);
                 } else {
                     const rsrc_t re = prsrc(a.eta, q1, need);
+                    const bool zf = !SP || q1 < elo || q1 >= nz - elo;  // near a z face
 #pragma unroll
-                    for (int j = 0; j < VY; ++j) bload<T, VX>(re, loff[j], et[j]);
+                    for (int j = 0; j < VY; ++j)
+                        bload<T, VX>(re, (zf || ((emask >> j) & 1u)) ? loff[j] : kOOB, et[j]);
                 }
             }
             if constexpr (!C::VRING) {

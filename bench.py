@@ -19,7 +19,8 @@ bounded number of whole-grid applications.
 turn FETCH_SIZE / WRITE_SIZE into bytes); --ceilings times copy kernels that
 walk memory like the apply (libwalkcopy.so) beside it; --only-headline skips everything
 but the timed stencil launches, --only-others runs only the Jacobi and fp64
-workloads, --only-wave {wave,pml,regions,pml_regions,blocked,both,all} only
+workloads, --only-wave {wave,pml,regions,pml_regions,blocked,blocked_regions,
+pml_blocked,both,all} only
 the 1032^3 leapfrog with those step kinds (both: wave and pml; all: every
 kind; for profiler runs).
 """
@@ -327,13 +328,13 @@ def bench_headline(torch, B, wl, args):
 
 def bench_wave(torch, B, wl, args,
                variants=("wave", "pml", "regions", "pml_regions", "blocked",
-                         "pml_blocked")):
+                         "blocked_regions", "pml_blocked")):
     """20-step leapfrog on 1032^3 (1024^3 interior), native time loop, with
     the pointwise step ("wave"), the PML kernel's step ("pml"), both
     launched as data regions ("regions", "pml_regions": pml_width = the
     sponge width, so eta is read only near the faces) and the
     time-blocked runs ("blocked", "pml_blocked": two steps per pass over four
-    buffers)."""
+    buffers; "blocked_regions": the plain one with the sponge width)."""
     w = wl.WAVE_1024
     e = w.extra
     dev = torch.device("cuda:0")
@@ -352,7 +353,7 @@ def bench_wave(torch, B, wl, args,
     u_prev = torch.zeros_like(vel2)
     u = torch.zeros_like(vel2)
     work = ([torch.zeros_like(vel2) for _ in range(2)]
-            if "blocked" in variants or "pml_blocked" in variants else None)
+            if any("blocked" in v for v in variants) else None)
     # pml_width 0: one launch reading eta everywhere (the "wave" line);
     # the "regions" line states the sponge width (data regions)
     d = B.desc_init("f32", shp, w.radius)
@@ -370,16 +371,19 @@ def bench_wave(torch, B, wl, args,
     # lack the other eta reads
     dr = B.desc_init("f32", shp, w.radius)
     dr.pml_width = e["sponge"]
-    # (the PML step's data regions run on its own 128-wide tiles)
+    # (the PML step's data regions run on its own 128-wide tiles, the
+    # two-step pass on 56-wide output tiles)
     eta_pts = {"regions": eta_read_points(w.interior, e["sponge"]),
                "pml_regions": eta_read_points(w.interior, e["sponge"],
-                                              tile_x=128)}
+                                              tile_x=128),
+               "blocked_regions": eta_read_points(w.interior, e["sponge"],
+                                                  tile_x=56)}
     res = {}
     for v in variants:
-        dv = dr if v in ("regions", "pml_regions") else d
-        if v in ("blocked", "pml_blocked"):
+        dv = dr if v in ("regions", "pml_regions", "blocked_regions") else d
+        if v in ("blocked", "pml_blocked", "blocked_regions"):
             # 20 steps = 10 passes; the fields end in (u_prev, u) again
-            fn = lambda: B.wave_run_blocked(d, u_prev, u, work[0], work[1],
+            fn = lambda: B.wave_run_blocked(dv, u_prev, u, work[0], work[1],
                                             vel2, eta, e["dt"], e["h"],
                                             w.sweeps, src, trace,
                                             pml=(v == "pml_blocked"))
@@ -400,7 +404,7 @@ def bench_wave(torch, B, wl, args,
                                         "%s_r4_f32" % v, WAVE_TRAFFIC[v])
                                     if v in WAVE_TRAFFIC else None,
                                     algorithmic_bytes_per_step=nbytes))
-        if v in ("blocked", "pml_blocked"):
+        if v in ("blocked", "pml_blocked", "blocked_regions"):
             # what a pass of two steps moves: the single step's reads plus
             # a second written field.  achieved / frac are the pass kernel's
             # own bytes over its own time; the per-step equivalent (20.09
@@ -413,9 +417,11 @@ def bench_wave(torch, B, wl, args,
             rl["frac"] = round(pass_b / (2 * per) / 1e9 / PEAK_HBM_GBS, 4)
             rl["pass_bytes"] = pass_b
             rl["traffic_per"] = "pass (one launch, two steps)"
-            rl["kernel"] = ("wave2_kernel<float,4,PML>" if v == "pml_blocked"
-                            else "wave2_kernel<float,4>")
-            rl["valu"] = valu_roofline(COUNTERS[v], 2 * per)
+            rl["kernel"] = {"pml_blocked": "wave2_kernel<float,4,PML>",
+                            "blocked_regions": "wave2_kernel<float,4,data regions>"
+                            }.get(v, "wave2_kernel<float,4>")
+            rl["valu"] = (valu_roofline(COUNTERS[v], 2 * per)
+                          if v in COUNTERS else None)
             rl["note"] = ("achieved/frac: pass bytes over pass time (one "
                           "pass = two steps); *_step_equivalent: 20.09 "
                           "B/point per step over the per-step time")
@@ -425,23 +431,34 @@ def bench_wave(torch, B, wl, args,
             res[v]["roofline"]["achieved_true_bytes"] = round(
                 true_b / per / 1e9, 1)
             res[v]["pml_width"] = e["sponge"]
+        if v == "blocked_regions":
+            # the pass reads eta once per point of its tiles (stage 1), on
+            # the points eta_read_points counts for 56-wide output tiles
+            # (the tiles' overlap columns aside)
+            true_b = res[v]["roofline"]["pass_bytes"] - 4 * (
+                w.interior_points - eta_pts[v])
+            res[v]["roofline"]["true_pass_bytes"] = true_b
+            res[v]["roofline"]["achieved_true_bytes"] = round(
+                true_b / (2 * per) / 1e9, 1)
+            res[v]["pml_width"] = e["sponge"]
         log("%s: %.1f GPoints/s, %.3f ms/step, %.1f GB/s"
             % ({"wave": "wave", "pml": "wave, PML step",
                 "regions": "wave, data regions",
                 "pml_regions": "wave, PML step, data regions",
                 "blocked": "wave, time-blocked",
+                "blocked_regions": "wave, time-blocked, data regions",
                 "pml_blocked": "wave, PML step, time-blocked"}[v],
                res[v]["value"],
                res[v]["ms_per_step"], ach))
     del vel2, eta, u_prev, u, work
     torch.cuda.empty_cache()
     for v in variants:
-        if v in ("regions", "pml_regions", "blocked",
+        if v in ("regions", "pml_regions", "blocked", "blocked_regions",
                  "pml_blocked"):  # updates timed above
             continue
         res[v]["cpu_baseline"] = None if args.no_cpu else cpu_wave_slab(
             wl, w, args.cpu_budget / 4, pml=(v == "pml"))
-    for v in ("regions", "blocked"):
+    for v in ("regions", "blocked", "blocked_regions"):
         if v in res:
             res[v]["cpu_baseline"] = res.get("wave", {}).get("cpu_baseline")
     for v in ("pml_regions", "pml_blocked"):
@@ -464,6 +481,8 @@ def bench_wave(torch, B, wl, args,
         out["data_regions"] = res["regions"]
     if "blocked" in res:
         out["time_blocked"] = res["blocked"]
+        if "blocked_regions" in res:
+            out["time_blocked"]["data_regions"] = res["blocked_regions"]
     return out
 
 
@@ -673,7 +692,8 @@ def main():
                          "walk (libwalkcopy.so) beside the apply, one JSON line")
     ap.add_argument("--only-wave",
                     choices=("wave", "pml", "regions", "pml_regions",
-                             "blocked", "pml_blocked", "both", "all"),
+                             "blocked", "blocked_regions", "pml_blocked",
+                             "both", "all"),
                     help="run only the 1032^3 leapfrog with that step "
                          "(profiling)")
     args = ap.parse_args()
@@ -709,7 +729,8 @@ def main():
         bench_wave(torch, B, wl, args,
                    variants={"both": ("wave", "pml"),
                              "all": ("wave", "pml", "regions", "pml_regions",
-                                     "blocked", "pml_blocked")}.get(
+                                     "blocked", "blocked_regions",
+                                     "pml_blocked")}.get(
                                  args.only_wave, (args.only_wave,)))
         if args.calib:
             calib_copy(torch)

@@ -286,9 +286,14 @@ int wave_run_pml(const stencil3d_desc *d, void *u_prev, void *u,
  * (wave_step(b[k-1], b[k] -> b[k+1]), then wave_add_source), with these
  * conditions: outside the interior u_prev and u must hold the same values
  * (zero, as a leapfrog from zero halos keeps them), since a pass takes
- * level k+1's non-interior points to be level k's; and d->pml_width is
- * ignored by the two-step passes (eta is read on the whole interior, which
- * gives the same bits where the pml_width claim holds).
+ * level k+1's non-interior points to be level k's.  With d->pml_width > 0
+ * (R = 4) each pass reads eta only where it may be non-zero, in one launch:
+ * its tiles on rows within pml_width of a y face read eta on every column,
+ * the others as wave_step's data regions do (columns near the x faces and
+ * the same number on every tile, planes near the z faces); the same bits
+ * under the pml_width guarantee.  On MI355X the 1024^3 R = 4 run with a
+ * 32-point sponge takes 2.87 ms per step with pml_width = 32 and 2.94 ms
+ * with 0, against 3.53 and 4.0 ms for wave_run.
  * Same arguments as wave_run otherwise.  Errors: those of wave_run, plus
  * ST_ERR_NULL / ST_ERR_ALIGN for work0 or work1 and ST_ERR_ALIAS where any
  * two of the four u buffers, vel2 and eta overlap (vel2 and eta may be the
@@ -309,10 +314,11 @@ int wave_run_blocked(const stencil3d_desc *d, void *u_prev, void *u,
  * last step.  Same arguments, buffer rotation, result placement, workspace
  * handling and conditions as wave_run_blocked; the results are bit-identical
  * to single wave_step_pml steps with their sources (up to the sign of a zero
- * result where d->pml_width makes the single steps skip eta).  On MI355X it
- * is slower than wave_run_pml for the 1024^3 R = 4 workload (4.27 against
- * 3.98 ms per step): eta's register ring and tiles leave room for only two
- * waves per SIMD on a smaller extended tile.
+ * result where d->pml_width makes the single steps skip eta; the passes
+ * read eta on the whole interior).  On MI355X the 1024^3 R = 4 workload
+ * takes 3.76 ms per step, against 3.98 for wave_run_pml and 3.73 for
+ * wave_run_pml with pml_width = 32: eta's register ring and tiles leave
+ * room for only two waves per SIMD on a smaller extended tile.
  */
 int wave_run_pml_blocked(const stencil3d_desc *d, void *u_prev, void *u,
                          void *work0, void *work1, const void *vel2,

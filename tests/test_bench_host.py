@@ -205,6 +205,11 @@ def test_eta_read_points_model():
     assert b.eta_read_points((n, n, n), pw) == want
     want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * (n // 4))
     assert b.eta_read_points((n, n, n), pw, tile_x=128) == want
+    # the two-step pass's 56-wide output tiles: 64 of every 112 columns
+    # (nine periods), the last 16 columns (band) and the x faces inside
+    # those: 592 columns
+    want = 2 * pw * n * n + (n - 2 * pw) * (2 * pw * n + (n - 2 * pw) * 592)
+    assert b.eta_read_points((n, n, n), pw, tile_x=56) == want
     # a ragged row of 1000 columns: bands [0, 32) and [480, 544), and the x
     # face rule reads [968, 1000), where the last tile's band would lie past
     # the row: 128 columns

@@ -204,9 +204,9 @@ def test_mixed_chunking_and_source_in_the_overlap(torch_dev):
 
 
 def test_no_source_and_pml_width(torch_dev):
-    """Without a source trace; with pml_width set the single steps of
-    wave_run launch data regions (eta read only near the faces) while the
-    passes read eta everywhere: equal."""
+    """Without a source trace; with pml_width set, the single steps of
+    wave_run and the passes of wave_run_blocked both launch data regions
+    (eta read only near the faces): equal."""
     torch, _ = torch_dev
     shape = (60, 70, 90)
     up, uc, v2, _ = _fields(shape, 1500)
@@ -248,6 +248,18 @@ def test_blocked_1024_two_steps(torch_dev):
     w1 = torch.zeros_like(uc)
     B.wave_run_blocked(d, up, uc, w0, w1, vel2, eta, e["dt"], e["h"], 2, src,
                        trace)
+    # the same pass with data regions (pml_width = the sponge width): the
+    # same bits over the whole array
+    log("  blocked 1024, pml_width %d" % e["sponge"])
+    dp = B.desc_init("f32", w.shape, R)
+    dp.pml_width = e["sponge"]
+    v0 = torch.zeros_like(uc)
+    v1 = torch.zeros_like(uc)
+    B.wave_run_blocked(dp, up, uc, v0, v1, vel2, eta, e["dt"], e["h"], 2, src,
+                       trace)
+    torch.cuda.synchronize()
+    assert torch.equal(v0, w0) and torch.equal(v1, w1), "data regions differ"
+    del v0, v1
     ref = torch.zeros_like(uc)
     B.wave_step(d, up, uc, ref, vel2, eta, e["dt"], e["h"])
     B.wave_add_source(d, ref, *src, float(np.float32(trace[0])))
@@ -259,6 +271,54 @@ def test_blocked_1024_two_steps(torch_dev):
     _same_interior(w1, up, "1024 step 2")
     del vel2, eta, up, uc, w0, w1, ref
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+@pytest.mark.parametrize("shape,s,widths,false_claim", [
+    # ragged in every direction
+    ((82, 75, 141), 12, (12, 30), 1),
+    # 1000 interior columns: tiles away from the x sponge and their own x
+    # edges, whose lanes skip eta away from the z faces
+    ((40, 44, 1008), 12, (12, 13), 6),
+    # six rows away from the y faces (8); none (11)
+    ((46, 30, 90), 8, (8, 11), 3),
+])
+def test_blocked_data_regions(oracle_mod, torch_dev, dt, shape, s, widths,
+                              false_claim):
+    """Two-step passes with data regions (R = 4: eta read only where it may
+    be nonzero): with eta = 0 at every interior point at least s from all
+    interior faces (and random in [0, 0.1] nearer), pml_width s (exact) and
+    larger (conservative) give the same bits as 0 over two passes; a false
+    claim changes the result, so the skipped loads are really skipped.  The
+    result also matches the oracle (four free steps)."""
+    torch, _ = torch_dev
+    npt = np.float32 if dt == "f32" else np.float64
+    up, uc, v2, et = _fields(shape, 1700 + s)
+    inner = np.zeros(shape, bool)
+    inner[R + s:-R - s, R + s:-R - s, R + s:-R - s] = True
+    et[inner] = 0.0
+    et = _zero_halo(et)
+    host = [a.astype(npt) for a in (up, uc, v2, et)]
+    up, uc, v2, et = (upload(a) for a in host)
+    runs = {}
+    for pw in (0,) + tuple(widths) + (false_claim,):
+        log("case blocked data regions %s %s sponge %d pml_width %d"
+            % (dt, shape, s, pw))
+        d = B.desc_init(dt, shape, R)
+        d.pml_width = pw
+        bufs = [up.clone(), uc.clone(), torch.zeros_like(uc),
+                torch.zeros_like(uc)]
+        old, new = B.wave_run_blocked(d, *bufs, v2, et, DT, H, 4)
+        runs[pw] = (old.cpu().numpy(), new.cpu().numpy())
+    for pw in widths:
+        for a, b in zip(runs[pw], runs[0]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), pw
+    assert not np.array_equal(runs[false_claim][1], runs[0][1])
+    c = oracle_mod.laplacian_weights(R)
+    _, ref = oracle_mod.wave_run(*host, R, c, DT, H, 4)
+    tol = 1e-4 if dt == "f32" else 1e-11
+    check_close(interior(runs[widths[0]][1], R), interior(ref, R), tol,
+                "4 free steps, blocked data regions")
 
 
 def _zero_halo_slab(shape, seed, z0, z1):
