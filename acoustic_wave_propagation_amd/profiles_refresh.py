@@ -36,7 +36,9 @@ CMDS = {
     + BENCH + "--only-headline --steps 5 --warmup 2",
     "tcc": PRE + "--pmc TCC_HIT_sum TCC_MISS_sum -T -d $RAW/pmc_tcc -o tcc"
     + BENCH + "--only-headline --steps 5 --warmup 2",
-    "wave_trace": PRE + "--kernel-trace --stats -T -d $RAW/prof_wave -o wave"
+    # full kernel names: the two-step passes with and without data regions
+    # differ only in a template argument
+    "wave_trace": PRE + "--kernel-trace --stats -d $RAW/prof_wave -o wave"
     + BENCH + "--only-wave all --no-cpu --steps 2",
 }
 # request latency and concurrency of the apply beside copies that walk
