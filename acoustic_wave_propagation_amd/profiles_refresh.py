@@ -65,7 +65,7 @@ LAT_KERNELS = [
     ("one-shot row copy", "%rows_kernel<0>%"),
     ("one-shot row copy, row-aligned stores", "%rows_kernel<1>%"),
 ]
-for _v in ("wave", "pml", "blocked", "pml_blocked"):
+for _v in ("wave", "pml", "blocked", "blocked_regions", "pml_blocked"):
     for _c, _n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         CMDS["%s_%s" % (_v, _n)] = (
             PRE + "--pmc %s -T -d $RAW/pmc_%s_%s -o %s" % (_c, _v, _n, _n)
@@ -163,8 +163,8 @@ def main(argv=None):
             lambda: P.latency_md([db("pmc_lat_tcp", "lat"), db("pmc_lat_ea", "lat")],
                                  LAT_KERNELS, [CMDS["lat_tcp"], CMDS["lat_ea"]]),
     }
-    for v in ("wave", "pml", "blocked", "pml_blocked"):
-        two = v in ("blocked", "pml_blocked")
+    for v in ("wave", "pml", "blocked", "blocked_regions", "pml_blocked"):
+        two = v in ("blocked", "blocked_regions", "pml_blocked")
         makers["%s_r4_1024cube_traffic.md" % v] = (lambda v=v, two=two: P.traffic_md(
             db("pmc_%s_fetch" % v, "fetch"), db("pmc_%s_write" % v, "write"),
             "wave2_kernel" if two else "star2p5d_kernel",

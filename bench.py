@@ -44,7 +44,7 @@ METRIC = ("GPoints/s and achieved HBM GB/s (% of peak), "
 PROF = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROF, "star2p5d_r4_512cube_traffic.md")
 WAVE_TRAFFIC = {v: os.path.join(PROF, "%s_r4_1024cube_traffic.md" % v)
-                for v in ("wave", "pml", "blocked", "pml_blocked")}
+                for v in ("wave", "pml", "blocked", "blocked_regions", "pml_blocked")}
 COUNTERS = {"headline": os.path.join(PROF, "star2p5d_r4_512cube_counters.md"),
             "blocked": os.path.join(PROF, "blocked_r4_1024cube_counters.md"),
             "pml_blocked": os.path.join(PROF, "pml_blocked_r4_1024cube_counters.md"),
