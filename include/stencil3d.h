@@ -83,13 +83,14 @@ extern "C" {
  * for the PML region, where only the latter reads eta).  If pml_width > 0
  * the caller guarantees that eta is exactly 0 at every interior point whose
  * distance (in points, along any axis) from the nearest interior face is
- * at least pml_width.  For R = 4 the wave and PML entry points then read
+ * at least pml_width.  For R = 4 the single wave and PML steps then read
  * eta only near the faces: the rows within pml_width of a y face as two
  * launches of their own; in the other rows on the columns near the x
  * faces, in the planes near the z faces, and on as many columns of every
- * tile (which keeps the tiles streaming in step).  The results are
- * bit-identical to pml_width = 0 under that guarantee, and wrong where it
- * does not hold.
+ * tile (which keeps the tiles streaming in step).  The two-step passes of
+ * wave_run_blocked apply the same rule in one launch (see there).  The
+ * results are bit-identical to pml_width = 0 under that guarantee, and
+ * wrong where it does not hold.
  * On MI355X a 1024^3 wave step with a 32-point sponge takes 3.53 ms with
  * pml_width = 32 and 4.0 ms with 0 (eta read everywhere in one launch);
  * the PML step 3.73 and 3.98 ms.
