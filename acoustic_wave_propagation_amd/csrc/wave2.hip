@@ -11,7 +11,7 @@ namespace st {
 namespace {
 
 // fp32, every radius (R = 4: the 25-point wave step).  One 640-thread
-// workgroup per compute unit, 4 x 1 points per thread (156 VGPRs at R = 4:
+// workgroup per compute unit, 4 x 1 points per thread (164 VGPRs at R = 4:
 // up to three waves per SIMD); the extended tile is 64 x 40, the output
 // tile 56 x 32.  The halo units wait in private LDS slots (PSTAGE), which
 // leaves room for the vel2/eta ring and two stage-2 tile sets; thread rows
