@@ -57,6 +57,19 @@ CMDS["lat_wave_tcp"] = (PRE + "--pmc " + LAT_TCP + " -d $RAW/pmc_lat_wave_tcp -o
                         + BENCH + "--only-wave wave --no-cpu --steps 1")
 CMDS["lat_wave_ea"] = (PRE + "--pmc " + LAT_EA + " -d $RAW/pmc_lat_wave_ea -o lat"
                        + BENCH + "--only-wave wave --no-cpu --steps 1")
+# the same counters on the two-step passes (plain, with data regions, PML)
+CMDS["lat_passes_tcp"] = (PRE + "--pmc " + LAT_TCP + " -d $RAW/pmc_lat_passes_tcp -o lat"
+                          + BENCH + "--only-wave all --no-cpu --steps 1")
+CMDS["lat_passes_ea"] = (PRE + "--pmc " + LAT_EA + " -d $RAW/pmc_lat_passes_ea -o lat"
+                         + BENCH + "--only-wave all --no-cpu --steps 1")
+PASS_KERNELS = [
+    ("two-step pass (wave2_kernel, 64 x 40 extended tiles)",
+     "%wave2_kernel<float, 4, st::Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>, false, false>%"),
+    ("two-step pass with data regions",
+     "%wave2_kernel<float, 4, st::Wave2Cfg<4, 1, 16, 40, 3, true, true, 2, true>, false, true>%"),
+    ("two-step PML pass (64 x 32 extended tiles)",
+     "%wave2_kernel<float, 4, st::Wave2Cfg<4, 1, 16, 32, 2, true, true, 2, true>, true, false>%"),
+]
 LAT_KERNELS = [
     ("R=4 apply (star2p5d_kernel, 256 x 16 tiles)", "%star2p5d_kernel<float, 4, false%"),
     ("z-march copy, 256 x 16 tiles", "%zmarch_kernel<64, 8, 0>%"),
@@ -159,6 +172,12 @@ def main(argv=None):
                                  [("R=4 wave step (star2p5d_kernel, 128 x 32 tiles)",
                                    "%star2p5d_kernel<float, 4, true%")],
                                  [CMDS["lat_wave_tcp"], CMDS["lat_wave_ea"]], sources="stream"),
+        "two_step_passes_r4_1024cube_latency.md":
+            lambda: P.latency_md([db("pmc_lat_passes_tcp", "lat"),
+                                  db("pmc_lat_passes_ea", "lat")],
+                                 PASS_KERNELS,
+                                 [CMDS["lat_passes_tcp"], CMDS["lat_passes_ea"]],
+                                 sources="blocked"),
         "apply_and_walk_copies_r4_512cube_latency.md":
             lambda: P.latency_md([db("pmc_lat_tcp", "lat"), db("pmc_lat_ea", "lat")],
                                  LAT_KERNELS, [CMDS["lat_tcp"], CMDS["lat_ea"]]),
